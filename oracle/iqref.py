@@ -1,0 +1,320 @@
+"""CPU oracle for the IsoQuant packed 3-bit KV cache (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, the smoke entry point and the benchmark's CPU-baseline
+leg may import this module. The product path (the HIP library and its Python
+binding) never touches it, and it shares no code, tables or constants with the
+HIP sources: the codebook, the Hadamard matrix and the quaternion algebra are
+all written out here independently.
+
+Everything is plain numpy in float64, except where the method itself fixes a
+narrower type: the rotated coordinates that are quantized, the per-vector norm
+and the quantization thresholds are float32, and the quantization decision is
+taken in float32 (the same precision the GPU decides in).
+
+Sources (titles of the pages; section names in brackets):
+  [RQ-abs]  arXiv 2608.08081 listing, "RotaryQuant" English abstract.
+  [RQ-news] rebasdaily.com news article on RotaryQuant, section on attention
+            over packed data ("妙处不只是压缩，而是不再展开").
+  [TQ-essay] zhichai.net essay "压缩与速度的博弈——TurboQuant 和 RotorQuant 的真相",
+            sections "Beta 分布的魔力", "Lloyd-Max 最优量化", "真正的瓶颈",
+            "为什么压缩 KV 缓存这么难？" (the attention formula).
+  [RQ-blurb] sd114.wiki RotorQuant page, section "V 缓存的逆旋转修复".
+
+Readings taken where the pages are silent or garbled (each is also listed in
+the design notes of the repository):
+  * R = B . Hn: the normalised Walsh-Hadamard transform in Sylvester (natural)
+    order without random signs comes first, then the block-diagonal SO(4)
+    rotation B ([RQ-abs]: "Walsh-Hadamard transform followed by block-diagonal
+    SO(4) rotations").
+  * Block b acts on dims 4b..4b+3 read as a quaternion (w, x, y, z):
+    v -> qL (x) v (x) conj(qR), Hamilton product. Parameters per head:
+    32 blocks x (qL, qR) x 4 = 256 ([RQ-abs], [RQ-news]). Stored float32
+    quaternions are renormalised in float64 before use.
+  * Codebook: 8-level Lloyd-Max quantizer for N(0, 1/d), d = 128
+    ([TQ-essay] "Lloyd-Max 最优量化"; the Beta(1/2,(d-1)/2) statement in
+    "Beta 分布的魔力" holds for the squared coordinate, the Gaussian limit is
+    what the codebook is built for). Centroids and midpoint thresholds are
+    computed in float64 and rounded to float32.
+  * The norm is that of the float32 rotated vector y (equal to ||x|| up to
+    rounding): n = fl32(sqrt(sum_j y_j^2)) with the sum in float64.
+  * Quantization: thr_k = fl32(t_k * n) (float32 multiply, round to nearest
+    even) and code_j = #{k : y_j > thr_k}; ties go to the lower code, a zero
+    vector gives all-zero codes, NaN gives code 0.
+  * Code numbering: code c is the c-th centroid in ascending order.
+  * Packing: code j occupies bits [3j, 3j+3) of a 384-bit little-endian
+    bitstream (48 bytes per row); bytes 3i..3i+2 hold codes 8i..8i+7.
+  * Dequantization: x_hat = n . R^-1 c[code], R^-1 = Hn . B^T ([RQ-blurb]:
+    the inverse rotation must be applied when reconstructing V).
+  * Attention: softmax(scale . q K_hat^T) V_hat per query head
+    ([TQ-essay] attention formula), query head g reads KV head g // G.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+D = 128
+N_BLOCKS = D // 4
+N_LEVELS = 8
+BITS = 3
+ROW_BYTES = D * BITS // 8   # 48
+
+
+# --------------------------------------------------------------------------
+# Codebook: Lloyd-Max for a Gaussian ([TQ-essay] "Lloyd-Max 最优量化")
+# --------------------------------------------------------------------------
+def _pdf(x: float) -> float:
+    if math.isinf(x):
+        return 0.0
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _cdf(x: float) -> float:
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def _cell_mass(a: float, b: float) -> float:
+    """P(a < X <= b) for X ~ N(0,1), computed on the side of the smaller tail."""
+    if a >= 0:
+        return 0.5 * math.erfc(a / math.sqrt(2.0)) - 0.5 * math.erfc(b / math.sqrt(2.0))
+    return _cdf(b) - _cdf(a)
+
+
+def lloyd_max_unit_gaussian(levels: int = N_LEVELS, tol: float = 1e-16, max_iter: int = 100000):
+    """Lloyd-Max quantizer of N(0,1): returns (centroids, thresholds) in float64.
+
+    The iteration the essay describes: start from some centroids, assign each
+    value to its nearest centroid (the cell boundaries are the midpoints),
+    replace every centroid by the mean of its cell, repeat until nothing moves.
+    For a Gaussian the cell mean has the closed form
+    (pdf(a) - pdf(b)) / (cdf(b) - cdf(a)).
+    """
+    c = np.linspace(-2.0, 2.0, levels)
+    for _ in range(max_iter):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = [-math.inf] + list(t) + [math.inf]
+        new = np.array([(_pdf(a) - _pdf(b)) / _cell_mass(a, b) for a, b in zip(edges[:-1], edges[1:])])
+        done = np.max(np.abs(new - c)) <= tol
+        c = new
+        if done:
+            break
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t
+
+
+def quantizer_mse_unit_gaussian(c: np.ndarray, t: np.ndarray) -> float:
+    """E[(X - Q(X))^2] for X ~ N(0,1) and the scalar quantizer (c, t), closed form."""
+    edges = [-math.inf] + list(t) + [math.inf]
+    total = 0.0
+    for k, (a, b) in enumerate(zip(edges[:-1], edges[1:])):
+        p = _cell_mass(a, b)
+        m1 = _pdf(a) - _pdf(b)                                    # int x pdf
+        apdf = 0.0 if math.isinf(a) else a * _pdf(a)
+        bpdf = 0.0 if math.isinf(b) else b * _pdf(b)
+        m2 = p + apdf - bpdf                                      # int x^2 pdf
+        total += m2 - 2.0 * c[k] * m1 + c[k] ** 2 * p
+    return total
+
+
+def codebook(d: int = D):
+    """Codebook for N(0, 1/d): (centroids float32[8], thresholds float32[7], centroids float64[8])."""
+    c, t = lloyd_max_unit_gaussian()
+    s = 1.0 / math.sqrt(d)
+    return (c * s).astype(np.float32), (t * s).astype(np.float32), c * s
+
+
+# --------------------------------------------------------------------------
+# Rotation: normalised WHT, then block-diagonal SO(4) ([RQ-abs], [RQ-news])
+# --------------------------------------------------------------------------
+def hadamard(n: int = D) -> np.ndarray:
+    """Sylvester Hadamard matrix: H_1 = [1], H_2m = [[H, H], [H, -H]]."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def wht(x: np.ndarray) -> np.ndarray:
+    """Normalised Walsh-Hadamard transform Hn x = H x / sqrt(d) over the last axis."""
+    d = x.shape[-1]
+    return np.asarray(x, np.float64) @ (hadamard(d).T / math.sqrt(d))
+
+
+def quat_mul(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Hamilton product p (x) q of quaternions stored (w, x, y, z) on the last axis."""
+    pw, px, py, pz = np.moveaxis(p, -1, 0)
+    qw, qx, qy, qz = np.moveaxis(q, -1, 0)
+    return np.stack([
+        pw * qw - px * qx - py * qy - pz * qz,
+        pw * qx + px * qw + py * qz - pz * qy,
+        pw * qy - px * qz + py * qw + pz * qx,
+        pw * qz + px * qy - py * qx + pz * qw,
+    ], axis=-1)
+
+
+def quat_conj(q: np.ndarray) -> np.ndarray:
+    return q * np.array([1.0, -1.0, -1.0, -1.0])
+
+
+def unit_quaternions(rot: np.ndarray):
+    """(qL, qR) float64 [..., 32, 4] from stored params [..., 32, 8], renormalised."""
+    r = np.asarray(rot, np.float64)
+    ql, qr = r[..., 0:4], r[..., 4:8]
+    ql = ql / np.linalg.norm(ql, axis=-1, keepdims=True)
+    qr = qr / np.linalg.norm(qr, axis=-1, keepdims=True)
+    return ql, qr
+
+
+def so4_apply(y: np.ndarray, rot: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Apply B (or B^T) to [..., 128] vectors; rot is [32, 8] for one head.
+
+    Forward per block: v -> qL (x) v (x) conj(qR). Inverse per block:
+    v -> conj(qL) (x) v (x) qR.
+    """
+    ql, qr = unit_quaternions(rot)
+    v = np.asarray(y, np.float64).reshape(y.shape[:-1] + (N_BLOCKS, 4))
+    if inverse:
+        out = quat_mul(quat_mul(quat_conj(ql), v), qr)
+    else:
+        out = quat_mul(quat_mul(ql, v), quat_conj(qr))
+    return out.reshape(y.shape)
+
+
+def so4_block_matrices(rot: np.ndarray) -> np.ndarray:
+    """The 32 4x4 matrices M_b of the forward block map (columns = images of e_i)."""
+    eye = np.eye(4)
+    ql, qr = unit_quaternions(rot)
+    m = np.empty((N_BLOCKS, 4, 4))
+    for i in range(4):
+        m[:, :, i] = quat_mul(quat_mul(ql, eye[i]), quat_conj(qr))
+    return m
+
+
+def rotate(x: np.ndarray, rot: np.ndarray) -> np.ndarray:
+    """y = B . Hn . x in float64 for [..., 128] vectors of one head."""
+    return so4_apply(wht(x), rot)
+
+
+def inverse_rotate(y: np.ndarray, rot: np.ndarray) -> np.ndarray:
+    """x = Hn . B^T . y in float64 (Hn is symmetric and its own inverse)."""
+    return wht(so4_apply(y, rot, inverse=True))
+
+
+# --------------------------------------------------------------------------
+# Norm, quantization, packing ([TQ-essay] "Beta 分布的魔力", "Lloyd-Max 最优量化",
+# "真正的瓶颈"; [RQ-abs] "3-bit scalar quantization", "packed 3-bit tensors")
+# --------------------------------------------------------------------------
+def quantize(y32: np.ndarray, thresholds32: np.ndarray):
+    """Codes (uint8 [..., 128]) and norms (float32 [...]) of float32 rotated vectors."""
+    y32 = np.asarray(y32, np.float32)
+    y64 = y32.astype(np.float64)
+    norm = np.sqrt(np.sum(y64 * y64, axis=-1)).astype(np.float32)
+    thr = thresholds32.astype(np.float32)[None, :] * norm.reshape(-1, 1)      # float32 products
+    thr = thr.reshape(norm.shape + (len(thresholds32),))
+    codes = np.sum(y32[..., :, None] > thr[..., None, :], axis=-1).astype(np.uint8)
+    return codes, norm
+
+
+def pack(codes: np.ndarray) -> np.ndarray:
+    """[..., 128] codes -> [..., 48] bytes; code j at bits [3j, 3j+3), little-endian."""
+    codes = np.asarray(codes, np.uint8)
+    bits = np.stack([(codes >> b) & 1 for b in range(BITS)], axis=-1)       # [..., 128, 3]
+    bits = bits.reshape(codes.shape[:-1] + (D * BITS,))
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def unpack(rows: np.ndarray) -> np.ndarray:
+    """[..., 48] bytes -> [..., 128] codes (inverse of ``pack``)."""
+    bits = np.unpackbits(np.asarray(rows, np.uint8), axis=-1, bitorder="little")
+    bits = bits.reshape(rows.shape[:-1] + (D, BITS)).astype(np.uint8)
+    return bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
+
+
+def rotate_quantize(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
+    """Full encode of [..., 128] vectors of one head: (packed rows, norms, float32 y)."""
+    y32 = rotate(np.asarray(x, np.float64), rot).astype(np.float32)
+    codes, norm = quantize(y32, thresholds32)
+    return pack(codes), norm, y32
+
+
+def dequantize(rows: np.ndarray, norms: np.ndarray, rot: np.ndarray, centroids32: np.ndarray) -> np.ndarray:
+    """x_hat = n . Hn . B^T . c[code] in float64 ([RQ-blurb]: V needs the inverse rotation)."""
+    c = centroids32.astype(np.float64)[unpack(rows)]
+    return np.asarray(norms, np.float64)[..., None] * inverse_rotate(c, rot)
+
+
+# --------------------------------------------------------------------------
+# Cache-level encode (the append call) and decode attention
+# --------------------------------------------------------------------------
+def encode_tokens(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
+    """Encode [n_tok][Hkv][128] -> rows [Hkv][n_tok][48], norms [Hkv][n_tok]."""
+    n_tok, hkv, _ = x.shape
+    rows = np.empty((hkv, n_tok, ROW_BYTES), np.uint8)
+    norms = np.empty((hkv, n_tok), np.float32)
+    for h in range(hkv):
+        r, n, _ = rotate_quantize(x[:, h, :], rot[h], thresholds32)
+        rows[h], norms[h] = r, n
+    return rows, norms
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale . q K^T) V for q [m][128], K/V [T][128]; T = 0 gives zeros."""
+    if k_hat.shape[0] == 0:
+        return np.zeros((q.shape[0], v_hat.shape[-1]))
+    p = softmax(scale * (np.asarray(q, np.float64) @ k_hat.T))
+    return p @ v_hat
+
+
+def decode_attention(q, k_rows, k_norms, v_rows, v_norms, rot, seq_start, seq_len, scale, centroids32,
+                     seqs=None, heads=None):
+    """Decode attention straight from the definition, in float64.
+
+    q [n_seqs][Hq][128]; k_rows/v_rows [Hkv][cap][48]; norms [Hkv][cap];
+    rot [Hkv][32][8]. The packed K and V of each sequence are dequantized
+    explicitly and ordinary softmax attention is taken over them. ``seqs`` and
+    ``heads`` restrict the computation to a sample; other outputs stay NaN.
+    """
+    n_seqs, hq, _ = q.shape
+    hkv = k_rows.shape[0]
+    g = hq // hkv
+    out = np.full((n_seqs, hq, D), np.nan)
+    for s in (range(n_seqs) if seqs is None else seqs):
+        a, n = int(seq_start[s]), int(seq_len[s])
+        for h in (range(hkv) if heads is None else heads):
+            kh = dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], centroids32)
+            vh = dequantize(v_rows[h, a:a + n], v_norms[h, a:a + n], rot[h], centroids32)
+            out[s, h * g:(h + 1) * g] = attention(q[s, h * g:(h + 1) * g], kh, vh, scale)
+    return out
+
+
+def decode_attention_rotated(q, k_rows, k_norms, v_rows, v_norms, rot, seq_start, seq_len, scale,
+                             centroids32):
+    """The packed-domain algorithm, step by step in float64 ([RQ-news], [RQ-abs]).
+
+    Rotate each query once (q' = R q), score every packed key as
+    n_t . (q' . c[code_t]), softmax, accumulate n_t . c[vcode_t] with the
+    weights, and apply one inverse rotation to the result. By orthogonality
+    of R this equals ``decode_attention``.
+    """
+    n_seqs, hq, _ = q.shape
+    hkv = k_rows.shape[0]
+    g = hq // hkv
+    c = centroids32.astype(np.float64)
+    out = np.zeros((n_seqs, hq, D))
+    for s in range(n_seqs):
+        a, n = int(seq_start[s]), int(seq_len[s])
+        if n == 0:
+            continue
+        for h in range(hkv):
+            qr = rotate(q[s, h * g:(h + 1) * g].astype(np.float64), rot[h])         # [g][128]
+            kc = c[unpack(k_rows[h, a:a + n])] * k_norms[h, a:a + n, None].astype(np.float64)
+            vc = c[unpack(v_rows[h, a:a + n])] * v_norms[h, a:a + n, None].astype(np.float64)
+            p = softmax(scale * (qr @ kc.T))
+            out[s, h * g:(h + 1) * g] = inverse_rotate(p @ vc, rot[h])
+    return out

@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each check is written as a function so the mutation tests at the bottom can
+re-run it against a deliberately broken copy of the oracle and see it fail.
+Nothing here needs a GPU.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+import scipy.special
+import scipy.stats
+from scipy.spatial.transform import Rotation
+
+import iqinputs
+from oracle import iqref as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rot(seed=7, layer=0, heads=1):
+    return iqinputs.rotation_params(seed, layer, heads)
+
+
+# ---------------------------------------------------------------- WHT ----
+def check_wht():
+    h = R.hadamard(128)
+    assert np.array_equal(h, scipy.linalg.hadamard(128))          # library routine
+    hn = R.wht(np.eye(128))                                        # rows = Hn e_i
+    assert np.allclose(hn @ hn, np.eye(128), atol=1e-13)           # self-inverse
+    assert np.allclose(hn, hn.T, atol=0)                           # symmetric
+    assert np.allclose(R.wht(np.eye(128)[0]), np.full(128, 1 / math.sqrt(128)), atol=1e-15)
+    x = np.random.default_rng(1).standard_normal((5, 128))
+    assert np.allclose(R.wht(x), x @ scipy.linalg.hadamard(128).T / math.sqrt(128), atol=1e-12)
+
+
+def test_wht_is_normalised_sylvester_hadamard():
+    check_wht()
+
+
+# ------------------------------------------------------- quaternions ----
+def check_quaternion_product():
+    one, i, j, k = np.eye(4)
+    assert np.allclose(R.quat_mul(i, j), k) and np.allclose(R.quat_mul(j, k), i)
+    assert np.allclose(R.quat_mul(k, i), j) and np.allclose(R.quat_mul(i, i), -one)
+    assert np.allclose(R.quat_mul(j, i), -k)
+    g = np.random.default_rng(2)
+    p, q = g.standard_normal((2, 50, 4))
+    assert np.allclose(np.linalg.norm(R.quat_mul(p, q), axis=-1),
+                       np.linalg.norm(p, axis=-1) * np.linalg.norm(q, axis=-1), atol=1e-12)
+    # q v q* rotates the vector part like scipy's rotation of the same quaternion
+    q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    u = g.standard_normal((50, 3))
+    v = np.concatenate([np.zeros((50, 1)), u], axis=1)
+    r = R.quat_mul(R.quat_mul(q, v), R.quat_conj(q))
+    ref = Rotation.from_quat(np.concatenate([q[:, 1:], q[:, :1]], axis=1)).apply(u)  # scalar-last
+    assert np.allclose(r[:, 0], 0, atol=1e-12) and np.allclose(r[:, 1:], ref, atol=1e-12)
+
+
+def test_quaternion_product_textbook():
+    check_quaternion_product()
+
+
+# --------------------------------------------------------------- SO(4) ----
+def check_so4():
+    rot = _rot(heads=3)
+    for h in range(3):
+        m = R.so4_block_matrices(rot[h])
+        for b in range(32):
+            assert np.allclose(m[b].T @ m[b], np.eye(4), atol=1e-14)
+            assert abs(np.linalg.det(m[b]) - 1.0) < 1e-13
+        y = np.random.default_rng(h).standard_normal((4, 128))
+        blocks = y.reshape(4, 32, 4)
+        by_matrix = np.einsum("bij,nbj->nbi", m, blocks).reshape(4, 128)
+        assert np.allclose(R.so4_apply(y, rot[h]), by_matrix, atol=1e-13)
+        assert np.allclose(R.so4_apply(R.so4_apply(y, rot[h]), rot[h], inverse=True), y, atol=1e-13)
+
+
+def test_so4_blocks_are_rotations():
+    check_so4()
+
+
+def check_rotation_special_cases():
+    # identity quaternions: R reduces to the normalised Hadamard transform
+    ident = np.tile(np.array([1, 0, 0, 0, 1, 0, 0, 0], np.float32), (32, 1))
+    x = np.random.default_rng(3).standard_normal((6, 128))
+    assert np.allclose(R.rotate(x, ident), x @ scipy.linalg.hadamard(128).T / math.sqrt(128), atol=1e-12)
+    # qL = qR = q: w is fixed and (x, y, z) is rotated by the SO(3) rotation of q
+    g = np.random.default_rng(4)
+    q = g.standard_normal((32, 4))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    rot = np.concatenate([q, q], axis=1)
+    y = g.standard_normal(128)
+    out = R.so4_apply(y, rot).reshape(32, 4)
+    blk = y.reshape(32, 4)
+    assert np.allclose(out[:, 0], blk[:, 0], atol=1e-12)
+    ref = Rotation.from_quat(np.concatenate([q[:, 1:], q[:, :1]], axis=1)).apply(blk[:, 1:])
+    assert np.allclose(out[:, 1:], ref, atol=1e-12)
+
+
+def test_rotation_special_cases():
+    check_rotation_special_cases()
+
+
+def check_rotation_round_trip():
+    rot = _rot(heads=1)[0]
+    x = np.random.default_rng(5).standard_normal((10, 128)) * 3
+    y = R.rotate(x, rot)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    assert np.allclose(R.inverse_rotate(y, rot), x, atol=1e-13)
+    full = R.rotate(np.eye(128), rot)        # rows: R e_i
+    assert np.allclose(full @ full.T, np.eye(128), atol=1e-13)
+    assert np.linalg.det(full) > 0
+
+
+def test_rotation_norm_preserving_and_invertible():
+    check_rotation_round_trip()
+
+
+def test_parameter_and_fma_counts():
+    # 256 stored parameters per head and 1,408 FMA per vector (news article on
+    # RotaryQuant, paragraph on the structured rotation; abstract: 256 per head)
+    rot = _rot(heads=4)
+    assert rot.shape == (4, 32, 8) and rot[0].size == 256
+    assert np.allclose(np.linalg.norm(rot.reshape(4, 32, 2, 4), axis=-1), 1, atol=1e-6)
+    wht_ops = int(math.log2(128)) * 128            # 7 butterfly stages of 128 add/sub
+    so4_fma = 32 * 16                              # one 4x4 matrix per block
+    assert wht_ops + so4_fma == 1408 and 128 * 128 == 16384
+
+
+# ------------------------------------------------------------ codebook ----
+def _golden_max():
+    th, lv, mse = [], [], None
+    with open(os.path.join(GOLDEN, "max1960_gaussian_8level.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            kind, val = line.split()
+            if kind == "threshold":
+                th.append(float(val))
+            elif kind == "level":
+                lv.append(float(val))
+            else:
+                mse = float(val)
+    return np.array(th), np.array(lv), mse
+
+
+def check_codebook():
+    c, t = R.lloyd_max_unit_gaussian()
+    th, lv, mse = _golden_max()
+    assert np.allclose(c[4:], lv, atol=6e-4) and np.allclose(c[:4], -lv[::-1], atol=6e-4)
+    assert np.allclose(t[4:], th, atol=6e-4) and np.allclose(t[:3], -th[::-1], atol=6e-4) and t[3] == 0
+    d = R.quantizer_mse_unit_gaussian(c, t)
+    assert abs(d - mse) < 1e-4
+    # optimality conditions by independent numerical integration
+    edges = [-np.inf] + list(t) + [np.inf]
+    for k in range(8):
+        mass = scipy.integrate.quad(scipy.stats.norm.pdf, edges[k], edges[k + 1], epsabs=1e-14)[0]
+        mom = scipy.integrate.quad(lambda x: x * scipy.stats.norm.pdf(x), edges[k], edges[k + 1], epsabs=1e-14)[0]
+        assert abs(mom / mass - c[k]) < 1e-9
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), atol=0)
+    quad_mse = sum(scipy.integrate.quad(lambda x, ck=c[k]: (x - ck) ** 2 * scipy.stats.norm.pdf(x),
+                                        edges[k], edges[k + 1], epsabs=1e-14)[0] for k in range(8))
+    assert abs(quad_mse - d) < 1e-9
+    # within ~2.7x of the Shannon lower bound 2^(-2b) (essay, Lloyd-Max section)
+    assert 4.0 ** -3 <= d <= 2.7 * 4.0 ** -3
+    c32, t32, c64 = R.codebook()
+    assert np.array_equal(c32, (c / math.sqrt(128)).astype(np.float32))
+    assert np.array_equal(t32, (t / math.sqrt(128)).astype(np.float32))
+
+
+def test_codebook_is_lloyd_max_gaussian():
+    check_codebook()
+
+
+def test_codebook_matches_kmeans_on_samples():
+    # Lloyd's algorithm as run by an independent library on N(0,1) samples
+    from sklearn.cluster import KMeans
+    x = np.random.default_rng(6).standard_normal(400_000).reshape(-1, 1)
+    km = KMeans(n_clusters=8, n_init=1, init=np.linspace(-2, 2, 8).reshape(-1, 1), max_iter=500, tol=1e-10).fit(x)
+    c, _ = R.lloyd_max_unit_gaussian()
+    assert np.allclose(np.sort(km.cluster_centers_.ravel()), c, atol=0.02)
+
+
+# --------------------------------------------------------- quantizer ----
+def check_quantize(codebook):
+    c32, t32, _ = codebook
+    g = np.random.default_rng(8)
+    y = (g.standard_normal((2000, 128)) * g.uniform(0.1, 30, (2000, 1))).astype(np.float32)
+    codes, n = R.quantize(y, t32)
+    assert np.array_equal(n, np.sqrt(np.sum(y.astype(np.float64) ** 2, axis=1)).astype(np.float32))
+    # brute force: nearest centroid of y/n
+    u = y.astype(np.float64) / n[:, None].astype(np.float64)
+    nearest = np.argmin(np.abs(u[..., None] - c32.astype(np.float64)), axis=-1)
+    diff = nearest != codes
+    if diff.any():
+        # only where u sits within float32 rounding of a cell boundary
+        gap = np.min(np.abs(u[diff][:, None] - t32.astype(np.float64)), axis=-1)
+        assert np.all(gap < 1e-6)
+    assert diff.mean() < 1e-5
+    # special cases
+    z, nz = R.quantize(np.zeros((1, 128), np.float32), t32)
+    assert nz[0] == 0 and not z.any()
+    e = np.zeros((1, 128), np.float32)
+    e[0, 5] = 3.0
+    ce, ne = R.quantize(e, t32)
+    assert ne[0] == 3.0 and ce[0, 5] == 7 and np.all(np.delete(ce[0], 5) == 3)   # 0 > thr_3 = 0 is false
+    e[0, 5] = -3.0
+    ce, _ = R.quantize(e, t32)
+    assert ce[0, 5] == 0
+    nan = np.full((1, 128), np.nan, np.float32)
+    cn, nn = R.quantize(nan, t32)
+    assert np.isnan(nn[0]) and not cn.any()
+
+
+def test_quantize_is_nearest_centroid(codebook):
+    check_quantize(codebook)
+
+
+def test_quantize_ties_go_to_lower_code(codebook):
+    c32, t32, _ = codebook
+    # y = (b, a, 0, ...) with n = fl32(sqrt(a^2 + b^2)) == 1 exactly, so the
+    # threshold fl32(t_k * n) is t_k itself; put a exactly on it.
+    tested = 0
+    for k in range(7):
+        a = np.float32(t32[k])
+        b0 = np.float32(np.sqrt(1.0 - float(a) ** 2))
+        for b in [b0, np.nextafter(b0, np.float32(2)), np.nextafter(b0, np.float32(0))]:
+            y = np.zeros((1, 128), np.float32)
+            y[0, 0], y[0, 1] = b, a
+            codes, n = R.quantize(y, t32)
+            if n[0] != 1.0:
+                continue
+            assert codes[0, 1] == k              # y_1 == thr_k is not above threshold k
+            y[0, 1] = np.nextafter(a, np.float32(1))
+            codes2, n2 = R.quantize(y, t32)
+            if n2[0] == 1.0:
+                assert codes2[0, 1] == k + 1     # one ulp above moves up one code
+            tested += 1
+            break
+    assert tested >= 5
+
+
+# ----------------------------------------------------------- packing ----
+def test_pack_golden():
+    with open(os.path.join(GOLDEN, "pack_pattern.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            lhs, rhs = line.split("|")
+            codes = np.zeros(128, np.uint8)
+            codes[:8] = [int(v) for v in lhs.split()]
+            row = R.pack(codes)
+            assert row.shape == (48,)
+            assert list(row[:3]) == [int(v, 16) for v in rhs.split()]
+            assert not row[3:].any()
+
+
+def test_pack_unpack_exhaustive():
+    for pos in range(128):
+        for v in range(8):
+            codes = np.zeros(128, np.uint8)
+            codes[pos] = v
+            row = R.pack(codes)
+            bits = np.unpackbits(row, bitorder="little")
+            assert bits.sum() == bin(v).count("1")
+            assert all(bits[3 * pos + b] == ((v >> b) & 1) for b in range(3))
+            assert np.array_equal(R.unpack(row), codes)
+    codes = np.random.default_rng(9).integers(0, 8, (100, 128)).astype(np.uint8)
+    assert np.array_equal(R.unpack(R.pack(codes)), codes)
+
+
+# ------------------------------------------------------- distortion ----
+def test_distortion_isotropic_inputs(codebook):
+    c32, t32, _ = codebook
+    rot = _rot(heads=1)[0]
+    x = np.random.default_rng(10).standard_normal((20000, 128))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    rows, n, _ = R.rotate_quantize(x, rot, t32)
+    d = np.mean(np.sum((x - R.dequantize(rows, n, rot, c32)) ** 2, axis=1))
+    assert abs(d - 0.03455) < 0.05 * 0.03455
+
+
+def test_rotation_isotropizes_outlier_channels():
+    rot = _rot(heads=1)[0]
+    x = iqinputs.kv(1, 0, "k", 20000, 1, "fixed_x8", "f32")[:, 0, :].astype(np.float64)
+    u0 = x / np.linalg.norm(x, axis=1, keepdims=True)
+    y = R.rotate(x, rot)
+    u = y / np.linalg.norm(y, axis=1, keepdims=True)
+    assert scipy.stats.kurtosis(u0.ravel()) > 10
+    assert abs(scipy.stats.kurtosis(u.ravel())) < 0.5
+    assert abs(u.var() * 128 - 1) < 0.01
+
+
+# -------------------------------------------------------- attention ----
+def _small_cache(codebook, n_tok=300, hkv=2, hq=4, seed=11, lens=(300,)):
+    c32, t32, _ = codebook
+    g = np.random.default_rng(seed)
+    rot = _rot(seed=seed, heads=hkv)
+    k = g.standard_normal((n_tok, hkv, 128))
+    v = g.standard_normal((n_tok, hkv, 128))
+    kr, kn = R.encode_tokens(k, rot, t32)
+    vr, vn = R.encode_tokens(v, rot, t32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    q = g.standard_normal((len(lens), hq, 128)).astype(np.float32)
+    return q, kr, kn, vr, vn, rot, starts, np.array(lens, np.int32)
+
+
+def test_attention_packed_domain_equals_brute_force(codebook):
+    c32 = codebook[0]
+    args = _small_cache(codebook, n_tok=300, lens=(120, 0, 1, 179))
+    scale = 1 / math.sqrt(128)
+    a = R.decode_attention(*args, scale, c32)
+    b = R.decode_attention_rotated(*args, scale, c32)
+    assert np.allclose(a, b, atol=1e-12, rtol=0)
+    assert np.all(a[1] == 0)                                          # empty sequence
+
+
+def test_attention_special_cases(codebook):
+    c32 = codebook[0]
+    q, kr, kn, vr, vn, rot, st, ln = _small_cache(codebook, n_tok=50, hkv=1, hq=2, lens=(50,))
+    v_hat = R.dequantize(vr[0], vn[0], rot[0], c32)
+    # one token: output is that token's value
+    one = R.decode_attention(q, kr, kn, vr, vn, rot, st, np.array([1], np.int32), 0.3, c32)
+    assert np.allclose(one[0, 0], v_hat[0], atol=1e-13)
+    # scale 0: plain mean of the values
+    z = R.decode_attention(q, kr, kn, vr, vn, rot, st, ln, 0.0, c32)
+    assert np.allclose(z[0, 1], v_hat.mean(0), atol=1e-13)
+    # identical keys: mean of the values
+    kr2 = np.repeat(kr[:, :1], 50, axis=1)
+    kn2 = np.repeat(kn[:, :1], 50, axis=1)
+    same = R.decode_attention(q, kr2, kn2, vr, vn, rot, st, ln, 0.2, c32)
+    assert np.allclose(same[0, 0], v_hat.mean(0), atol=1e-13)
+    # softmax against the library routine
+    s = np.random.default_rng(3).standard_normal((3, 40)) * 20
+    assert np.allclose(R.softmax(s), scipy.special.softmax(s, axis=-1), atol=1e-15)
+
+
+def test_needle_is_recovered(codebook):
+    """A key planted as 4x the query wins the attention (moe30b shape, shortened)."""
+    c32, t32, _ = codebook
+    w = iqinputs.WORKLOADS["moe30b_gqa_t32768"]
+    inp = iqinputs.layer_inputs(w, 0, n_tokens=4096)
+    kr, kn = R.encode_tokens(inp["k"], inp["rot"], t32)
+    p = int(inp["needle_slot"][0])
+    for h in range(w.num_kv_heads):
+        kh = R.dequantize(kr[h], kn[h], inp["rot"][h], c32)
+        qg = inp["q"][0, h * w.group].astype(np.float64)
+        wts = R.softmax(kh @ qg / math.sqrt(128))
+        assert int(np.argmax(wts)) == p and wts[p] > 0.99
+
+
+# ------------------------------------------------------- mutations ----
+# A plausible slip anywhere in the oracle must fail one of the pins above.
+def _expect_fail(fn, *a):
+    with pytest.raises(AssertionError):
+        fn(*a)
+
+
+def test_mutation_wrong_hamilton_sign(monkeypatch):
+    good = R.quat_mul
+
+    def bad(p, q):
+        out = good(p, q)
+        pw, px, py, pz = np.moveaxis(p, -1, 0)
+        qw, qx, qy, qz = np.moveaxis(q, -1, 0)
+        out = out.copy()
+        out[..., 1] = pw * qx + px * qw - py * qz + pz * qy        # cross-product sign flipped
+        return out
+    monkeypatch.setattr(R, "quat_mul", bad)
+    _expect_fail(check_quaternion_product)
+
+
+def test_mutation_inverse_in_wrong_order(monkeypatch):
+    monkeypatch.setattr(R, "inverse_rotate", lambda y, rot: R.so4_apply(R.wht(y), rot, inverse=True))
+    _expect_fail(check_rotation_round_trip)
+
+
+def test_mutation_unnormalised_wht(monkeypatch):
+    monkeypatch.setattr(R, "wht", lambda x: np.asarray(x, np.float64) @ R.hadamard(x.shape[-1]).T)
+    _expect_fail(check_wht)
+
+
+def test_mutation_codebook_uniform_init_not_iterated(monkeypatch):
+    monkeypatch.setattr(R, "lloyd_max_unit_gaussian",
+                        lambda levels=8, **k: (np.linspace(-2, 2, 8), 0.5 * (np.linspace(-2, 2, 8)[:-1] + np.linspace(-2, 2, 8)[1:])))
+    _expect_fail(check_codebook)
+
+
+def test_mutation_quantize_ge_instead_of_gt(monkeypatch, codebook):
+    good = R.quantize
+
+    def bad(y32, t32):
+        codes, n = good(y32, t32)
+        thr = (t32[None, :] * n.reshape(-1, 1)).reshape(n.shape + (7,))
+        return np.sum(y32[..., :, None] >= thr[..., None, :], axis=-1).astype(np.uint8), n
+    monkeypatch.setattr(R, "quantize", bad)
+    _expect_fail(check_quantize, codebook)
