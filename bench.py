@@ -1,0 +1,194 @@
+"""Benchmark: packed 3-bit KV decode on one MI355X.
+
+Workload (default): the 30B-A3B-MoE-shaped GQA decode at 32768 tokens of
+context, 48 layers, 32 query heads, 4 KV heads, head dim 128, batch 1, K/V
+fp16 with four fixed outlier channels x8 (synthetic, seeded). Untimed set-up
+fills every layer's packed cache with 32767 tokens through the library's own
+bulk encode. One timed step = for each of the 48 layers: encode and append
+one new token (K and V) and run decode attention over the full 32768-token
+packed cache.
+
+Printed JSON line: value = packed K/V bytes read by the decode per step /
+step time (GB/s); roofline = the decode launch (split + merge kernels,
+bracketed by HIP events on the launch stream) against the 8 TB/s HBM peak;
+cpu_baseline = the CPU oracle's decode on a bounded sample of the same
+workload. The quantize-append rate is measured on the set-up's bulk encode.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROW_BYTES = 48 + 4          # packed codes + fp32 norm, one (token, KV head, K or V)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="moe30b_gqa_t32768")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the oracle's decode (float64, numpy) on (layer 0, KV head h) samples."""
+    import numpy as np
+    import iqinputs
+    from oracle import iqref as R
+
+    c32, t32, _ = R.codebook()
+    T = w.seq_len
+    rot = iqinputs.rotation_params(w.seed, 0, w.num_kv_heads)
+    k = iqinputs.kv(w.seed, 0, "k", T, w.num_kv_heads, w.outliers, w.dtype)
+    v = iqinputs.kv(w.seed, 0, "v", T, w.num_kv_heads, w.outliers, w.dtype)
+    q = iqinputs.queries(w.seed, 0, 1, w.num_q_heads)
+    kr, kn = R.encode_tokens(k, rot, t32)
+    vr, vn = R.encode_tokens(v, rot, t32)
+    st, ln = np.array([0], np.int32), np.array([T], np.int32)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        h = done % w.num_kv_heads
+        R.decode_attention(q, kr, kn, vr, vn, rot, st, ln, 1.0 / math.sqrt(128), c32, seqs=[0], heads=[h])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    nbytes = done * T * 2 * ROW_BYTES
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} (layer 0, KV head) decodes of {T} tokens x {w.group} query heads, "
+                      f"float64 numpy oracle, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import iqinputs
+    import quantized_kv_cache_wht_amd as iq
+
+    w = iqinputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, L, hq, hkv = w.seq_len, w.n_layers, w.num_q_heads, w.num_kv_heads
+    fdt = torch.float16 if w.dtype == "f16" else torch.float32
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device=dev)
+
+    def synth_kv(n, seed):
+        gen.manual_seed(seed)
+        x = torch.randn((n, hkv, 128), generator=gen, device=dev, dtype=torch.float32)
+        if w.outliers == "fixed_x8":
+            x[:, :, list(iqinputs.FIXED_OUTLIER_CHANNELS)] *= iqinputs.FIXED_OUTLIER_SCALE
+        else:
+            tdist = torch.distributions.StudentT(torch.tensor(3.0, device=dev))
+            for h in range(hkv):
+                ch = torch.randperm(128, generator=gen, device=dev)[:6]
+                x[:, h, ch] = tdist.sample((n, 6))
+        return x.to(fdt).contiguous()
+
+    # ---- set-up: fill the caches (untimed except the bulk-encode rate) ----
+    caches, qs = [], []
+    enc_ms = []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for l in range(L):
+        rot = torch.from_numpy(iqinputs.rotation_params(w.seed, l, hkv)).to(dev)
+        c = iq.PackedKVCache.allocate(hkv, T, rot, device=dev)
+        k, v = synth_kv(T - 1, 2 * l), synth_kv(T - 1, 2 * l + 1)
+        ev0.record(stream)
+        iq.iq_rotate_quantize_append(c, k, v, first_slot=0)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        enc_ms.append(ev0.elapsed_time(ev1))
+        del k, v
+        caches.append(c)
+        qs.append(torch.from_numpy(iqinputs.queries(w.seed, l, 1, hq)).to(dev))
+    enc_ms = sorted(enc_ms)[len(enc_ms) // 2]
+    append_tok_layers_per_s = (T - 1) / (enc_ms * 1e-3)
+
+    new_k = [synth_kv(1, 10_000 + l) for l in range(L)]
+    new_v = [synth_kv(1, 20_000 + l) for l in range(L)]
+    seq_start = torch.zeros(1, dtype=torch.int32, device=dev)
+    seq_len = torch.full((1,), T, dtype=torch.int32, device=dev)
+    ws = torch.empty(iq.iq_decode_workspace_bytes(1, hq, hkv, T), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((1, hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
+
+    n_ev = (args.steps) * L
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(timed_idx=None):
+        for l in range(L):
+            iq.iq_rotate_quantize_append(caches[l], new_k[l], new_v[l], first_slot=T - 1, stream=stream)
+            if timed_idx is not None:
+                starts[timed_idx * L + l].record(stream)
+            iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws,
+                                   stream=stream)
+            if timed_idx is not None:
+                ends[timed_idx * L + l].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_per_step = el * 1e3 / args.steps
+    dec_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+    bytes_per_launch = hkv * T * 2 * ROW_BYTES
+    achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
+    bytes_per_step = L * bytes_per_launch
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "packed-KV decode attention GB/s & % HBM peak; quantize-append tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "context": T, "layers": L, "num_q_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": 128, "batch": 1, "kv_input": w.dtype,
+                   "step": "per layer: append 1 token (K,V) + decode over the packed cache"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_launch_us": {"mean": round(float(dec_us.mean()), 3), "median": round(float(np.median(dec_us)), 3),
+                             "min": round(float(dec_us.min()), 3)},
+        "quantize_append_token_layers_per_s": round(append_tok_layers_per_s, 1),
+        "quantize_append_bulk_ms": round(enc_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

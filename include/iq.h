@@ -1,0 +1,152 @@
+/*
+ * iq.h -- C ABI of libiq: IsoQuant packed 3-bit KV cache on AMD MI355X (gfx950).
+ *
+ * The method (arXiv 2608.08081 "RotaryQuant" abstract; rebasdaily.com news
+ * article on RotaryQuant, section on attention over packed data):
+ *   encode   y = B . Hn . x   (normalised Walsh-Hadamard transform Hn, then
+ *                              block-diagonal SO(4) rotation B, 32 blocks of 4
+ *                              dims, each from two unit quaternions: 256
+ *                              parameters per head), n = ||y||, 3-bit
+ *                              Lloyd-Max code per coordinate for N(0, 1/128)
+ *                              (zhichai.net TurboQuant/RotorQuant essay,
+ *                              sections "Beta 分布的魔力" and
+ *                              "Lloyd-Max 最优量化"), packed 48 bytes per row.
+ *   decode   attention computed directly on the packed K/V in the rotated
+ *            domain, followed by one inverse rotation of the output.
+ *
+ * Conventions shared by every entry point:
+ *   - d = head_dim = 128 only (anything else: IQ_ERR_UNSUPPORTED).
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library never allocates, frees or retains them, and keeps no state
+ *     besides a lazily computed host copy of the codebook.
+ *   - All GPU work is enqueued asynchronously on `stream` (a hipStream_t;
+ *     NULL = the legacy default stream). A return of IQ_OK means the work was
+ *     launched, not that it has finished.
+ *   - Errors: every argument that can be checked on the host is checked
+ *     before anything is launched; a failed check returns a negative
+ *     iq_status and launches nothing. IQ_ERR_HIP reports a failed launch.
+ *     NaN/Inf inputs are not checked; they propagate.
+ *   - Packed row layout: code j of a 128-dim vector occupies bits [3j, 3j+3)
+ *     of a 384-bit little-endian bitstream (48 bytes; bytes 3i..3i+2 hold
+ *     codes 8i..8i+7). Code c is the c-th centroid in ascending order.
+ *   - Rotation parameters: float rot[num_kv_heads][32][8]; block b of head h
+ *     is rot[h][b] = {qL.w, qL.x, qL.y, qL.z, qR.w, qR.x, qR.y, qR.z} and maps
+ *     dims 4b..4b+3, read as a quaternion v = (w,x,y,z), to qL (x) v (x) conj(qR).
+ *     Quaternions are renormalised before use. K and V of a head share it.
+ */
+#ifndef IQ_H_
+#define IQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define IQ_API __attribute__((visibility("default")))
+#else
+#define IQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IQ_OK = 0,
+  IQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum, Hq % Hkv != 0 ... */
+  IQ_ERR_UNSUPPORTED = -2,   /* head_dim != 128, group size > 16 */
+  IQ_ERR_CAPACITY = -3,      /* contiguous slot range outside [0, capacity) */
+  IQ_ERR_WORKSPACE = -4,     /* workspace smaller than iq_decode_workspace_bytes() */
+  IQ_ERR_HIP = -5            /* a HIP launch failed */
+} iq_status;
+
+typedef enum { IQ_F32 = 0, IQ_F16 = 1 } iq_dtype;
+
+/* One layer of the packed cache. All pointers are device memory. */
+typedef struct {
+  int32_t head_dim;       /* must be 128 */
+  int32_t num_kv_heads;   /* Hkv >= 1 */
+  int32_t capacity;       /* rows per KV head (one flat token axis shared by all sequences) */
+  uint8_t* k_codes;       /* [num_kv_heads][capacity][48], 16-byte aligned */
+  uint8_t* v_codes;       /* [num_kv_heads][capacity][48], 16-byte aligned */
+  float* k_norms;         /* [num_kv_heads][capacity] */
+  float* v_norms;         /* [num_kv_heads][capacity] */
+  const float* rot;       /* [num_kv_heads][32][8] */
+} iq_cache_view;
+
+/* Human-readable name of a status code (static string). */
+IQ_API const char* iq_status_string(iq_status s);
+
+/* Host only. The codebook: 8 Lloyd-Max centroids of N(0, 1/128) in ascending
+ * order and the 7 cell boundaries (midpoints), computed in double and rounded
+ * to float (zhichai.net essay, section "Lloyd-Max 最优量化"). Both arrays are
+ * host memory written by the call. */
+IQ_API iq_status iq_codebook(float centroids[8], float thresholds[7]);
+
+/* Rotate fp32 vectors with the per-head rotation (the first half of the
+ * encode; the same transform is applied to queries before scoring).
+ *   x, y   device float [n_tokens][num_heads][128]; y may equal x.
+ *   rot    device float [num_heads][32][8].
+ *   inverse = 0: y = B . Hn . x;  inverse = 1: y = Hn . B^T . x.           */
+IQ_API iq_status iq_rotate(const float* rot, int32_t num_heads, const float* x, float* y,
+                    int32_t n_tokens, int32_t inverse, void* stream);
+
+/* Quantize and pack vectors that are already rotated (the second half of the
+ * encode: norm, 3-bit codes, packing).
+ *   y      device float [n_vectors][128] (rotated coordinates).
+ *   codes  device uint8 [n_vectors][48]; norms device float [n_vectors].
+ * n = fl32(sqrt(sum y_j^2)) with a double-precision sum; code_j =
+ * #{k : y_j > fl32(t_k * n)}. A zero vector gives n = 0 and all-zero codes. */
+IQ_API iq_status iq_quantize_pack(const float* y, int64_t n_vectors, uint8_t* codes, float* norms,
+                           void* stream);
+
+/* Rotate, quantize and pack new K and V tokens into the cache (the pages'
+ * quantize-on-insert; RotorQuant page, deferred quantization section).
+ *   k, v        device [n_tokens][num_kv_heads][128] of in_dtype (f32 or f16).
+ *   slots       device int32 [n_tokens] destination rows, or NULL for the
+ *               contiguous rows first_slot .. first_slot + n_tokens - 1
+ *               (checked against capacity on the host). With `slots`, a slot
+ *               outside [0, capacity) is skipped on the device (nothing written).
+ * Writes view->k_codes/v_codes rows and view->k_norms/v_norms entries.
+ * n_tokens = 0 is a no-op. */
+IQ_API iq_status iq_rotate_quantize_append(const iq_cache_view* view, const void* k, const void* v,
+                                    iq_dtype in_dtype, int32_t n_tokens, int32_t first_slot,
+                                    const int32_t* slots, void* stream);
+
+/* Reconstruct K and V rows explicitly: x_hat = n . Hn . B^T . c[code]
+ * (the unfused path; RotorQuant page, inverse-rotation fix for V).
+ *   rows first_slot .. first_slot + n_tokens - 1 of every KV head
+ *   k_out, v_out  device [n_tokens][num_kv_heads][128] of out_dtype; either
+ *                 may be NULL to skip it. */
+IQ_API iq_status iq_dequantize(const iq_cache_view* view, int32_t first_slot, int32_t n_tokens,
+                        iq_dtype out_dtype, void* k_out, void* v_out, void* stream);
+
+/* Bytes of workspace iq_decode_attention needs for these sizes (0 if the
+ * sizes are invalid). */
+IQ_API size_t iq_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t max_seq_len);
+
+/* Decode attention on the packed cache (news article on RotaryQuant:
+ * scores on packed K, softmax, accumulation from packed V, inverse rotation;
+ * zhichai.net essay: softmax(Q K^T / sqrt(d)) V).
+ *   q          device float [n_seqs][num_q_heads][128], one query per sequence.
+ *   seq_start  device int32 [n_seqs], first cache row of each sequence.
+ *   seq_len    device int32 [n_seqs], rows of each sequence; each must be
+ *              <= max_seq_len (a host-side bound that sizes the launch).
+ *   scale      softmax scale (1/sqrt(128) for plain attention).
+ *   out        device float [n_seqs][num_q_heads][128].
+ *   workspace  device memory of at least iq_decode_workspace_bytes() bytes,
+ *              16-byte aligned; its contents need no initialisation.
+ * Query head g reads KV head g / (num_q_heads / num_kv_heads); the group size
+ * must be 1, 2, 4, 8 or 16. A sequence with seq_len = 0 gets a zero output. A sequence
+ * whose rows fall outside [0, capacity), or whose length exceeds max_seq_len,
+ * gets NaN outputs (no out-of-bounds read happens). */
+IQ_API iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t num_q_heads,
+                              const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                              int32_t max_seq_len, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQ_H_ */

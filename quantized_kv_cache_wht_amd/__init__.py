@@ -1,0 +1,239 @@
+"""IsoQuant packed 3-bit KV cache for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libiq.so`` (declared in
+``include/iq.h``). Every step of the method runs in the library's HIP
+kernels; this module only checks tensor shapes and dtypes, passes device
+pointers and the current HIP stream, and turns error codes into exceptions.
+PyTorch supplies device memory and streams. There is no CPU fallback: if the
+library has not been built, importing the binding's functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import numpy as np
+import torch
+
+HEAD_DIM = 128
+ROW_BYTES = 48
+ROT_PARAMS_PER_HEAD = 256
+
+IQ_OK = 0
+IQ_F32 = 0
+IQ_F16 = 1
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiq.so")
+_lib = None
+
+
+class IqError(RuntimeError):
+    """A libiq call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class CacheView(ctypes.Structure):
+    """Mirror of ``iq_cache_view``."""
+    _fields_ = [
+        ("head_dim", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("k_norms", ctypes.c_void_p),
+        ("v_norms", ctypes.c_void_p),
+        ("rot", ctypes.c_void_p),
+    ]
+
+
+_SIGNATURES = {
+    "iq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "iq_codebook": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "iq_rotate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "iq_quantize_pack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
+    "iq_rotate_quantize_append": (ctypes.c_int, [ctypes.POINTER(CacheView), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
+    "iq_dequantize": (ctypes.c_int, [ctypes.POINTER(CacheView), ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "iq_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32]),
+    "iq_decode_attention": (ctypes.c_int, [ctypes.POINTER(CacheView), ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libiq (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libiq.so not found at {_LIB_PATH}; build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().iq_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != IQ_OK:
+        raise IqError(fn, status)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# --------------------------------------------------------------------------
+def iq_codebook():
+    """(centroids float32[8], thresholds float32[7]) as the library computes them (host call)."""
+    c = np.zeros(8, np.float32)
+    t = np.zeros(7, np.float32)
+    _check("iq_codebook", lib().iq_codebook(c.ctypes.data, t.ctypes.data))
+    return c, t
+
+
+@dataclasses.dataclass
+class PackedKVCache:
+    """Device buffers of one layer of the packed cache (allocated with torch)."""
+    k_codes: torch.Tensor     # uint8 [Hkv][capacity][48]
+    v_codes: torch.Tensor
+    k_norms: torch.Tensor     # float32 [Hkv][capacity]
+    v_norms: torch.Tensor
+    rot: torch.Tensor         # float32 [Hkv][32][8]
+
+    @classmethod
+    def allocate(cls, num_kv_heads: int, capacity: int, rot: torch.Tensor, device="cuda") -> "PackedKVCache":
+        z8 = lambda: torch.zeros((num_kv_heads, capacity, ROW_BYTES), dtype=torch.uint8, device=device)
+        zf = lambda: torch.zeros((num_kv_heads, capacity), dtype=torch.float32, device=device)
+        rot = rot.to(device=device, dtype=torch.float32).contiguous()
+        if tuple(rot.shape) != (num_kv_heads, 32, 8):
+            raise ValueError("rot must be [num_kv_heads][32][8]")
+        return cls(z8(), z8(), zf(), zf(), rot)
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_codes.shape[0]
+
+    @property
+    def capacity(self) -> int:
+        return self.k_codes.shape[1]
+
+    def view(self) -> CacheView:
+        for name in ("k_codes", "v_codes"):
+            _dev(getattr(self, name), torch.uint8, name)
+        for name in ("k_norms", "v_norms", "rot"):
+            _dev(getattr(self, name), torch.float32, name)
+        return CacheView(HEAD_DIM, self.num_kv_heads, self.capacity, self.k_codes.data_ptr(),
+                         self.v_codes.data_ptr(), self.k_norms.data_ptr(), self.v_norms.data_ptr(),
+                         self.rot.data_ptr())
+
+
+def iq_rotate(rot: torch.Tensor, x: torch.Tensor, inverse: bool = False, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """y = B Hn x (or Hn B^T x) for x float32 [n_tokens][num_heads][128]."""
+    n_tok, heads, d = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _check("iq_rotate", lib().iq_rotate(_dev(rot, torch.float32, "rot"), heads, _dev(x, torch.float32, "x"),
+                                        _dev(out, torch.float32, "out"), n_tok, int(bool(inverse)),
+                                        _stream(stream)))
+    return out
+
+
+def iq_quantize_pack(y: torch.Tensor, stream=None):
+    """Codes uint8 [n][48] and norms float32 [n] of rotated vectors y float32 [n][128]."""
+    n = y.shape[0]
+    codes = torch.empty((n, ROW_BYTES), dtype=torch.uint8, device=y.device)
+    norms = torch.empty((n,), dtype=torch.float32, device=y.device)
+    _check("iq_quantize_pack", lib().iq_quantize_pack(_dev(y, torch.float32, "y"), n, codes.data_ptr(),
+                                                      norms.data_ptr(), _stream(stream)))
+    return codes, norms
+
+
+def _in_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return IQ_F32
+    if t.dtype == torch.float16:
+        return IQ_F16
+    raise TypeError("K/V must be float32 or float16")
+
+
+def iq_rotate_quantize_append(cache: PackedKVCache, k: torch.Tensor, v: torch.Tensor, first_slot: int = 0,
+                              slots: torch.Tensor | None = None, stream=None) -> None:
+    """Encode new tokens k, v [n_tokens][Hkv][128] into the cache rows."""
+    n_tok = k.shape[0]
+    dt = _in_dtype(k)
+    if v.dtype != k.dtype or v.shape != k.shape:
+        raise ValueError("k and v must match")
+    sp = _dev(slots, torch.int32, "slots") if slots is not None else None
+    view = cache.view()
+    _check("iq_rotate_quantize_append",
+           lib().iq_rotate_quantize_append(ctypes.byref(view), _dev(k, k.dtype, "k"), _dev(v, v.dtype, "v"), dt,
+                                           n_tok, first_slot, sp, _stream(stream)))
+
+
+def iq_dequantize(cache: PackedKVCache, first_slot: int, n_tokens: int, out_dtype=torch.float32, stream=None):
+    """Explicit reconstruction of K and V rows: two tensors [n_tokens][Hkv][128]."""
+    dt = {torch.float32: IQ_F32, torch.float16: IQ_F16}[out_dtype]
+    shape = (n_tokens, cache.num_kv_heads, HEAD_DIM)
+    k_out = torch.empty(shape, dtype=out_dtype, device=cache.k_codes.device)
+    v_out = torch.empty(shape, dtype=out_dtype, device=cache.k_codes.device)
+    view = cache.view()
+    _check("iq_dequantize", lib().iq_dequantize(ctypes.byref(view), first_slot, n_tokens, dt, k_out.data_ptr(),
+                                                v_out.data_ptr(), _stream(stream)))
+    return k_out, v_out
+
+
+def iq_decode_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int) -> int:
+    return int(lib().iq_decode_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, max_seq_len))
+
+
+def iq_decode_attention(cache: PackedKVCache, q: torch.Tensor, seq_start: torch.Tensor, seq_len: torch.Tensor,
+                        max_seq_len: int, scale: float | None = None, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention on the packed cache: q float32 [n_seqs][Hq][128] -> out [n_seqs][Hq][128]."""
+    n_seqs, hq, _ = q.shape
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    need = iq_decode_workspace_bytes(n_seqs, hq, cache.num_kv_heads, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    view = cache.view()
+    _check("iq_decode_attention",
+           lib().iq_decode_attention(ctypes.byref(view), _dev(q, torch.float32, "q"), hq,
+                                     _dev(seq_start, torch.int32, "seq_start"), _dev(seq_len, torch.int32, "seq_len"),
+                                     n_seqs, max_seq_len, scale, _dev(out, torch.float32, "out"),
+                                     _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return out

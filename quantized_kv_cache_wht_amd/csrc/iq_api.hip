@@ -1,0 +1,194 @@
+// C ABI of libiq (declared in include/iq.h): host-side validation, the
+// codebook, and kernel launches. No allocation, no retained device state.
+#include <math.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "../../include/iq.h"
+#include "iq_launch.h"
+
+namespace iq {
+
+// Lloyd-Max quantizer of N(0,1) with 8 levels, solved on the positive half
+// (the optimum is symmetric): cells (0, b1], (b1, b2], (b2, b3], (b3, inf)
+// with b_k the midpoints of neighbouring levels, each level the Gaussian mean
+// of its cell, iterated to a fixed point (zhichai.net essay, section
+// "Lloyd-Max 最优量化": assign to the nearest level, move each level to the
+// mean of what it received, repeat).
+static void lloyd_max_positive_half(double level[4], double bound[3]) {
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  auto pdf = [&](double x) { return isinf(x) ? 0.0 : inv_sqrt_2pi * exp(-0.5 * x * x); };
+  auto upper_tail = [](double x) { return isinf(x) ? 0.0 : 0.5 * erfc(x * 0.70710678118654752440); };
+  double y[4] = {0.25, 0.75, 1.25, 2.0};
+  for (int it = 0; it < 200000; ++it) {
+    const double e[5] = {0.0, 0.5 * (y[0] + y[1]), 0.5 * (y[1] + y[2]), 0.5 * (y[2] + y[3]), INFINITY};
+    double ny[4];
+    for (int k = 0; k < 4; ++k) ny[k] = (pdf(e[k]) - pdf(e[k + 1])) / (upper_tail(e[k]) - upper_tail(e[k + 1]));
+    bool same = true;
+    for (int k = 0; k < 4; ++k) {
+      if (ny[k] != y[k]) same = false;
+      y[k] = ny[k];
+    }
+    if (same) break;
+  }
+  for (int k = 0; k < 4; ++k) level[k] = y[k];
+  for (int k = 0; k < 3; ++k) bound[k] = 0.5 * (y[k] + y[k + 1]);
+}
+
+static const Codebook& codebook() {
+  static Codebook cb;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    double lv[4], bd[3];
+    lloyd_max_positive_half(lv, bd);
+    const double s = 1.0 / sqrt(128.0);       // N(0, 1/d), d = 128
+    for (int k = 0; k < 4; ++k) {
+      cb.c[4 + k] = static_cast<float>(lv[k] * s);
+      cb.c[3 - k] = -cb.c[4 + k];
+    }
+    cb.t[3] = 0.0f;
+    for (int k = 0; k < 3; ++k) {
+      cb.t[4 + k] = static_cast<float>(bd[k] * s);
+      cb.t[2 - k] = -cb.t[4 + k];
+    }
+  });
+  return cb;
+}
+
+static iq_status hip_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
+
+static iq_status check_view(const iq_cache_view* v) {
+  if (v == nullptr) return IQ_ERR_INVALID_ARG;
+  if (v->head_dim != kDim) return IQ_ERR_UNSUPPORTED;
+  if (v->num_kv_heads < 1 || v->capacity < 0) return IQ_ERR_INVALID_ARG;
+  if (!v->k_codes || !v->v_codes || !v->k_norms || !v->v_norms || !v->rot) return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(v->k_codes) | reinterpret_cast<uintptr_t>(v->v_codes)) & 15u)
+    return IQ_ERR_INVALID_ARG;
+  return IQ_OK;
+}
+
+}  // namespace iq
+
+using namespace iq;
+
+extern "C" {
+
+const char* iq_status_string(iq_status s) {
+  switch (s) {
+    case IQ_OK: return "ok";
+    case IQ_ERR_INVALID_ARG: return "invalid argument";
+    case IQ_ERR_UNSUPPORTED: return "unsupported shape";
+    case IQ_ERR_CAPACITY: return "slot range outside the cache capacity";
+    case IQ_ERR_WORKSPACE: return "workspace too small";
+    case IQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+iq_status iq_codebook(float centroids[8], float thresholds[7]) {
+  if (!centroids || !thresholds) return IQ_ERR_INVALID_ARG;
+  const Codebook& cb = codebook();
+  for (int k = 0; k < 8; ++k) centroids[k] = cb.c[k];
+  for (int k = 0; k < 7; ++k) thresholds[k] = cb.t[k];
+  return IQ_OK;
+}
+
+iq_status iq_rotate(const float* rot, int32_t num_heads, const float* x, float* y, int32_t n_tokens,
+                    int32_t inverse, void* stream) {
+  if (!rot || !x || !y || num_heads < 1 || n_tokens < 0 || (inverse != 0 && inverse != 1))
+    return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) return IQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return IQ_OK;
+  RotateArgs a{x, y, rot, n_tokens, num_heads};
+  return hip_status(launch_rotate(a, inverse != 0, static_cast<hipStream_t>(stream)));
+}
+
+iq_status iq_quantize_pack(const float* y, int64_t n_vectors, uint8_t* codes, float* norms, void* stream) {
+  if (!y || !codes || !norms || n_vectors < 0) return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(y) & 15u) || (reinterpret_cast<uintptr_t>(codes) & 3u))
+    return IQ_ERR_INVALID_ARG;
+  if (n_vectors == 0) return IQ_OK;
+  QuantArgs a{y, codes, norms, n_vectors, codebook()};
+  return hip_status(launch_quantize_pack(a, static_cast<hipStream_t>(stream)));
+}
+
+iq_status iq_rotate_quantize_append(const iq_cache_view* view, const void* k, const void* v,
+                                    iq_dtype in_dtype, int32_t n_tokens, int32_t first_slot,
+                                    const int32_t* slots, void* stream) {
+  iq_status st = check_view(view);
+  if (st != IQ_OK) return st;
+  if (in_dtype != IQ_F32 && in_dtype != IQ_F16) return IQ_ERR_INVALID_ARG;
+  if (n_tokens < 0) return IQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return IQ_OK;
+  if (!k || !v) return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) return IQ_ERR_INVALID_ARG;
+  if (!slots && (first_slot < 0 || static_cast<int64_t>(first_slot) + n_tokens > view->capacity))
+    return IQ_ERR_CAPACITY;
+  AppendArgs a{k, v, slots, view->rot, view->k_codes, view->v_codes, view->k_norms, view->v_norms,
+               n_tokens, first_slot, view->num_kv_heads, view->capacity, codebook()};
+  return hip_status(launch_append(a, in_dtype == IQ_F16, static_cast<hipStream_t>(stream)));
+}
+
+iq_status iq_dequantize(const iq_cache_view* view, int32_t first_slot, int32_t n_tokens, iq_dtype out_dtype,
+                        void* k_out, void* v_out, void* stream) {
+  iq_status st = check_view(view);
+  if (st != IQ_OK) return st;
+  if (out_dtype != IQ_F32 && out_dtype != IQ_F16) return IQ_ERR_INVALID_ARG;
+  if (n_tokens < 0) return IQ_ERR_INVALID_ARG;
+  if (first_slot < 0 || static_cast<int64_t>(first_slot) + n_tokens > view->capacity) return IQ_ERR_CAPACITY;
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15u) return IQ_ERR_INVALID_ARG;
+  if (n_tokens == 0 || (!k_out && !v_out)) return IQ_OK;
+  DequantArgs a{view->k_codes, view->v_codes, view->k_norms, view->v_norms, view->rot, k_out, v_out,
+                first_slot, n_tokens, view->num_kv_heads, view->capacity, codebook()};
+  return hip_status(launch_dequant(a, out_dtype == IQ_F16, static_cast<hipStream_t>(stream)));
+}
+
+static bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+size_t iq_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
+  if (n_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 0) return 0;
+  int32_t split_len, n_splits;
+  decode_plan(n_seqs, num_kv_heads, max_seq_len, &split_len, &n_splits);
+  return decode_workspace_floats(n_seqs, num_q_heads, n_splits) * sizeof(float);
+}
+
+iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t num_q_heads,
+                              const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                              int32_t max_seq_len, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  iq_status st = check_view(view);
+  if (st != IQ_OK) return st;
+  if (n_seqs < 0 || max_seq_len < 0 || num_q_heads < 1) return IQ_ERR_INVALID_ARG;
+  if (num_q_heads % view->num_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / view->num_kv_heads;
+  if (!group_supported(group)) return IQ_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return IQ_OK;
+  if (!q || !seq_start || !seq_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return IQ_ERR_INVALID_ARG;
+  if (workspace_bytes < iq_decode_workspace_bytes(n_seqs, num_q_heads, view->num_kv_heads, max_seq_len))
+    return IQ_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.k_codes = view->k_codes;
+  a.v_codes = view->v_codes;
+  a.k_norms = view->k_norms;
+  a.v_norms = view->v_norms;
+  a.rot = view->rot;
+  a.q = q;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.n_seqs = n_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = view->num_kv_heads;
+  a.group = group;
+  a.capacity = view->capacity;
+  a.max_seq_len = max_seq_len;
+  decode_plan(n_seqs, view->num_kv_heads, max_seq_len, &a.split_len, &a.n_splits);
+  a.qscale = scale * 1.4426950408889634f;   // log2(e): scores kept in base 2
+  a.cb = codebook();
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// Device-side building blocks shared by the libiq kernels (gfx950, wave64).
+//
+// Vector layout used by every per-vector kernel: four consecutive lanes own
+// one 128-dim vector, lane part p = lane & 3 holding the 32 contiguous dims
+// 32p .. 32p+31. The Walsh-Hadamard butterflies over index bits 0..4 then stay
+// inside a lane (registers), and the two remaining stages (bits 5 and 6) pair
+// lanes p^1 and p^2, which DPP quad permutations reach without LDS. Each SO(4)
+// block (4 contiguous dims) lies inside one lane, and the 32 codes of a lane
+// are exactly bytes 12p .. 12p+11 of the packed row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iq {
+
+constexpr int kDim = 128;
+constexpr int kBlocks = 32;          // SO(4) blocks per vector
+constexpr int kRowBytes = 48;        // 128 x 3 bits
+constexpr int kPerLane = 32;         // dims per lane (4 lanes per vector)
+
+struct Codebook {
+  float c[8];   // centroids of N(0, 1/128), ascending
+  float t[7];   // cell boundaries (midpoints), ascending; t[3] == 0
+};
+
+// ---------------------------------------------------------------- DPP ----
+// quad_perm selectors: lane i of every quad reads lane sel[i] of that quad.
+constexpr int kQuadXor1 = 0xB1;   // [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // [2,3,0,1]
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
+}
+
+// ---------------------------------------------------------------- WHT ----
+// Unnormalised Sylvester Hadamard transform of the 128-vector held by a quad
+// of lanes (x = this lane's 32 dims). The 1/sqrt(128) is folded into the SO(4)
+// matrices by the callers.
+__device__ __forceinline__ void wht128_quad(float (&x)[kPerLane], int part) {
+#pragma unroll
+  for (int h = 1; h < kPerLane; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+  // bit 5: partner part ^ 1; the lane with the bit set keeps (partner - self)
+  {
+    const float s = (part & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) x[i] = __builtin_fmaf(x[i], s, dpp_f32<kQuadXor1>(x[i]));
+  }
+  {
+    const float s = (part & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) x[i] = __builtin_fmaf(x[i], s, dpp_f32<kQuadXor2>(x[i]));
+  }
+}
+
+// ------------------------------------------------------------- SO(4) ----
+// Hamilton product of quaternions (w, x, y, z).
+__device__ __forceinline__ void qmul(const float a[4], const float b[4], float r[4]) {
+  r[0] = a[0] * b[0] - a[1] * b[1] - a[2] * b[2] - a[3] * b[3];
+  r[1] = a[0] * b[1] + a[1] * b[0] + a[2] * b[3] - a[3] * b[2];
+  r[2] = a[0] * b[2] - a[1] * b[3] + a[2] * b[0] + a[3] * b[1];
+  r[3] = a[0] * b[3] + a[1] * b[2] - a[2] * b[1] + a[3] * b[0];
+}
+
+// Row-major 4x4 matrix of v -> qL (x) v (x) conj(qR), times `scale`, from the
+// 8 stored parameters of one block (quaternions renormalised here).
+__device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m[16]) {
+  float ql[4], qr[4];
+  float nl = 0.f, nr = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ql[i] = p8[i];
+    qr[i] = p8[4 + i];
+    nl += ql[i] * ql[i];
+    nr += qr[i] * qr[i];
+  }
+  nl = 1.0f / sqrtf(nl);
+  nr = 1.0f / sqrtf(nr);
+  const float qrc[4] = {qr[0] * nr, -qr[1] * nr, -qr[2] * nr, -qr[3] * nr};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ql[i] *= nl;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float e[4] = {0.f, 0.f, 0.f, 0.f};
+    e[c] = 1.0f;
+    float t[4], col[4];
+    qmul(ql, e, t);
+    qmul(t, qrc, col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[r] * scale;
+  }
+}
+
+// Fill LDS with the 32 block matrices of one head (row-major, scaled by
+// 1/sqrt(128)). Must be called by all threads of the block; threads 0..31 work.
+__device__ __forceinline__ void load_head_matrices(const float* __restrict__ rot_head, float* sm) {
+  const int t = threadIdx.x;
+  if (t < kBlocks) {
+    float m[16];
+    so4_matrix(rot_head + t * 8, 0.08838834764831845f, m);   // 1/sqrt(128)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm[t * 16 + i] = m[i];
+  }
+}
+
+// y_b = M_b y_b for this lane's 8 blocks (transpose = use M_b^T).
+template <bool kTranspose>
+__device__ __forceinline__ void so4_apply_lane(float (&x)[kPerLane], const float* sm, int part) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const float4* mp = reinterpret_cast<const float4*>(sm + (part * 8 + b) * 16);
+    const float4 r0 = mp[0], r1 = mp[1], r2 = mp[2], r3 = mp[3];
+    const float m[16] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w,
+                         r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
+    const float v0 = x[4 * b], v1 = x[4 * b + 1], v2 = x[4 * b + 2], v3 = x[4 * b + 3];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a0 = kTranspose ? m[0 * 4 + r] : m[r * 4 + 0];
+      const float a1 = kTranspose ? m[1 * 4 + r] : m[r * 4 + 1];
+      const float a2 = kTranspose ? m[2 * 4 + r] : m[r * 4 + 2];
+      const float a3 = kTranspose ? m[3 * 4 + r] : m[r * 4 + 3];
+      x[4 * b + r] = __builtin_fmaf(a3, v3, __builtin_fmaf(a2, v2, __builtin_fmaf(a1, v1, a0 * v0)));
+    }
+  }
+}
+
+// --------------------------------------------------- norm and codes ----
+// n = fl32(sqrt(sum y^2)), sum in double over the quad. Every lane of the quad
+// gets the same value.
+__device__ __forceinline__ float quad_norm(const float (&y)[kPerLane]) {
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const double d = static_cast<double>(y[i]);
+    s = __builtin_fma(d, d, s);
+  }
+  s += dpp_f64<kQuadXor1>(s);
+  s += dpp_f64<kQuadXor2>(s);
+  return __double2float_rn(sqrt(s));
+}
+
+// code = #{k : y > thr_k}. The thresholds are symmetric (thr_{6-k} = -thr_k,
+// thr_3 = 0), so with a = |y|: y > 0 gives 4 + #{k>=4 : a > thr_k}, and
+// y <= 0 gives 3 - #{k>=4 : a >= thr_k}.
+__device__ __forceinline__ uint32_t code_of(float y, float t4, float t5, float t6) {
+  const float a = fabsf(y);
+  if (y > 0.0f) {
+    return 4u + (a > t4) + (a > t5) + (a > t6);
+  }
+  // y <= 0 or NaN. For NaN every comparison is false, giving code 3 - 0 = 3;
+  // the definition gives 0, so NaN is handled explicitly.
+  if (y != y) return 0u;
+  return 3u - ((a >= t4) + (a >= t5) + (a >= t6));
+}
+
+// Pack 32 codes (3 bits each) into 3 dwords, code i at bits [3i, 3i+3).
+__device__ __forceinline__ void pack32(const uint32_t (&c)[kPerLane], uint32_t (&w)[3]) {
+  uint64_t lo = 0, hi = 0;   // 96-bit accumulator
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int bit = 3 * i;
+    if (bit < 64) {
+      lo |= static_cast<uint64_t>(c[i]) << bit;
+      if (bit > 61) hi |= static_cast<uint64_t>(c[i]) >> (64 - bit);
+    } else {
+      hi |= static_cast<uint64_t>(c[i]) << (bit - 64);
+    }
+  }
+  w[0] = static_cast<uint32_t>(lo);
+  w[1] = static_cast<uint32_t>(lo >> 32);
+  w[2] = static_cast<uint32_t>(hi);
+}
+
+// Code i (0..31) of a 96-bit group held in 3 dwords.
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[3], int i) {
+  const int bit = 3 * i;
+  const int word = bit >> 5, off = bit & 31;
+  if (off <= 29) return (w[word] >> off) & 7u;
+  return __builtin_amdgcn_alignbit(w[word + 1], w[word], off) & 7u;
+}
+
+// Centroid of a code by selects (no dynamically indexed arrays): the codebook
+// is symmetric, c[v] = c[4 + (v & 3)] for v >= 4 and -c[7 - v] for v < 4.
+__device__ __forceinline__ float centroid(uint32_t v, const Codebook& cb) {
+  const uint32_t m = v & 3u;
+  const bool neg = v < 4u;
+  const uint32_t idx = neg ? (3u - m) : m;
+  const float lo = (idx & 1u) ? cb.c[5] : cb.c[4];
+  const float hi = (idx & 1u) ? cb.c[7] : cb.c[6];
+  const float mag = (idx & 2u) ? hi : lo;
+  return neg ? -mag : mag;
+}
+
+}  // namespace iq

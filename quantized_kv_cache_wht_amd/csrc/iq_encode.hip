@@ -1,0 +1,262 @@
+// Encode-side kernels of libiq: rotate (WHT then SO(4)), quantize to 3-bit
+// Lloyd-Max codes with a per-vector norm, pack; plus the inverse direction.
+//
+// The method is the encode of IsoQuant (arXiv 2608.08081 "RotaryQuant"
+// abstract: Walsh-Hadamard transform followed by block-diagonal SO(4)
+// rotations, then 3-bit scalar quantization; zhichai.net TurboQuant/RotorQuant
+// essay, sections "Beta 分布的魔力" and "Lloyd-Max 最优量化" for the unit-norm
+// Gaussian codebook; section "真正的瓶颈" for reading packed codes in whole
+// words rather than byte by byte).
+//
+// Launch shape: 256 threads = 64 vectors per pass (4 lanes per vector, see
+// iq_device.h); every block works on one KV head (its 32 SO(4) matrices sit in
+// LDS) and strides over tokens. All kernels keep every lane alive through the
+// DPP butterflies and only mask loads and stores.
+#include "iq_device.h"
+#include "iq_launch.h"
+
+namespace iq {
+
+constexpr int kEncThreads = 256;
+constexpr int kVecPerBlock = kEncThreads / 4;
+
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* __restrict__ src, bool ok, float (&x)[kPerLane]);
+
+template <>
+__device__ __forceinline__ void load_vec<float>(const float* __restrict__ src, bool ok, float (&x)[kPerLane]) {
+#pragma unroll
+  for (int i = 0; i < kPerLane / 4; ++i) {
+    float4 v = ok ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_vec<_Float16>(const _Float16* __restrict__ src, bool ok, float (&x)[kPerLane]) {
+  typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int i = 0; i < kPerLane / 8; ++i) {
+    half8 v;
+    if (ok) {
+      v = reinterpret_cast<const half8*>(src)[i];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[8 * i + j] = static_cast<float>(v[j]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_vec(T* __restrict__ dst, const float (&x)[kPerLane]);
+
+template <>
+__device__ __forceinline__ void store_vec<float>(float* __restrict__ dst, const float (&x)[kPerLane]) {
+#pragma unroll
+  for (int i = 0; i < kPerLane / 4; ++i)
+    reinterpret_cast<float4*>(dst)[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+}
+
+template <>
+__device__ __forceinline__ void store_vec<_Float16>(_Float16* __restrict__ dst, const float (&x)[kPerLane]) {
+  typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int i = 0; i < kPerLane / 8; ++i) {
+    half8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = static_cast<_Float16>(x[8 * i + j]);
+    reinterpret_cast<half8*>(dst)[i] = v;
+  }
+}
+
+// Norm, codes and the lane's 3 packed dwords of a rotated vector.
+__device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], const Codebook& cb,
+                                                    uint32_t (&w)[3]) {
+  const float n = quad_norm(y);
+  const float t4 = __fmul_rn(cb.t[4], n), t5 = __fmul_rn(cb.t[5], n), t6 = __fmul_rn(cb.t[6], n);
+  uint32_t c[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) c[i] = code_of(y[i], t4, t5, t6);
+  pack32(c, w);
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// Append: x (K or V of new tokens) -> codes + norms in the cache.
+// grid = (token blocks, num_kv_heads, 2 [K, V])
+template <typename T>
+__global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
+  __shared__ __align__(16) float sm[kBlocks * 16];
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  __syncthreads();
+
+  const T* __restrict__ src = static_cast<const T*>(is_v ? a.v : a.k);
+  uint8_t* __restrict__ codes = is_v ? a.v_codes : a.k_codes;
+  float* __restrict__ norms = is_v ? a.v_norms : a.k_norms;
+  const int part = threadIdx.x & 3;
+  const int vec = threadIdx.x >> 2;
+
+  for (int tok0 = blockIdx.x * kVecPerBlock; tok0 < a.n_tokens; tok0 += gridDim.x * kVecPerBlock) {
+    const int tok = tok0 + vec;
+    const bool ok = tok < a.n_tokens;
+    float x[kPerLane];
+    load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
+    wht128_quad(x, part);
+    so4_apply_lane<false>(x, sm, part);
+    uint32_t w[3];
+    const float n = quantize_pack_lane(x, a.cb, w);
+    if (ok) {
+      const int slot = a.slots ? a.slots[tok] : a.first_slot + tok;
+      if (slot >= 0 && slot < a.capacity) {
+        const size_t row = static_cast<size_t>(h) * a.capacity + slot;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kRowBytes + part * 12);
+        dst[0] = w[0];
+        dst[1] = w[1];
+        dst[2] = w[2];
+        if (part == 0) norms[row] = n;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rotate fp32 vectors: y = B Hn x (forward) or x = Hn B^T y (inverse).
+// grid = (token blocks, num_heads)
+template <bool kInverse>
+__global__ __launch_bounds__(kEncThreads) void rotate_kernel(RotateArgs a) {
+  __shared__ __align__(16) float sm[kBlocks * 16];
+  const int h = blockIdx.y;
+  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  __syncthreads();
+  const int part = threadIdx.x & 3;
+  const int vec = threadIdx.x >> 2;
+  for (int tok0 = blockIdx.x * kVecPerBlock; tok0 < a.n_tokens; tok0 += gridDim.x * kVecPerBlock) {
+    const int tok = tok0 + vec;
+    const bool ok = tok < a.n_tokens;
+    const size_t off = (static_cast<size_t>(ok ? tok : 0) * a.num_heads + h) * kDim + part * kPerLane;
+    float x[kPerLane];
+    load_vec<float>(a.x + off, ok, x);
+    if (kInverse) {
+      so4_apply_lane<true>(x, sm, part);
+      wht128_quad(x, part);
+    } else {
+      wht128_quad(x, part);
+      so4_apply_lane<false>(x, sm, part);
+    }
+    if (ok) store_vec<float>(a.y + off, x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantize + pack already-rotated fp32 vectors (flat [n][128] -> [n][48], [n]).
+__global__ __launch_bounds__(kEncThreads) void quantize_pack_kernel(QuantArgs a) {
+  const int part = threadIdx.x & 3;
+  for (int64_t v0 = static_cast<int64_t>(blockIdx.x) * kVecPerBlock; v0 < a.n_vectors;
+       v0 += static_cast<int64_t>(gridDim.x) * kVecPerBlock) {
+    const int64_t v = v0 + (threadIdx.x >> 2);
+    const bool ok = v < a.n_vectors;
+    float y[kPerLane];
+    load_vec<float>(a.y + (ok ? v : 0) * kDim + part * kPerLane, ok, y);
+    uint32_t w[3];
+    const float n = quantize_pack_lane(y, a.cb, w);
+    if (ok) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + v * kRowBytes + part * 12);
+      dst[0] = w[0];
+      dst[1] = w[1];
+      dst[2] = w[2];
+      if (part == 0) a.norms[v] = n;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize cache rows: x_hat = n Hn B^T c[code].
+// grid = (token blocks, num_kv_heads, 2 [K, V])
+template <typename T>
+__global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
+  __shared__ __align__(16) float sm[kBlocks * 16];
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  T* __restrict__ out = static_cast<T*>(is_v ? a.v_out : a.k_out);
+  if (out == nullptr) return;   // uniform across the block
+  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  __syncthreads();
+  const uint8_t* __restrict__ codes = is_v ? a.v_codes : a.k_codes;
+  const float* __restrict__ norms = is_v ? a.v_norms : a.k_norms;
+  const int part = threadIdx.x & 3;
+  const int vec = threadIdx.x >> 2;
+  for (int tok0 = blockIdx.x * kVecPerBlock; tok0 < a.n_tokens; tok0 += gridDim.x * kVecPerBlock) {
+    const int tok = tok0 + vec;
+    const bool ok = tok < a.n_tokens;
+    const size_t row = static_cast<size_t>(h) * a.capacity + a.first_slot + (ok ? tok : 0);
+    uint32_t w[3] = {0u, 0u, 0u};
+    float n = 0.f;
+    if (ok) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + row * kRowBytes + part * 12);
+      w[0] = src[0];
+      w[1] = src[1];
+      w[2] = src[2];
+      n = norms[row];
+    }
+    float x[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) x[i] = centroid(code_at(w, i), a.cb);
+    so4_apply_lane<true>(x, sm, part);
+    wht128_quad(x, part);
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) x[i] *= n;
+    if (ok) store_vec<T>(out + (static_cast<size_t>(tok) * a.num_kv_heads + h) * kDim + part * kPerLane, x);
+  }
+}
+
+// ------------------------------------------------------------- launchers ----
+static int enc_grid_x(int64_t n_vectors_per_y, int64_t y_blocks) {
+  // enough blocks to fill the chip several times over, each looping a few passes
+  const int64_t need = (n_vectors_per_y + kVecPerBlock - 1) / kVecPerBlock;
+  const int64_t target = (2048 + y_blocks - 1) / y_blocks;
+  int64_t g = need < target ? need : target;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s) {
+  dim3 grid(enc_grid_x(a.n_tokens, 2LL * a.num_kv_heads), a.num_kv_heads, 2);
+  if (f16)
+    hipLaunchKernelGGL(append_kernel<_Float16>, grid, dim3(kEncThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(kEncThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate(const RotateArgs& a, bool inverse, hipStream_t s) {
+  dim3 grid(enc_grid_x(a.n_tokens, a.num_heads), a.num_heads, 1);
+  if (inverse)
+    hipLaunchKernelGGL(rotate_kernel<true>, grid, dim3(kEncThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(rotate_kernel<false>, grid, dim3(kEncThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s) {
+  dim3 grid(enc_grid_x(a.n_vectors, 1), 1, 1);
+  hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(kEncThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, bool f16, hipStream_t s) {
+  dim3 grid(enc_grid_x(a.n_tokens, 2LL * a.num_kv_heads), a.num_kv_heads, 2);
+  if (f16)
+    hipLaunchKernelGGL(dequant_kernel<_Float16>, grid, dim3(kEncThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(dequant_kernel<float>, grid, dim3(kEncThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace iq

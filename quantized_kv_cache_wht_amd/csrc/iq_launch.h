@@ -1,0 +1,92 @@
+// Host-side launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "iq_device.h"
+
+namespace iq {
+
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+  const float* rot;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_norms;
+  float* v_norms;
+  int32_t n_tokens;
+  int32_t first_slot;
+  int32_t num_kv_heads;
+  int32_t capacity;
+  Codebook cb;
+};
+
+struct RotateArgs {
+  const float* x;
+  float* y;
+  const float* rot;
+  int32_t n_tokens;
+  int32_t num_heads;
+};
+
+struct QuantArgs {
+  const float* y;
+  uint8_t* codes;
+  float* norms;
+  int64_t n_vectors;
+  Codebook cb;
+};
+
+struct DequantArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_norms;
+  const float* v_norms;
+  const float* rot;
+  void* k_out;
+  void* v_out;
+  int32_t first_slot;
+  int32_t n_tokens;
+  int32_t num_kv_heads;
+  int32_t capacity;
+  Codebook cb;
+};
+
+struct DecodeArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_norms;
+  const float* v_norms;
+  const float* rot;
+  const float* q;
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  float* out;
+  float* ws;             // partials [n_seqs][Hq][n_splits][2 + 128]
+  int32_t n_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t capacity;
+  int32_t max_seq_len;
+  int32_t split_len;     // tokens per split (multiple of the chunk)
+  int32_t n_splits;      // splits per (seq, kv head) at max_seq_len
+  float qscale;          // softmax scale * log2(e)
+  Codebook cb;
+};
+
+hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s);
+hipError_t launch_rotate(const RotateArgs& a, bool inverse, hipStream_t s);
+hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, bool f16, hipStream_t s);
+
+// split-K plan for decode (shared by the workspace query and the launch)
+void decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t* split_len,
+                 int32_t* n_splits);
+size_t decode_workspace_floats(int32_t n_seqs, int32_t num_q_heads, int32_t n_splits);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace iq

@@ -1,0 +1,101 @@
+"""Host-side checks of libiq's C ABI: it loads, exports what include/iq.h
+declares, computes the same codebook as the oracle, and rejects invalid
+arguments before launching anything. No GPU is needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_kv_cache_wht_amd as iq
+from oracle import iqref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "iq.h")).read()
+    return sorted(set(re.findall(r"IQ_API\s+[\w\s\*]+?\b(iq_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 8, names
+    h = ctypes.CDLL(iq.library_path())
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(iq._SIGNATURES)
+
+
+def test_codebook_matches_oracle_bit_for_bit():
+    c, t = iq.iq_codebook()
+    oc, ot, _ = iqref.codebook()
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert iq.status_string(s)
+    assert iq.status_string(-99) == "unknown status"
+
+
+def _view(head_dim=128, hkv=2, cap=100, ptr=0x10000):
+    return iq.CacheView(head_dim, hkv, cap, ptr, ptr + 0x1000, ptr + 0x2000, ptr + 0x3000, ptr + 0x4000)
+
+
+def test_append_validation():
+    L = iq.lib()
+    v = _view()
+    p = ctypes.c_void_p(0x20000)
+    assert L.iq_rotate_quantize_append(None, p, p, 1, 4, 0, None, None) == -1
+    assert L.iq_rotate_quantize_append(ctypes.byref(_view(head_dim=64)), p, p, 1, 4, 0, None, None) == -2
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 7, 4, 0, None, None) == -1      # dtype
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, -1, 0, None, None) == -1     # n_tokens
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 4, 97, None, None) == -3     # past capacity
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 4, -1, None, None) == -3
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), None, p, 1, 4, 0, None, None) == -1
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), ctypes.c_void_p(0x20004), p, 1, 4, 0, None, None) == -1
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 0, 0, None, None) == 0       # no-op
+    bad = _view(ptr=0x10008)                                                                # misaligned codes
+    assert L.iq_rotate_quantize_append(ctypes.byref(bad), p, p, 1, 4, 0, None, None) == -1
+
+
+def test_decode_validation():
+    L = iq.lib()
+    v = _view(hkv=2)
+    p = ctypes.c_void_p(0x30000)
+    need = L.iq_decode_workspace_bytes(1, 8, 2, 100)
+    assert need > 0
+    args = lambda hq=8, ws=need, n=1, ml=100: (ctypes.byref(v), p, hq, p, p, n, ml, 0.1, p, p, ws, None)
+    assert L.iq_decode_attention(*args(hq=7)) == -1          # Hq % Hkv
+    assert L.iq_decode_attention(*args(hq=6)) == -2          # group 3 unsupported
+    assert L.iq_decode_attention(*args(hq=64)) == -2         # group 32 unsupported
+    assert L.iq_decode_attention(*args(ws=need - 1)) == -4
+    assert L.iq_decode_attention(*args(n=-1)) == -1
+    assert L.iq_decode_attention(*args(n=0)) == 0
+    assert L.iq_decode_workspace_bytes(-1, 8, 2, 100) == 0
+    # workspace grows with context and shrinks to one split for short contexts
+    assert L.iq_decode_workspace_bytes(1, 32, 4, 32768) >= L.iq_decode_workspace_bytes(1, 32, 4, 1024)
+    assert L.iq_decode_workspace_bytes(1, 32, 8, 1) == 32 * 132 * 4
+
+
+def test_dequant_and_rotate_validation():
+    L = iq.lib()
+    v = _view()
+    p = ctypes.c_void_p(0x40000)
+    assert L.iq_dequantize(ctypes.byref(v), 90, 20, 0, p, p, None) == -3
+    assert L.iq_dequantize(ctypes.byref(v), 0, 20, 3, p, p, None) == -1
+    assert L.iq_dequantize(ctypes.byref(v), 0, 20, 0, None, None, None) == 0
+    assert L.iq_rotate(None, 1, p, p, 4, 0, None) == -1
+    assert L.iq_rotate(p, 1, p, p, 4, 2, None) == -1
+    assert L.iq_rotate(p, 0, p, p, 4, 0, None) == -1
+    assert L.iq_quantize_pack(p, -1, p, p, None) == -1
+    assert L.iq_quantize_pack(p, 0, p, p, None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        iq.iq_quantize_pack(torch.zeros(4, 128))

@@ -1,0 +1,254 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X only).
+
+Tolerances (stated by the method's spec and restated here):
+  * codes and norms: bit-exact when both sides quantize the same float32
+    rotated vectors (``iq_quantize_pack``); through the full encode
+    (``iq_rotate_quantize_append``, where the GPU rotates in float32) a code
+    may differ only where the oracle's y/n lies within 1e-6 of a cell
+    boundary, and such codes must be fewer than 1e-5 of all codes;
+  * attention outputs: max-abs error <= 2e-3 and relative L2 error <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import iqinputs
+import quantized_kv_cache_wht_amd as iq
+from oracle import iqref as R
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+C32, T32, _ = R.codebook()
+SCALE = 1.0 / math.sqrt(128)
+
+
+def _t(a, dtype=None):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV) if dtype is None else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _assert_attention_close(got, ref, what=""):
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    print(f"[{what}] max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert max_abs <= 2e-3 and rel <= 1e-3, (what, max_abs, rel)
+
+
+def _boundary_mismatch_ok(codes_gpu, codes_ref, y_ref, n_ref):
+    """Mismatched codes must sit within 1e-6 of a boundary (in y/n units) and be < 1e-5 of all."""
+    diff = codes_gpu != codes_ref
+    nd = int(diff.sum())
+    if nd:
+        u = y_ref[diff].astype(np.float64) / np.broadcast_to(n_ref[..., None], y_ref.shape)[diff].astype(np.float64)
+        gap = np.min(np.abs(u[:, None] - T32.astype(np.float64)[None, :]), axis=1)
+        assert np.all(gap <= 1e-6), gap.max()
+        assert np.all(np.abs(codes_gpu[diff].astype(int) - codes_ref[diff].astype(int)) == 1)
+    assert nd < 1e-5 * codes_ref.size, (nd, codes_ref.size)
+    return nd
+
+
+# ------------------------------------------------------------- rotation ----
+@pytest.mark.parametrize("n_tok,heads", [(1, 1), (300, 3), (4096, 8)])
+def test_rotate_matches_oracle(n_tok, heads):
+    rot = iqinputs.rotation_params(101, n_tok, heads)
+    x = np.random.default_rng(n_tok).standard_normal((n_tok, heads, 128)).astype(np.float32) * 5
+    y = _np(iq.iq_rotate(_t(rot), _t(x)))
+    ref = np.stack([R.rotate(x[:, h].astype(np.float64), rot[h]) for h in range(heads)], axis=1)
+    scale = np.linalg.norm(x.astype(np.float64), axis=-1, keepdims=True)
+    assert np.max(np.abs(y - ref) / scale) < 2e-6
+    back = _np(iq.iq_rotate(_t(rot), _t(y), inverse=True))
+    assert np.max(np.abs(back - x) / scale) < 4e-6
+
+
+# ------------------------------------------------------ quantize + pack ----
+def test_quantize_pack_bit_exact_on_same_rotated_input():
+    g = np.random.default_rng(5)
+    rot = iqinputs.rotation_params(5, 0, 1)[0]
+    x = iqinputs.kv(5, 0, "k", 6000, 1, "fixed_x8", "f32")[:, 0].astype(np.float64)
+    x *= g.uniform(1e-3, 1e3, (6000, 1))
+    y = R.rotate(x, rot).astype(np.float32)
+    extra = np.zeros((5, 128), np.float32)
+    extra[1, 7] = 2.5                                     # single nonzero: zeros land on the tie at 0
+    extra[2] = np.nan
+    extra[3] = np.float32(1e-20) * np.ones(128, np.float32)
+    extra[4, :] = -1.0
+    # exact ties at the positive and negative boundaries (norm fixed to 1)
+    ties = []
+    for k in range(7):
+        a = np.float32(T32[k])
+        b = np.float32(np.sqrt(1.0 - float(a) ** 2))
+        v = np.zeros(128, np.float32)
+        v[0], v[1] = b, a
+        ties.append(v)
+    y = np.concatenate([y, extra, np.array(ties)], axis=0)
+    codes_ref, n_ref = R.quantize(y, T32)
+    rows_ref = R.pack(codes_ref)
+    codes, norms = iq.iq_quantize_pack(_t(y))
+    codes, norms = _np(codes), _np(norms)
+    assert np.array_equal(codes, rows_ref)
+    nan = np.isnan(n_ref)
+    assert np.array_equal(np.isnan(norms), nan)
+    assert np.array_equal(norms[~nan].view(np.uint32), n_ref[~nan].view(np.uint32))
+
+
+# --------------------------------------------------------------- append ----
+def _encode_ref(x, rot):
+    """Oracle encode of [n][Hkv][128]: codes [Hkv][n][128], norms, y32."""
+    hkv = x.shape[1]
+    out_c, out_n, out_y = [], [], []
+    for h in range(hkv):
+        y32 = R.rotate(x[:, h].astype(np.float64), rot[h]).astype(np.float32)
+        c, n = R.quantize(y32, T32)
+        out_c.append(c), out_n.append(n), out_y.append(y32)
+    return np.stack(out_c), np.stack(out_n), np.stack(out_y)
+
+
+@pytest.mark.parametrize("wname,n_tok,first", [("single_head_t512", 512, 0), ("dense8b_gqa_t8192", 1000, 37),
+                                               ("moe30b_gqa_t32768", 333, 5)])
+def test_append_matches_oracle(wname, n_tok, first):
+    w = iqinputs.WORKLOADS[wname]
+    rot = iqinputs.rotation_params(w.seed, 0, w.num_kv_heads)
+    k = iqinputs.kv(w.seed, 0, "k", n_tok, w.num_kv_heads, w.outliers, w.dtype)
+    v = iqinputs.kv(w.seed, 0, "v", n_tok, w.num_kv_heads, w.outliers, w.dtype)
+    cache = iq.PackedKVCache.allocate(w.num_kv_heads, first + n_tok + 3, _t(rot))
+    iq.iq_rotate_quantize_append(cache, _t(k), _t(v), first_slot=first)
+    total = 0
+    for name, x in (("k", k), ("v", v)):
+        codes_ref, n_ref, y_ref = _encode_ref(x, rot)
+        rows = _np(getattr(cache, f"{name}_codes"))[:, first:first + n_tok]
+        norms = _np(getattr(cache, f"{name}_norms"))[:, first:first + n_tok]
+        total += _boundary_mismatch_ok(R.unpack(rows), codes_ref, y_ref, n_ref)
+        assert np.max(np.abs(norms - n_ref) / n_ref) < 2e-6
+        untouched = _np(getattr(cache, f"{name}_codes"))[:, :first]
+        assert not untouched.any()
+    print(f"boundary mismatches: {total}")
+
+
+def test_append_with_slot_list_and_out_of_range_slots():
+    hkv = 2
+    rot = iqinputs.rotation_params(9, 0, hkv)
+    k = iqinputs.kv(9, 0, "k", 70, hkv, "student_t6", "f16")
+    v = iqinputs.kv(9, 0, "v", 70, hkv, "student_t6", "f16")
+    slots = np.random.default_rng(1).permutation(100)[:70].astype(np.int32)
+    slots[3] = -1
+    slots[10] = 100                       # == capacity: skipped
+    cache = iq.PackedKVCache.allocate(hkv, 100, _t(rot))
+    iq.iq_rotate_quantize_append(cache, _t(k), _t(v), slots=_t(slots))
+    kc = _np(cache.k_codes)
+    codes_ref, n_ref, y_ref = _encode_ref(k, rot)
+    good = (slots >= 0) & (slots < 100)
+    _boundary_mismatch_ok(R.unpack(kc[:, slots[good]]), codes_ref[:, good], y_ref[:, good], n_ref[:, good])
+    written = np.zeros(100, bool)
+    written[slots[good]] = True
+    assert not kc[:, ~written].any()
+
+
+# ------------------------------------------------------------ dequantize ----
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
+def test_dequantize_matches_oracle(out_dtype):
+    hkv, n = 3, 777
+    rot = iqinputs.rotation_params(3, 1, hkv)
+    x = iqinputs.kv(3, 1, "k", n, hkv, "fixed_x8", "f32")
+    rows, norms = R.encode_tokens(x, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, n, _t(rot))
+    cache.k_codes.copy_(_t(rows))
+    cache.v_codes.copy_(_t(rows[:, ::-1].copy()))
+    cache.k_norms.copy_(_t(norms))
+    cache.v_norms.copy_(_t(norms[:, ::-1].copy()))
+    k_out, v_out = iq.iq_dequantize(cache, 100, 600, out_dtype)
+    k_out, v_out = _np(k_out).astype(np.float64), _np(v_out).astype(np.float64)
+    tol = 2e-6 if out_dtype == torch.float32 else 1e-3
+    for h in range(hkv):
+        ref_k = R.dequantize(rows[h, 100:700], norms[h, 100:700], rot[h], C32)
+        ref_v = R.dequantize(rows[h, ::-1][100:700], norms[h, ::-1][100:700], rot[h], C32)
+        nk = norms[h, 100:700, None]
+        assert np.max(np.abs(k_out[:, h] - ref_k) / nk) < tol
+        assert np.max(np.abs(v_out[:, h] - ref_v) / norms[h, ::-1][100:700, None]) < tol
+
+
+# ---------------------------------------------------------------- decode ----
+def _oracle_cache(seed, hkv, total, outliers="student_t6", dtype="f16"):
+    rot = iqinputs.rotation_params(seed, 0, hkv)
+    k = iqinputs.kv(seed, 0, "k", total, hkv, outliers, dtype)
+    v = iqinputs.kv(seed, 0, "v", total, hkv, outliers, dtype)
+    kr, kn = R.encode_tokens(k, rot, T32)
+    vr, vn = R.encode_tokens(v, rot, T32)
+    return rot, kr, kn, vr, vn
+
+
+def _upload(rot, kr, kn, vr, vn, capacity=None):
+    hkv, total, _ = kr.shape
+    cap = total if capacity is None else capacity
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot))
+    cache.k_codes[:, :total].copy_(_t(kr))
+    cache.v_codes[:, :total].copy_(_t(vr))
+    cache.k_norms[:, :total].copy_(_t(kn))
+    cache.v_norms[:, :total].copy_(_t(vn))
+    return cache
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [
+    (1, 1, [512]),
+    (2, 1, [1, 255, 256, 257]),
+    (8, 2, [0, 700, 1300]),
+    (32, 4, [2100]),
+    (16, 1, [513, 3]),
+    (32, 8, [1024, 77, 4000]),
+])
+def test_decode_matches_oracle(hq, hkv, lens):
+    lens = np.array(lens, np.int32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    total = int(lens.sum())
+    rot, kr, kn, vr, vn = _oracle_cache(hq * 100 + hkv, hkv, max(total, 1))
+    cache = _upload(rot, kr, kn, vr, vn, capacity=max(total, 1) + 5)
+    q = iqinputs.queries(hq, 0, len(lens), hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), int(lens.max())))
+    ref = R.decode_attention(q, kr, kn, vr, vn, rot, starts, lens, SCALE, C32)
+    _assert_attention_close(out, ref, f"hq={hq} hkv={hkv} lens={list(lens)}")
+    for s in np.nonzero(lens == 0)[0]:
+        assert np.all(out[s] == 0)
+
+
+def test_decode_invalid_ranges_give_nan_and_no_fault():
+    hkv, hq = 2, 4
+    rot, kr, kn, vr, vn = _oracle_cache(77, hkv, 300)
+    cache = _upload(rot, kr, kn, vr, vn)
+    starts = np.array([0, 250, -1, 10], np.int32)
+    lens = np.array([100, 100, 5, 200], np.int32)       # seq 1 runs past capacity, seq 2 negative start
+    q = iqinputs.queries(3, 0, 4, hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), 150))   # seq 3 exceeds max_seq_len
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[2])) and np.all(np.isnan(out[3]))
+    ref = R.decode_attention(q, kr, kn, vr, vn, rot, starts, lens, SCALE, C32, seqs=[0])
+    _assert_attention_close(out[0], ref[0], "valid seq beside invalid ones")
+
+
+def test_decode_is_deterministic():
+    hkv, hq = 4, 32
+    rot, kr, kn, vr, vn = _oracle_cache(5, hkv, 5000)
+    cache = _upload(rot, kr, kn, vr, vn)
+    q = _t(iqinputs.queries(5, 0, 1, hq))
+    st, ln = _t(np.array([0], np.int32)), _t(np.array([5000], np.int32))
+    a = _np(iq.iq_decode_attention(cache, q, st, ln, 5000))
+    b = _np(iq.iq_decode_attention(cache, q, st, ln, 5000))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_single_head_workload_end_to_end():
+    """512 fp32 tokens, one head: GPU encode + GPU decode vs the oracle's encode + attention."""
+    w = iqinputs.WORKLOADS["single_head_t512"]
+    inp = iqinputs.layer_inputs(w, 0)
+    cache = iq.PackedKVCache.allocate(1, 512, _t(inp["rot"]))
+    iq.iq_rotate_quantize_append(cache, _t(inp["k"]), _t(inp["v"]))
+    out = _np(iq.iq_decode_attention(cache, _t(inp["q"]), _t(inp["seq_start"]), _t(inp["seq_len"]), 512))
+    kr, kn = R.encode_tokens(inp["k"], inp["rot"], T32)
+    vr, vn = R.encode_tokens(inp["v"], inp["rot"], T32)
+    ref = R.decode_attention(inp["q"], kr, kn, vr, vn, inp["rot"], inp["seq_start"], inp["seq_len"], SCALE, C32)
+    _assert_attention_close(out, ref, "single_head_t512 end to end")
