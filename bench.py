@@ -54,7 +54,7 @@ def cpu_baseline(w, budget_s: float):
     v = iqinputs.kv(w.seed, 0, "v", T, w.num_kv_heads, w.outliers, w.dtype)
     q = iqinputs.queries(w.seed, 0, 1, w.num_q_heads)
     kr, kn = R.encode_tokens(k, rot, t32)
-    vr, vn = R.encode_tokens(v, rot, t32)
+    vr, vn = R.encode_tokens_v(v, rot, t32)
     st, ln = np.array([0], np.int32), np.array([T], np.int32)
     done, t0 = 0, time.perf_counter()
     while True:

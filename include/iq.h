@@ -26,9 +26,17 @@
  *     before anything is launched; a failed check returns a negative
  *     iq_status and launches nothing. IQ_ERR_HIP reports a failed launch.
  *     NaN/Inf inputs are not checked; they propagate.
- *   - Packed row layout: code j of a 128-dim vector occupies bits [3j, 3j+3)
- *     of a 384-bit little-endian bitstream (48 bytes; bytes 3i..3i+2 hold
- *     codes 8i..8i+7). Code c is the c-th centroid in ascending order.
+ *   - Codes: code c is the c-th centroid in ascending order, 3 bits each.
+ *   - K layout: one 48-byte row per cache slot; code j of the row occupies
+ *     bits [3j, 3j+3) of a 384-bit little-endian bitstream (bytes 3i..3i+2
+ *     hold codes 8i..8i+7).
+ *   - V layout: tiles of 8 consecutive slots (slot s in tile s/8 at position
+ *     r = s%8), 384 bytes each; the code of dim j of the slot at position r
+ *     occupies bits [24j + 3r, 24j + 3r + 3) of the tile's little-endian
+ *     bitstream. (The same 48 bytes per slot, ordered so that the 8 codes of
+ *     one dim are adjacent.)
+ *   - Capacity must be a multiple of 32 slots; code arrays and norm arrays
+ *     must be 16-byte aligned.
  *   - Rotation parameters: float rot[num_kv_heads][32][8]; block b of head h
  *     is rot[h][b] = {qL.w, qL.x, qL.y, qL.z, qR.w, qR.x, qR.y, qR.z} and maps
  *     dims 4b..4b+3, read as a quaternion v = (w,x,y,z), to qL (x) v (x) conj(qR).
@@ -65,9 +73,10 @@ typedef enum { IQ_F32 = 0, IQ_F16 = 1 } iq_dtype;
 typedef struct {
   int32_t head_dim;       /* must be 128 */
   int32_t num_kv_heads;   /* Hkv >= 1 */
-  int32_t capacity;       /* rows per KV head (one flat token axis shared by all sequences) */
-  uint8_t* k_codes;       /* [num_kv_heads][capacity][48], 16-byte aligned */
-  uint8_t* v_codes;       /* [num_kv_heads][capacity][48], 16-byte aligned */
+  int32_t capacity;       /* slots per KV head (one flat token axis shared by all
+                             sequences); a multiple of 32 */
+  uint8_t* k_codes;       /* [num_kv_heads][capacity][48] K rows, 16-byte aligned */
+  uint8_t* v_codes;       /* [num_kv_heads][capacity/8][384] V tiles, 16-byte aligned */
   float* k_norms;         /* [num_kv_heads][capacity] */
   float* v_norms;         /* [num_kv_heads][capacity] */
   const float* rot;       /* [num_kv_heads][32][8] */
@@ -106,8 +115,10 @@ IQ_API iq_status iq_quantize_pack(const float* y, int64_t n_vectors, uint8_t* co
  *               contiguous rows first_slot .. first_slot + n_tokens - 1
  *               (checked against capacity on the host). With `slots`, a slot
  *               outside [0, capacity) is skipped on the device (nothing written).
- * Writes view->k_codes/v_codes rows and view->k_norms/v_norms entries.
- * n_tokens = 0 is a no-op. */
+ * Writes view->k_codes rows, the slots' bits of view->v_codes tiles (other
+ * slots of a partly written tile keep their codes) and view->k_norms/v_norms
+ * entries. Calls that write the same V tile must not run concurrently.
+ * Slots in a slot list must be distinct. n_tokens = 0 is a no-op. */
 IQ_API iq_status iq_rotate_quantize_append(const iq_cache_view* view, const void* k, const void* v,
                                     iq_dtype in_dtype, int32_t n_tokens, int32_t first_slot,
                                     const int32_t* slots, void* stream);

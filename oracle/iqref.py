@@ -41,8 +41,14 @@ the design notes of the repository):
     even) and code_j = #{k : y_j > thr_k}; ties go to the lower code, a zero
     vector gives all-zero codes, NaN gives code 0.
   * Code numbering: code c is the c-th centroid in ascending order.
-  * Packing: code j occupies bits [3j, 3j+3) of a 384-bit little-endian
-    bitstream (48 bytes per row); bytes 3i..3i+2 hold codes 8i..8i+7.
+  * Packing of K: code j occupies bits [3j, 3j+3) of a 384-bit little-endian
+    bitstream (48 bytes per token row); bytes 3i..3i+2 hold codes 8i..8i+7.
+  * Packing of V: tokens are grouped in tiles of 8 consecutive cache slots
+    (slot s in tile s // 8, position s % 8); a tile is a 3072-bit
+    little-endian bitstream (384 bytes, the same 48 bytes per token) in which
+    the code of dimension j of the token at position r sits at bits
+    [24j + 3r, 24j + 3r + 3). The pages only say the codes are packed; this
+    dim-major order keeps the eight codes of one dimension together.
   * Dequantization: x_hat = n . R^-1 c[code], R^-1 = Hn . B^T ([RQ-blurb]:
     the inverse rotation must be applied when reconstructing V).
   * Attention: softmax(scale . q K_hat^T) V_hat per query head
@@ -230,6 +236,31 @@ def unpack(rows: np.ndarray) -> np.ndarray:
     return bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
 
 
+TILE = 8                    # tokens per V tile
+TILE_BYTES = TILE * ROW_BYTES   # 384
+
+
+def pack_tiles(codes: np.ndarray) -> np.ndarray:
+    """[..., 8*n, 128] codes of consecutive slots (first slot a multiple of 8) -> [..., n, 384] V tiles."""
+    codes = np.asarray(codes, np.uint8)
+    n_tok = codes.shape[-2]
+    assert n_tok % TILE == 0
+    c = codes.reshape(codes.shape[:-2] + (n_tok // TILE, TILE, D))             # [..., tile, r, j]
+    bits = np.stack([(c >> b) & 1 for b in range(BITS)], axis=-1)            # [..., tile, r, j, b]
+    bits = np.swapaxes(bits, -3, -2)                                          # [..., tile, j, r, b]
+    bits = bits.reshape(bits.shape[:-3] + (D * TILE * BITS,))                 # bit 24j + 3r + b
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def unpack_tiles(tiles: np.ndarray) -> np.ndarray:
+    """[..., n, 384] V tiles -> [..., 8*n, 128] codes (inverse of ``pack_tiles``)."""
+    bits = np.unpackbits(np.asarray(tiles, np.uint8), axis=-1, bitorder="little")
+    bits = bits.reshape(tiles.shape[:-1] + (D, TILE, BITS)).astype(np.uint8)  # [..., tile, j, r, b]
+    c = bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)              # [..., tile, j, r]
+    c = np.swapaxes(c, -1, -2)                                                # [..., tile, r, j]
+    return c.reshape(c.shape[:-3] + (c.shape[-3] * TILE, D))
+
+
 def rotate_quantize(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
     """Full encode of [..., 128] vectors of one head: (packed rows, norms, float32 y)."""
     y32 = rotate(np.asarray(x, np.float64), rot).astype(np.float32)
@@ -237,24 +268,42 @@ def rotate_quantize(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
     return pack(codes), norm, y32
 
 
-def dequantize(rows: np.ndarray, norms: np.ndarray, rot: np.ndarray, centroids32: np.ndarray) -> np.ndarray:
+def dequantize_codes(codes: np.ndarray, norms: np.ndarray, rot: np.ndarray, centroids32: np.ndarray) -> np.ndarray:
     """x_hat = n . Hn . B^T . c[code] in float64 ([RQ-blurb]: V needs the inverse rotation)."""
-    c = centroids32.astype(np.float64)[unpack(rows)]
+    c = centroids32.astype(np.float64)[np.asarray(codes)]
     return np.asarray(norms, np.float64)[..., None] * inverse_rotate(c, rot)
+
+
+def dequantize(rows: np.ndarray, norms: np.ndarray, rot: np.ndarray, centroids32: np.ndarray) -> np.ndarray:
+    """Dequantize packed K rows [..., 48]."""
+    return dequantize_codes(unpack(rows), norms, rot, centroids32)
 
 
 # --------------------------------------------------------------------------
 # Cache-level encode (the append call) and decode attention
 # --------------------------------------------------------------------------
-def encode_tokens(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
-    """Encode [n_tok][Hkv][128] -> rows [Hkv][n_tok][48], norms [Hkv][n_tok]."""
+def encode_codes(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
+    """Encode [n_tok][Hkv][128] -> codes [Hkv][n_tok][128] (uint8), norms [Hkv][n_tok]."""
     n_tok, hkv, _ = x.shape
-    rows = np.empty((hkv, n_tok, ROW_BYTES), np.uint8)
+    codes = np.empty((hkv, n_tok, D), np.uint8)
     norms = np.empty((hkv, n_tok), np.float32)
     for h in range(hkv):
-        r, n, _ = rotate_quantize(x[:, h, :], rot[h], thresholds32)
-        rows[h], norms[h] = r, n
-    return rows, norms
+        y32 = rotate(np.asarray(x[:, h, :], np.float64), rot[h]).astype(np.float32)
+        codes[h], norms[h] = quantize(y32, thresholds32)
+    return codes, norms
+
+
+def encode_tokens(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
+    """Encode [n_tok][Hkv][128] -> K rows [Hkv][n_tok][48], norms [Hkv][n_tok]."""
+    codes, norms = encode_codes(x, rot, thresholds32)
+    return pack(codes), norms
+
+
+def encode_tokens_v(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
+    """Encode [n_tok][Hkv][128] (n_tok a multiple of 8, slots 0..n_tok-1) -> V tiles
+    [Hkv][n_tok/8][384], norms [Hkv][n_tok]."""
+    codes, norms = encode_codes(x, rot, thresholds32)
+    return pack_tiles(codes), norms
 
 
 def softmax(s: np.ndarray) -> np.ndarray:
@@ -271,14 +320,22 @@ def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float)
     return p @ v_hat
 
 
-def decode_attention(q, k_rows, k_norms, v_rows, v_norms, rot, seq_start, seq_len, scale, centroids32,
+def v_codes_range(v_tiles: np.ndarray, a: int, n: int) -> np.ndarray:
+    """Codes [n][128] of slots a..a+n-1 of one head's V tiles [cap/8][384]."""
+    t0, t1 = a // TILE, (a + n + TILE - 1) // TILE
+    codes = unpack_tiles(v_tiles[t0:t1])
+    return codes[a - t0 * TILE:a - t0 * TILE + n]
+
+
+def decode_attention(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_len, scale, centroids32,
                      seqs=None, heads=None):
     """Decode attention straight from the definition, in float64.
 
-    q [n_seqs][Hq][128]; k_rows/v_rows [Hkv][cap][48]; norms [Hkv][cap];
-    rot [Hkv][32][8]. The packed K and V of each sequence are dequantized
-    explicitly and ordinary softmax attention is taken over them. ``seqs`` and
-    ``heads`` restrict the computation to a sample; other outputs stay NaN.
+    q [n_seqs][Hq][128]; k_rows [Hkv][cap][48]; v_tiles [Hkv][cap/8][384];
+    norms [Hkv][cap]; rot [Hkv][32][8]. The packed K and V of each sequence
+    are dequantized explicitly and ordinary softmax attention is taken over
+    them. ``seqs`` and ``heads`` restrict the computation to a sample; other
+    outputs stay NaN.
     """
     n_seqs, hq, _ = q.shape
     hkv = k_rows.shape[0]
@@ -288,12 +345,12 @@ def decode_attention(q, k_rows, k_norms, v_rows, v_norms, rot, seq_start, seq_le
         a, n = int(seq_start[s]), int(seq_len[s])
         for h in (range(hkv) if heads is None else heads):
             kh = dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], centroids32)
-            vh = dequantize(v_rows[h, a:a + n], v_norms[h, a:a + n], rot[h], centroids32)
+            vh = dequantize_codes(v_codes_range(v_tiles[h], a, n), v_norms[h, a:a + n], rot[h], centroids32)
             out[s, h * g:(h + 1) * g] = attention(q[s, h * g:(h + 1) * g], kh, vh, scale)
     return out
 
 
-def decode_attention_rotated(q, k_rows, k_norms, v_rows, v_norms, rot, seq_start, seq_len, scale,
+def decode_attention_rotated(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_len, scale,
                              centroids32):
     """The packed-domain algorithm, step by step in float64 ([RQ-news], [RQ-abs]).
 
@@ -314,7 +371,7 @@ def decode_attention_rotated(q, k_rows, k_norms, v_rows, v_norms, rot, seq_start
         for h in range(hkv):
             qr = rotate(q[s, h * g:(h + 1) * g].astype(np.float64), rot[h])         # [g][128]
             kc = c[unpack(k_rows[h, a:a + n])] * k_norms[h, a:a + n, None].astype(np.float64)
-            vc = c[unpack(v_rows[h, a:a + n])] * v_norms[h, a:a + n, None].astype(np.float64)
+            vc = c[v_codes_range(v_tiles[h], a, n)] * v_norms[h, a:a + n, None].astype(np.float64)
             p = softmax(scale * (qr @ kc.T))
             out[s, h * g:(h + 1) * g] = inverse_rotate(p @ vc, rot[h])
     return out

@@ -19,6 +19,9 @@ import torch
 
 HEAD_DIM = 128
 ROW_BYTES = 48
+TILE = 8                    # V tiles: 8 slots, dim-major
+TILE_BYTES = TILE * ROW_BYTES
+CAPACITY_MULTIPLE = 32      # cache capacity must be a multiple of this
 ROT_PARAMS_PER_HEAD = 256
 
 IQ_OK = 0
@@ -127,21 +130,28 @@ def iq_codebook():
 
 @dataclasses.dataclass
 class PackedKVCache:
-    """Device buffers of one layer of the packed cache (allocated with torch)."""
+    """Device buffers of one layer of the packed cache (allocated with torch).
+
+    K is stored as one 48-byte row per slot; V as 384-byte tiles of 8 slots
+    (dim-major: code of dim j of the slot at tile position r at bits 24j + 3r).
+    """
     k_codes: torch.Tensor     # uint8 [Hkv][capacity][48]
-    v_codes: torch.Tensor
+    v_codes: torch.Tensor     # uint8 [Hkv][capacity / 8][384]
     k_norms: torch.Tensor     # float32 [Hkv][capacity]
     v_norms: torch.Tensor
     rot: torch.Tensor         # float32 [Hkv][32][8]
 
     @classmethod
     def allocate(cls, num_kv_heads: int, capacity: int, rot: torch.Tensor, device="cuda") -> "PackedKVCache":
-        z8 = lambda: torch.zeros((num_kv_heads, capacity, ROW_BYTES), dtype=torch.uint8, device=device)
-        zf = lambda: torch.zeros((num_kv_heads, capacity), dtype=torch.float32, device=device)
+        """Zeroed cache with at least ``capacity`` slots (rounded up to a multiple of 32)."""
+        cap = -(-capacity // CAPACITY_MULTIPLE) * CAPACITY_MULTIPLE
+        zf = lambda: torch.zeros((num_kv_heads, cap), dtype=torch.float32, device=device)
         rot = rot.to(device=device, dtype=torch.float32).contiguous()
         if tuple(rot.shape) != (num_kv_heads, 32, 8):
             raise ValueError("rot must be [num_kv_heads][32][8]")
-        return cls(z8(), z8(), zf(), zf(), rot)
+        return cls(torch.zeros((num_kv_heads, cap, ROW_BYTES), dtype=torch.uint8, device=device),
+                   torch.zeros((num_kv_heads, cap // TILE, TILE_BYTES), dtype=torch.uint8, device=device),
+                   zf(), zf(), rot)
 
     @property
     def num_kv_heads(self) -> int:

@@ -36,6 +36,37 @@ static void lloyd_max_positive_half(double level[4], double bound[3]) {
   for (int k = 0; k < 3; ++k) bound[k] = 0.5 * (y[k] + y[k + 1]);
 }
 
+// fp16 form of the centroids for the matrix-core contractions: alpha * c is
+// split into an fp16 hi part and an fp16 remainder, together good to ~2^-22.
+// alpha in [8, 16) is searched (2^-20 grid) so that the hi part alone is as
+// close as possible (worst ~2e-5 relative), which keeps the remainders small.
+static void centroid_fp16(Codebook& cb) {
+  double best = 1e30, best_a = 8.0;
+  const int steps = 1 << 20;
+  for (int i = 0; i < steps; ++i) {
+    const double al = 8.0 + 8.0 * i / steps;
+    double worst = 0.0;
+    for (int k = 4; k < 8; ++k) {
+      const double x = al * static_cast<double>(cb.c[k]);
+      const double r = static_cast<double>(static_cast<_Float16>(static_cast<float>(x)));
+      const double e = fabs(r - x) / x;
+      worst = e > worst ? e : worst;
+    }
+    if (worst < best) {
+      best = worst;
+      best_a = al;
+    }
+  }
+  for (int k = 0; k < 4; ++k) {
+    const double x = best_a * static_cast<double>(cb.c[4 + k]);
+    const _Float16 hv = static_cast<_Float16>(static_cast<float>(x));
+    const _Float16 lv = static_cast<_Float16>(static_cast<float>(x - static_cast<double>(hv)));
+    cb.h16[k] = __builtin_bit_cast(uint16_t, hv);
+    cb.l16[k] = __builtin_bit_cast(uint16_t, lv);
+  }
+  cb.inv_alpha = static_cast<float>(1.0 / best_a);
+}
+
 static const Codebook& codebook() {
   static Codebook cb;
   static std::once_flag once;
@@ -52,6 +83,7 @@ static const Codebook& codebook() {
       cb.t[4 + k] = static_cast<float>(bd[k] * s);
       cb.t[2 - k] = -cb.t[4 + k];
     }
+    centroid_fp16(cb);
   });
   return cb;
 }
@@ -61,9 +93,10 @@ static iq_status hip_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_
 static iq_status check_view(const iq_cache_view* v) {
   if (v == nullptr) return IQ_ERR_INVALID_ARG;
   if (v->head_dim != kDim) return IQ_ERR_UNSUPPORTED;
-  if (v->num_kv_heads < 1 || v->capacity < 0) return IQ_ERR_INVALID_ARG;
+  if (v->num_kv_heads < 1 || v->capacity < 0 || v->capacity % 32 != 0) return IQ_ERR_INVALID_ARG;
   if (!v->k_codes || !v->v_codes || !v->k_norms || !v->v_norms || !v->rot) return IQ_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(v->k_codes) | reinterpret_cast<uintptr_t>(v->v_codes)) & 15u)
+  if ((reinterpret_cast<uintptr_t>(v->k_codes) | reinterpret_cast<uintptr_t>(v->v_codes) |
+       reinterpret_cast<uintptr_t>(v->k_norms) | reinterpret_cast<uintptr_t>(v->v_norms)) & 15u)
     return IQ_ERR_INVALID_ARG;
   return IQ_OK;
 }
@@ -148,8 +181,8 @@ static bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g 
 
 size_t iq_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
   if (n_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 0) return 0;
-  int32_t split_len, n_splits;
-  decode_plan(n_seqs, num_kv_heads, max_seq_len, &split_len, &n_splits);
+  int32_t bps, n_splits;
+  decode_plan(n_seqs, num_kv_heads, max_seq_len, &bps, &n_splits);
   return decode_workspace_floats(n_seqs, num_q_heads, n_splits) * sizeof(float);
 }
 
@@ -185,7 +218,7 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   a.group = group;
   a.capacity = view->capacity;
   a.max_seq_len = max_seq_len;
-  decode_plan(n_seqs, view->num_kv_heads, max_seq_len, &a.split_len, &a.n_splits);
+  decode_plan(n_seqs, view->num_kv_heads, max_seq_len, &a.blocks_per_split, &a.n_splits);
   a.qscale = scale * 1.4426950408889634f;   // log2(e): scores kept in base 2
   a.cb = codebook();
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));

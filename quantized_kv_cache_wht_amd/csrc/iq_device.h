@@ -20,9 +20,15 @@ constexpr int kRowBytes = 48;        // 128 x 3 bits
 constexpr int kPerLane = 32;         // dims per lane (4 lanes per vector)
 
 struct Codebook {
-  float c[8];   // centroids of N(0, 1/128), ascending
-  float t[7];   // cell boundaries (midpoints), ascending; t[3] == 0
+  float c[8];        // centroids of N(0, 1/128), ascending
+  float t[7];        // cell boundaries (midpoints), ascending; t[3] == 0
+  uint16_t h16[4];   // fp16 bit patterns of alpha * c[4..7] (the positive half) ...
+  uint16_t l16[4];   // ... and of the remainders alpha * c - h16
+  float inv_alpha;   // 1 / alpha: c[k] = (h16 + l16) * inv_alpha to ~2^-22
 };
+
+constexpr int kTile = 8;                   // tokens per V tile
+constexpr int kTileBytes = kTile * kRowBytes;   // 384
 
 // ---------------------------------------------------------------- DPP ----
 // quad_perm selectors: lane i of every quad reads lane sel[i] of that quad.
@@ -207,6 +213,31 @@ __device__ __forceinline__ float centroid(uint32_t v, const Codebook& cb) {
   const float hi = (idx & 1u) ? cb.c[7] : cb.c[6];
   const float mag = (idx & 2u) ? hi : lo;
   return neg ? -mag : mag;
+}
+
+// fp16 bit pattern of the hi (kLo = false) or lo (kLo = true) part of
+// alpha * c[v]; negative codes mirror the positive half (a sign flip of both).
+template <bool kLo>
+__device__ __forceinline__ uint32_t centroid_f16(uint32_t v, const Codebook& cb) {
+  const uint16_t* t = kLo ? cb.l16 : cb.h16;
+  const uint32_t m = v & 3u;
+  const bool neg = v < 4u;
+  const uint32_t idx = neg ? (3u - m) : m;
+  const uint32_t a = (idx & 1u) ? t[1] : t[0];
+  const uint32_t b = (idx & 1u) ? t[3] : t[2];
+  const uint32_t mag = (idx & 2u) ? b : a;
+  return neg ? (mag ^ 0x8000u) : mag;
+}
+
+// 6-bit field starting at compile-time bit OFF of a little-endian dword array.
+template <int OFF>
+__device__ __forceinline__ uint32_t field6(const uint32_t* w) {
+  constexpr int word = OFF >> 5, off = OFF & 31;
+  if constexpr (off <= 26) {
+    return (w[word] >> off) & 63u;
+  } else {
+    return __builtin_amdgcn_alignbit(w[word + 1], w[word], off) & 63u;
+  }
 }
 
 }  // namespace iq

@@ -88,10 +88,37 @@ __device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], 
 
 // ---------------------------------------------------------------------------
 // Append: x (K or V of new tokens) -> codes + norms in the cache.
-// grid = (token blocks, num_kv_heads, 2 [K, V])
+// grid = (windows, num_kv_heads, 2 [K, V]). Without a slot list a window is
+// 64 consecutive slots starting at a multiple of 8 (so every V tile belongs
+// to exactly one window); with a slot list it is 64 consecutive tokens.
+
+// Assemble the 96 bits of dims 4jq .. 4jq+3 of one V tile from the packed
+// rows of its 8 slots (rows in LDS, 12 dwords each): bit 24 d + 3 r holds
+// the code of dim 4 jq + d of the slot at position r.
+__device__ __forceinline__ void tile_quad_bits(const uint32_t (*rows)[12], int r0, int jq, uint32_t (&out)[3]) {
+  out[0] = out[1] = out[2] = 0u;
+  const int bit = 12 * jq;                  // dims 4jq.. start at bit 12 jq of a row
+  const int word = bit >> 5, off = bit & 31;
+#pragma unroll
+  for (int r = 0; r < kTile; ++r) {
+    const uint32_t lo = rows[r0 + r][word];
+    const uint32_t hi = (word + 1 < 12) ? rows[r0 + r][word + 1] : 0u;
+    const uint32_t c12 = __builtin_amdgcn_alignbit(hi, lo, off) & 0xfffu;   // 4 codes
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t c = (c12 >> (3 * d)) & 7u;
+      const int pos = 24 * d + 3 * r;       // compile-time after unrolling
+      out[pos >> 5] |= c << (pos & 31);
+      if ((pos & 31) > 29) out[(pos >> 5) + 1] |= c >> (32 - (pos & 31));
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   __shared__ __align__(16) float sm[kBlocks * 16];
+  __shared__ __align__(16) uint32_t rows[kVecPerBlock][12];
+  __shared__ int row_ok[kVecPerBlock];
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
   load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
@@ -102,27 +129,92 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   float* __restrict__ norms = is_v ? a.v_norms : a.k_norms;
   const int part = threadIdx.x & 3;
   const int vec = threadIdx.x >> 2;
+  const bool scatter = a.slots != nullptr;
+  const int w0 = scatter ? 0 : (a.first_slot & ~(kTile - 1));   // first window start (slot or token)
+  const int span = scatter ? a.n_tokens : (a.first_slot - w0 + a.n_tokens);
+  const int n_windows = (span + kVecPerBlock - 1) / kVecPerBlock;
 
-  for (int tok0 = blockIdx.x * kVecPerBlock; tok0 < a.n_tokens; tok0 += gridDim.x * kVecPerBlock) {
-    const int tok = tok0 + vec;
-    const bool ok = tok < a.n_tokens;
+  for (int win = blockIdx.x; win < n_windows; win += gridDim.x) {
+    const int tok = scatter ? win * kVecPerBlock + vec : w0 + win * kVecPerBlock + vec - a.first_slot;
+    const bool ok = tok >= 0 && tok < a.n_tokens;
     float x[kPerLane];
     load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
     wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
     uint32_t w[3];
     const float n = quantize_pack_lane(x, a.cb, w);
-    if (ok) {
-      const int slot = a.slots ? a.slots[tok] : a.first_slot + tok;
-      if (slot >= 0 && slot < a.capacity) {
-        const size_t row = static_cast<size_t>(h) * a.capacity + slot;
+    const int slot = ok ? (scatter ? a.slots[tok] : a.first_slot + tok) : -1;
+    const bool in_cap = slot >= 0 && slot < a.capacity;
+    const size_t row = static_cast<size_t>(h) * a.capacity + (in_cap ? slot : 0);
+    if (in_cap && part == 0) norms[row] = n;
+    if (!is_v) {
+      if (in_cap) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kRowBytes + part * 12);
         dst[0] = w[0];
         dst[1] = w[1];
         dst[2] = w[2];
-        if (part == 0) norms[row] = n;
+      }
+      continue;
+    }
+    if (scatter) {
+      // V, arbitrary slots: merge this token's codes into its tile with atomics
+      if (in_cap) {
+        uint32_t* tile = reinterpret_cast<uint32_t*>(codes + (row / kTile) * kTileBytes);
+        const int r = slot & (kTile - 1);
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+          const uint32_t c = code_at(w, i);
+          const int pos = 24 * (part * kPerLane + i) + 3 * r;
+          const int wd = pos >> 5, off = pos & 31;
+          atomicAnd(tile + wd, ~(7u << off));
+          atomicOr(tile + wd, c << off);
+          if (off > 29) {
+            atomicAnd(tile + wd + 1, ~(7u >> (32 - off)));
+            atomicOr(tile + wd + 1, c >> (32 - off));
+          }
+        }
+      }
+      continue;
+    }
+    // V, contiguous slots: stage rows in LDS, then write whole tile groups
+    rows[vec][3 * part] = w[0];
+    rows[vec][3 * part + 1] = w[1];
+    rows[vec][3 * part + 2] = w[2];
+    if (part == 0) row_ok[vec] = in_cap ? 1 : 0;
+    __syncthreads();
+    {
+      const int tt = threadIdx.x >> 5, jq = threadIdx.x & 31;     // tile of the window, dims 4jq..4jq+3
+      uint32_t mask = 0u;
+#pragma unroll
+      for (int r = 0; r < kTile; ++r) mask |= row_ok[tt * kTile + r] ? (1u << r) : 0u;
+      if (mask != 0u) {
+        uint32_t bits[3];
+        tile_quad_bits(rows, tt * kTile, jq, bits);
+        const int first_slot_of_tile = w0 + win * kVecPerBlock + tt * kTile;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(
+            codes + ((static_cast<size_t>(h) * a.capacity + first_slot_of_tile) / kTile) * kTileBytes + 12 * jq);
+        if (mask != 0xffu) {
+          uint32_t keep[3] = {0u, 0u, 0u};
+#pragma unroll
+          for (int r = 0; r < kTile; ++r) {
+            if (!(mask & (1u << r))) {
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                const int pos = 24 * d + 3 * r;
+                keep[pos >> 5] |= 7u << (pos & 31);
+                if ((pos & 31) > 29) keep[(pos >> 5) + 1] |= 7u >> (32 - (pos & 31));
+              }
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 3; ++k) bits[k] = (dst[k] & keep[k]) | (bits[k] & ~keep[k]);
+        }
+        dst[0] = bits[0];
+        dst[1] = bits[1];
+        dst[2] = bits[2];
       }
     }
+    __syncthreads();
   }
 }
 
@@ -199,11 +291,27 @@ __global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
     uint32_t w[3] = {0u, 0u, 0u};
     float n = 0.f;
     if (ok) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + row * kRowBytes + part * 12);
-      w[0] = src[0];
-      w[1] = src[1];
-      w[2] = src[2];
       n = norms[row];
+      if (!is_v) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + row * kRowBytes + part * 12);
+        w[0] = src[0];
+        w[1] = src[1];
+        w[2] = src[2];
+      } else {
+        // dims 32p .. 32p+31 of this slot: 3 bits at 24 j + 3 r of its tile
+        const uint32_t* tile = reinterpret_cast<const uint32_t*>(codes + (row / kTile) * kTileBytes);
+        const int r = static_cast<int>(row & (kTile - 1));
+        uint32_t c[kPerLane];
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+          const int pos = 24 * (part * kPerLane + i) + 3 * r;
+          const int wd = pos >> 5, off = pos & 31;
+          const uint32_t lo = tile[wd];
+          const uint32_t hi = off > 29 ? tile[wd + 1] : 0u;
+          c[i] = __builtin_amdgcn_alignbit(hi, lo, off) & 7u;
+        }
+        pack32(c, w);
+      }
     }
     float x[kPerLane];
 #pragma unroll

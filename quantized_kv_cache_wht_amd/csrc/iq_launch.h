@@ -65,16 +65,16 @@ struct DecodeArgs {
   const int32_t* seq_start;
   const int32_t* seq_len;
   float* out;
-  float* ws;             // partials [n_seqs][Hq][n_splits][2 + 128]
+  float* ws;             // partials [n_seqs][Hq][n_splits][132]
   int32_t n_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
   int32_t capacity;
   int32_t max_seq_len;
-  int32_t split_len;     // tokens per split (multiple of the chunk)
-  int32_t n_splits;      // splits per (seq, kv head) at max_seq_len
-  float qscale;          // softmax scale * log2(e)
+  int32_t blocks_per_split;   // 32-slot blocks per split
+  int32_t n_splits;           // splits per (seq, kv head) at max_seq_len
+  float qscale;               // softmax scale * log2(e)
   Codebook cb;
 };
 
@@ -84,7 +84,7 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f16, hipStream_t s);
 
 // split-K plan for decode (shared by the workspace query and the launch)
-void decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t* split_len,
+void decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t* blocks_per_split,
                  int32_t* n_splits);
 size_t decode_workspace_floats(int32_t n_seqs, int32_t num_q_heads, int32_t n_splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

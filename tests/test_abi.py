@@ -41,7 +41,7 @@ def test_status_strings():
     assert iq.status_string(-99) == "unknown status"
 
 
-def _view(head_dim=128, hkv=2, cap=100, ptr=0x10000):
+def _view(head_dim=128, hkv=2, cap=128, ptr=0x10000):
     return iq.CacheView(head_dim, hkv, cap, ptr, ptr + 0x1000, ptr + 0x2000, ptr + 0x3000, ptr + 0x4000)
 
 
@@ -53,12 +53,13 @@ def test_append_validation():
     assert L.iq_rotate_quantize_append(ctypes.byref(_view(head_dim=64)), p, p, 1, 4, 0, None, None) == -2
     assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 7, 4, 0, None, None) == -1      # dtype
     assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, -1, 0, None, None) == -1     # n_tokens
-    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 4, 97, None, None) == -3     # past capacity
+    assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 4, 125, None, None) == -3    # past capacity
+    assert L.iq_rotate_quantize_append(ctypes.byref(_view(cap=100)), p, p, 1, 4, 0, None, None) == -1  # cap % 32
     assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 4, -1, None, None) == -3
     assert L.iq_rotate_quantize_append(ctypes.byref(v), None, p, 1, 4, 0, None, None) == -1
     assert L.iq_rotate_quantize_append(ctypes.byref(v), ctypes.c_void_p(0x20004), p, 1, 4, 0, None, None) == -1
     assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 0, 0, None, None) == 0       # no-op
-    bad = _view(ptr=0x10008)                                                                # misaligned codes
+    bad = _view(ptr=0x10008)                                                                # misaligned arrays
     assert L.iq_rotate_quantize_append(ctypes.byref(bad), p, p, 1, 4, 0, None, None) == -1
 
 
@@ -85,7 +86,7 @@ def test_dequant_and_rotate_validation():
     L = iq.lib()
     v = _view()
     p = ctypes.c_void_p(0x40000)
-    assert L.iq_dequantize(ctypes.byref(v), 90, 20, 0, p, p, None) == -3
+    assert L.iq_dequantize(ctypes.byref(v), 120, 20, 0, p, p, None) == -3
     assert L.iq_dequantize(ctypes.byref(v), 0, 20, 3, p, p, None) == -1
     assert L.iq_dequantize(ctypes.byref(v), 0, 20, 0, None, None, None) == 0
     assert L.iq_rotate(None, 1, p, p, 4, 0, None) == -1

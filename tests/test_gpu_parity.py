@@ -121,15 +121,34 @@ def test_append_matches_oracle(wname, n_tok, first):
     cache = iq.PackedKVCache.allocate(w.num_kv_heads, first + n_tok + 3, _t(rot))
     iq.iq_rotate_quantize_append(cache, _t(k), _t(v), first_slot=first)
     total = 0
+    cap = cache.capacity
     for name, x in (("k", k), ("v", v)):
         codes_ref, n_ref, y_ref = _encode_ref(x, rot)
-        rows = _np(getattr(cache, f"{name}_codes"))[:, first:first + n_tok]
+        if name == "k":
+            all_codes = R.unpack(_np(cache.k_codes))
+        else:
+            all_codes = R.unpack_tiles(_np(cache.v_codes))
+        assert all_codes.shape == (w.num_kv_heads, cap, 128)
         norms = _np(getattr(cache, f"{name}_norms"))[:, first:first + n_tok]
-        total += _boundary_mismatch_ok(R.unpack(rows), codes_ref, y_ref, n_ref)
+        total += _boundary_mismatch_ok(all_codes[:, first:first + n_tok], codes_ref, y_ref, n_ref)
         assert np.max(np.abs(norms - n_ref) / n_ref) < 2e-6
-        untouched = _np(getattr(cache, f"{name}_codes"))[:, :first]
-        assert not untouched.any()
+        assert not all_codes[:, :first].any() and not all_codes[:, first + n_tok:].any()
     print(f"boundary mismatches: {total}")
+
+
+def test_append_v_tiles_keep_neighbours():
+    """Appends that start and end inside V tiles leave the other slots of those tiles intact."""
+    hkv = 2
+    rot = iqinputs.rotation_params(21, 0, hkv)
+    x = iqinputs.kv(21, 0, "v", 64, hkv, "student_t6", "f16")
+    cache = iq.PackedKVCache.allocate(hkv, 64, _t(rot))
+    # three calls covering slots 0..63: [0, 13), [13, 14), [14, 64)
+    for a0, a1 in [(0, 13), (13, 14), (14, 64)]:
+        iq.iq_rotate_quantize_append(cache, _t(x[a0:a1]), _t(x[a0:a1]), first_slot=a0)
+    one = iq.PackedKVCache.allocate(hkv, 64, _t(rot))
+    iq.iq_rotate_quantize_append(one, _t(x), _t(x), first_slot=0)
+    assert torch.equal(cache.v_codes, one.v_codes) and torch.equal(cache.k_codes, one.k_codes)
+    assert torch.equal(cache.v_norms, one.v_norms)
 
 
 def test_append_with_slot_list_and_out_of_range_slots():
@@ -142,56 +161,65 @@ def test_append_with_slot_list_and_out_of_range_slots():
     slots[10] = 100                       # == capacity: skipped
     cache = iq.PackedKVCache.allocate(hkv, 100, _t(rot))
     iq.iq_rotate_quantize_append(cache, _t(k), _t(v), slots=_t(slots))
-    kc = _np(cache.k_codes)
-    codes_ref, n_ref, y_ref = _encode_ref(k, rot)
-    good = (slots >= 0) & (slots < 100)
-    _boundary_mismatch_ok(R.unpack(kc[:, slots[good]]), codes_ref[:, good], y_ref[:, good], n_ref[:, good])
-    written = np.zeros(100, bool)
+    assert cache.capacity == 128
+    slots[10] = 128                       # beyond the rounded-up capacity: skipped
+    cache = iq.PackedKVCache.allocate(hkv, 100, _t(rot))
+    iq.iq_rotate_quantize_append(cache, _t(k), _t(v), slots=_t(slots))
+    good = (slots >= 0) & (slots < 128)
+    written = np.zeros(128, bool)
     written[slots[good]] = True
-    assert not kc[:, ~written].any()
+    for name, x, codes_all in (("k", k, R.unpack(_np(cache.k_codes))), ("v", v, R.unpack_tiles(_np(cache.v_codes)))):
+        codes_ref, n_ref, y_ref = _encode_ref(x, rot)
+        _boundary_mismatch_ok(codes_all[:, slots[good]], codes_ref[:, good], y_ref[:, good], n_ref[:, good])
+        assert not codes_all[:, ~written].any()
 
 
 # ------------------------------------------------------------ dequantize ----
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
 def test_dequantize_matches_oracle(out_dtype):
-    hkv, n = 3, 777
+    hkv, n = 3, 800
     rot = iqinputs.rotation_params(3, 1, hkv)
     x = iqinputs.kv(3, 1, "k", n, hkv, "fixed_x8", "f32")
-    rows, norms = R.encode_tokens(x, rot, T32)
+    codes, norms = R.encode_codes(x, rot, T32)
+    vcodes = codes[:, ::-1].copy()
+    vnorms = norms[:, ::-1].copy()
     cache = iq.PackedKVCache.allocate(hkv, n, _t(rot))
-    cache.k_codes.copy_(_t(rows))
-    cache.v_codes.copy_(_t(rows[:, ::-1].copy()))
+    cache.k_codes.copy_(_t(R.pack(codes)))
+    cache.v_codes.copy_(_t(R.pack_tiles(vcodes)))
     cache.k_norms.copy_(_t(norms))
-    cache.v_norms.copy_(_t(norms[:, ::-1].copy()))
-    k_out, v_out = iq.iq_dequantize(cache, 100, 600, out_dtype)
+    cache.v_norms.copy_(_t(vnorms))
+    k_out, v_out = iq.iq_dequantize(cache, 101, 600, out_dtype)
     k_out, v_out = _np(k_out).astype(np.float64), _np(v_out).astype(np.float64)
     tol = 2e-6 if out_dtype == torch.float32 else 1e-3
     for h in range(hkv):
-        ref_k = R.dequantize(rows[h, 100:700], norms[h, 100:700], rot[h], C32)
-        ref_v = R.dequantize(rows[h, ::-1][100:700], norms[h, ::-1][100:700], rot[h], C32)
-        nk = norms[h, 100:700, None]
-        assert np.max(np.abs(k_out[:, h] - ref_k) / nk) < tol
-        assert np.max(np.abs(v_out[:, h] - ref_v) / norms[h, ::-1][100:700, None]) < tol
+        ref_k = R.dequantize_codes(codes[h, 101:701], norms[h, 101:701], rot[h], C32)
+        ref_v = R.dequantize_codes(vcodes[h, 101:701], vnorms[h, 101:701], rot[h], C32)
+        assert np.max(np.abs(k_out[:, h] - ref_k) / norms[h, 101:701, None]) < tol
+        assert np.max(np.abs(v_out[:, h] - ref_v) / vnorms[h, 101:701, None]) < tol
 
 
 # ---------------------------------------------------------------- decode ----
 def _oracle_cache(seed, hkv, total, outliers="student_t6", dtype="f16"):
+    """Oracle-encoded cache of ``total`` slots rounded up to a multiple of 32 (padding slots encode zeros)."""
+    cap = -(-max(total, 1) // 32) * 32
     rot = iqinputs.rotation_params(seed, 0, hkv)
-    k = iqinputs.kv(seed, 0, "k", total, hkv, outliers, dtype)
-    v = iqinputs.kv(seed, 0, "v", total, hkv, outliers, dtype)
+    k = np.zeros((cap, hkv, 128), np.float16 if dtype == "f16" else np.float32)
+    v = np.zeros_like(k)
+    k[:total] = iqinputs.kv(seed, 0, "k", total, hkv, outliers, dtype)
+    v[:total] = iqinputs.kv(seed, 0, "v", total, hkv, outliers, dtype)
     kr, kn = R.encode_tokens(k, rot, T32)
-    vr, vn = R.encode_tokens(v, rot, T32)
-    return rot, kr, kn, vr, vn
+    vt, vn = R.encode_tokens_v(v, rot, T32)
+    return rot, kr, kn, vt, vn
 
 
-def _upload(rot, kr, kn, vr, vn, capacity=None):
-    hkv, total, _ = kr.shape
-    cap = total if capacity is None else capacity
+def _upload(rot, kr, kn, vt, vn):
+    hkv, cap, _ = kr.shape
     cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot))
-    cache.k_codes[:, :total].copy_(_t(kr))
-    cache.v_codes[:, :total].copy_(_t(vr))
-    cache.k_norms[:, :total].copy_(_t(kn))
-    cache.v_norms[:, :total].copy_(_t(vn))
+    assert cache.capacity == cap
+    cache.k_codes.copy_(_t(kr))
+    cache.v_codes.copy_(_t(vt))
+    cache.k_norms.copy_(_t(kn))
+    cache.v_norms.copy_(_t(vn))
     return cache
 
 
@@ -207,8 +235,8 @@ def test_decode_matches_oracle(hq, hkv, lens):
     lens = np.array(lens, np.int32)
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
     total = int(lens.sum())
-    rot, kr, kn, vr, vn = _oracle_cache(hq * 100 + hkv, hkv, max(total, 1))
-    cache = _upload(rot, kr, kn, vr, vn, capacity=max(total, 1) + 5)
+    rot, kr, kn, vr, vn = _oracle_cache(hq * 100 + hkv, hkv, total + 5)
+    cache = _upload(rot, kr, kn, vr, vn)
     q = iqinputs.queries(hq, 0, len(lens), hq)
     out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), int(lens.max())))
     ref = R.decode_attention(q, kr, kn, vr, vn, rot, starts, lens, SCALE, C32)
@@ -222,7 +250,8 @@ def test_decode_invalid_ranges_give_nan_and_no_fault():
     rot, kr, kn, vr, vn = _oracle_cache(77, hkv, 300)
     cache = _upload(rot, kr, kn, vr, vn)
     starts = np.array([0, 250, -1, 10], np.int32)
-    lens = np.array([100, 100, 5, 200], np.int32)       # seq 1 runs past capacity, seq 2 negative start
+    lens = np.array([100, 100, 5, 200], np.int32)       # seq 1 runs past capacity (320), seq 2 negative start
+    assert cache.capacity == 320
     q = iqinputs.queries(3, 0, 4, hq)
     out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), 150))   # seq 3 exceeds max_seq_len
     assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[2])) and np.all(np.isnan(out[3]))
@@ -249,6 +278,6 @@ def test_single_head_workload_end_to_end():
     iq.iq_rotate_quantize_append(cache, _t(inp["k"]), _t(inp["v"]))
     out = _np(iq.iq_decode_attention(cache, _t(inp["q"]), _t(inp["seq_start"]), _t(inp["seq_len"]), 512))
     kr, kn = R.encode_tokens(inp["k"], inp["rot"], T32)
-    vr, vn = R.encode_tokens(inp["v"], inp["rot"], T32)
+    vr, vn = R.encode_tokens_v(inp["v"], inp["rot"], T32)
     ref = R.decode_attention(inp["q"], kr, kn, vr, vn, inp["rot"], inp["seq_start"], inp["seq_len"], SCALE, C32)
     _assert_attention_close(out, ref, "single_head_t512 end to end")

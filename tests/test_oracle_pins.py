@@ -273,6 +273,39 @@ def test_pack_unpack_exhaustive():
     assert np.array_equal(R.unpack(R.pack(codes)), codes)
 
 
+def test_tile_pack_golden():
+    """V tiles: dim j of slot r (0..7) at bits [24j + 3r, 24j + 3r + 3)."""
+    codes = np.zeros((8, 128), np.uint8)
+    codes[:, 0] = [1, 2, 3, 4, 5, 6, 7, 0]          # dim 0 holds the same 24-bit pattern as pack_pattern
+    codes[3, 1] = 5                                  # dim 1, slot 3 -> bit 24 + 9 = 33 -> byte 4 bits 1, 3
+    codes[7, 127] = 7                                # last dim, last slot -> bits 3069..3071
+    tile = R.pack_tiles(codes)[0]
+    assert tile.shape == (384,)
+    assert list(tile[:3]) == [0xD1, 0x58, 0x1F]
+    assert tile[4] == 0b1010 and tile[3] == 0 and tile[5] == 0
+    assert tile[383] == 0xE0
+    assert np.array_equal(R.unpack_tiles(tile[None])[0:8], codes)
+
+
+def test_tile_pack_round_trip_and_rows_agree():
+    codes = np.random.default_rng(12).integers(0, 8, (3, 40, 128)).astype(np.uint8)
+    tiles = R.pack_tiles(codes)
+    assert tiles.shape == (3, 5, 384)
+    assert np.array_equal(R.unpack_tiles(tiles), codes)
+    # the same codes are reachable slot by slot through v_codes_range
+    for a, n in [(0, 40), (3, 9), (17, 1), (39, 1), (8, 16)]:
+        assert np.array_equal(R.v_codes_range(tiles[1], a, n), codes[1, a:a + n])
+    # exhaustive single-code placement
+    for r in range(8):
+        for j in (0, 1, 63, 127):
+            for v in range(8):
+                c = np.zeros((8, 128), np.uint8)
+                c[r, j] = v
+                bits = np.unpackbits(R.pack_tiles(c), bitorder="little")
+                assert bits.sum() == bin(v).count("1")
+                assert all(bits[24 * j + 3 * r + b] == ((v >> b) & 1) for b in range(3))
+
+
 # ------------------------------------------------------- distortion ----
 def test_distortion_isotropic_inputs(codebook):
     c32, t32, _ = codebook
@@ -296,14 +329,14 @@ def test_rotation_isotropizes_outlier_channels():
 
 
 # -------------------------------------------------------- attention ----
-def _small_cache(codebook, n_tok=300, hkv=2, hq=4, seed=11, lens=(300,)):
+def _small_cache(codebook, n_tok=304, hkv=2, hq=4, seed=11, lens=(300,)):
     c32, t32, _ = codebook
     g = np.random.default_rng(seed)
     rot = _rot(seed=seed, heads=hkv)
     k = g.standard_normal((n_tok, hkv, 128))
     v = g.standard_normal((n_tok, hkv, 128))
     kr, kn = R.encode_tokens(k, rot, t32)
-    vr, vn = R.encode_tokens(v, rot, t32)
+    vr, vn = R.encode_tokens_v(v, rot, t32)
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
     q = g.standard_normal((len(lens), hq, 128)).astype(np.float32)
     return q, kr, kn, vr, vn, rot, starts, np.array(lens, np.int32)
@@ -311,7 +344,7 @@ def _small_cache(codebook, n_tok=300, hkv=2, hq=4, seed=11, lens=(300,)):
 
 def test_attention_packed_domain_equals_brute_force(codebook):
     c32 = codebook[0]
-    args = _small_cache(codebook, n_tok=300, lens=(120, 0, 1, 179))
+    args = _small_cache(codebook, n_tok=304, lens=(120, 0, 1, 179))
     scale = 1 / math.sqrt(128)
     a = R.decode_attention(*args, scale, c32)
     b = R.decode_attention_rotated(*args, scale, c32)
@@ -321,8 +354,8 @@ def test_attention_packed_domain_equals_brute_force(codebook):
 
 def test_attention_special_cases(codebook):
     c32 = codebook[0]
-    q, kr, kn, vr, vn, rot, st, ln = _small_cache(codebook, n_tok=50, hkv=1, hq=2, lens=(50,))
-    v_hat = R.dequantize(vr[0], vn[0], rot[0], c32)
+    q, kr, kn, vr, vn, rot, st, ln = _small_cache(codebook, n_tok=56, hkv=1, hq=2, lens=(50,))
+    v_hat = R.dequantize_codes(R.unpack_tiles(vr[0])[:50], vn[0, :50], rot[0], c32)
     # one token: output is that token's value
     one = R.decode_attention(q, kr, kn, vr, vn, rot, st, np.array([1], np.int32), 0.3, c32)
     assert np.allclose(one[0, 0], v_hat[0], atol=1e-13)
@@ -330,8 +363,8 @@ def test_attention_special_cases(codebook):
     z = R.decode_attention(q, kr, kn, vr, vn, rot, st, ln, 0.0, c32)
     assert np.allclose(z[0, 1], v_hat.mean(0), atol=1e-13)
     # identical keys: mean of the values
-    kr2 = np.repeat(kr[:, :1], 50, axis=1)
-    kn2 = np.repeat(kn[:, :1], 50, axis=1)
+    kr2 = np.repeat(kr[:, :1], 56, axis=1)
+    kn2 = np.repeat(kn[:, :1], 56, axis=1)
     same = R.decode_attention(q, kr2, kn2, vr, vn, rot, st, ln, 0.2, c32)
     assert np.allclose(same[0, 0], v_hat.mean(0), atol=1e-13)
     # softmax against the library routine
