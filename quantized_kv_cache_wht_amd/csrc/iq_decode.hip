@@ -4,34 +4,36 @@
 // What is computed (news article on RotaryQuant, section on attention over
 // packed data; arXiv 2608.08081 abstract; zhichai.net essay's attention
 // formula softmax(Q K^T / sqrt(d)) V):
-//   q'_g    = R q_g                                          (query rotated once)
-//   s_{g,t} = scale log2(e) nK_t sum_j q'_{g,j} c[kcode_{t,j}] (score in the rotated domain)
+//   q'_g    = R q_g                                            (query rotated once)
+//   s_{g,t} = scale log2(e) nK_t sum_j q'_{g,j} c[kcode_{t,j}]   (score in the rotated domain)
 //   o'_g    = sum_t 2^(s_{g,t} - m) nV_t c[vcode_t] / sum_t 2^(s_{g,t} - m)
-//   out_g   = R^-1 o'_g = Hn B^T o'_g                          (one inverse rotation)
+//   out_g   = R^-1 o'_g = Hn B^T o'_g                            (one inverse rotation)
 // Full-precision K and V are never formed in memory.
 //
-// Contractions on MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulate). Per wave
-// and per block of 32 cache slots:
-//   * scores: two 16-token tiles x 4 k-steps; A = centroids of the packed K
-//     codes, B = the rotated queries. For G <= 8 the 16 B columns hold the
-//     query split into fp16 hi (columns g) and lo (columns g + 8) parts and
-//     one DPP row rotation adds the two halves, so the query keeps ~22 bits.
-//   * PV: A = softmax weights times V norms, again split hi (rows g) / lo
-//     (rows g + 8); B = centroids of the packed V codes; 8 column tiles of 16
-//     dims, K = the 32 tokens.
-// Centroids enter the MFMA as fp16(alpha c) with a scale alpha chosen so that
-// all eight are within 2e-5 relative of the float32 codebook; 1/alpha is
-// applied to the fp32 results.
-//
-// Code -> fp16 pair conversion: a 64-entry table (all pairs of codes) in LDS,
-// replicated 32 times so each lane of a half-wave reads its own bank.
+// Contractions on MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulate). Each
+// centroid enters as alpha * c = hi + lo (two fp16 numbers, ~22 bits
+// together); the two halves sit in adjacent K slots of the code operand and
+// the other operand repeats its value in both slots, so one MFMA forms
+// (hi + lo) * x. Per wave and per block of 32 cache slots:
+//   * scores: two 16-token tiles x 8 k-steps of 4 dims; A = code centroids,
+//     B = the rotated query. For G <= 8 the 16 B columns hold the query split
+//     into fp16 hi (columns g) and lo (columns g + 8) and one DPP row rotation
+//     adds the halves, so the query keeps ~22 bits as well.
+//   * PV: 8 column tiles of 16 dims x 2 groups of 16 tokens; A = softmax
+//     weights times V norms (hi rows g, lo rows g + 8), B = code centroids.
+// Code pairs become operand dwords through a 64-entry table in LDS (entry p =
+// {hi(c_a) | lo(c_a) << 16, hi(c_b) | lo(c_b) << 16} for the codes a, b of
+// pair p), replicated 16 times so the lanes of a 16-lane group hit distinct
+// banks; one 8-byte read fills two operand registers.
 //
 // Layout of the cache (see include/iq.h): K rows of 48 bytes per token; V in
-// tiles of 8 slots, dim-major, so the 8 codes one PV operand needs (one dim,
-// 8 consecutive tokens) are 24 adjacent bits.
+// tiles of 8 slots, dim-major, so the codes one PV operand needs (one dim,
+// consecutive tokens) are adjacent bits.
 //
-// Softmax reference: m tracks max_t(s_t + max(0, log2 nV_t)) (an exponent
-// bound), so p_t nV_t <= 1 and the fp16 operand never overflows.
+// Softmax reference m: an upper bound of s_t + log2(nV_t) (via the exponent
+// of nV), raised lazily (only when a block exceeds it by more than 2^8), so
+// p_t nV_t <= 256 and the fp16 operand never overflows while accumulator
+// rescaling is rare.
 #include <math.h>
 
 #include "iq_device.h"
@@ -45,6 +47,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 union H8 {
   half8 h;
   uint32_t u[4];
+  uint2 u2[2];
 };
 
 constexpr int kDecThreads = 256;
@@ -55,12 +58,8 @@ constexpr int kTargetBlocks = 512;   // split-K occupancy target (work-groups)
 constexpr int kMinBlocksPerSplit = 8;
 constexpr int kMaxSplits = 2048;
 constexpr int kLutEntries = 64;      // all pairs of 3-bit codes
-constexpr int kLutCopies = 16;       // one per lane of a 16-lane group (8-byte entries)
-
-// The pair table: entry p holds {hi(c[p&7]) | hi(c[p>>3]) << 16, lo(...) | lo(...) << 16}.
-struct Operand {
-  half8 hi, lo;
-};
+constexpr int kLutCopies = 16;       // one per lane of a 16-lane group
+constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
 
 __device__ __forceinline__ bool seq_ok(const DecodeArgs& a, int s, int* start, int* len) {
   const int st = a.seq_start[s];
@@ -83,38 +82,183 @@ __device__ __forceinline__ float dpp_row_ror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
 
-// Operand (hi and lo halves) for the 8 codes at bits BIT .. BIT+23 of w:
-// four code pairs, each one 8-byte table read.
+// Table entry of the code pair at bit BIT of w: {hi|lo of code a, hi|lo of code b}.
 template <int BIT, int N>
-__device__ __forceinline__ Operand pair_operand(const uint32_t (&w)[N], const uint2* __restrict__ lut, uint32_t l15) {
-  H8 hi, lo;
-  const uint2 e0 = lut[(field6<BIT + 0>(w) << 4) | l15];
-  const uint2 e1 = lut[(field6<BIT + 6>(w) << 4) | l15];
-  const uint2 e2 = lut[(field6<BIT + 12>(w) << 4) | l15];
-  const uint2 e3 = lut[(field6<BIT + 18>(w) << 4) | l15];
-  hi.u[0] = e0.x; hi.u[1] = e1.x; hi.u[2] = e2.x; hi.u[3] = e3.x;
-  lo.u[0] = e0.y; lo.u[1] = e1.y; lo.u[2] = e2.y; lo.u[3] = e3.y;
-  return Operand{hi.h, lo.h};
+__device__ __forceinline__ uint2 pair_entry(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
+  constexpr int word = BIT >> 5, off = BIT & 31;
+  const uint32_t src = (off <= 26) ? w[word] : __builtin_amdgcn_alignbit(w[word + 1], w[word], off);
+  constexpr int field = (off <= 26) ? off : 0;
+  // byte address = field * 128 + lane_off, as one bit-field extract and one
+  // shift-add (the compiler's own lowering of this takes three instructions)
+  uint32_t addr;
+  asm("v_bfe_u32 %0, %1, %2, 6\n\tv_lshl_add_u32 %0, %0, 7, %3" : "=&v"(addr) : "v"(src), "i"(field), "v"(lane_off));
+  return *reinterpret_cast<const uint2*>(lut + addr);
 }
 
-// A operand of the score MFMA for k-step KAPPA: codes of dims 32q + 8 KAPPA .. +7,
-// bits 24 KAPPA .. +23 of the lane's 96 K bits.
-template <int KAPPA>
-__device__ __forceinline__ Operand k_operand(const uint32_t (&kw)[3], const uint2* __restrict__ lut, uint32_t l15) {
-  return pair_operand<24 * KAPPA>(kw, lut, l15);
+// 2^x on the transcendental unit (results below 2^-126 flush to 0, which the
+// softmax weights tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Code operand for the 4 codes at bits BIT .. BIT+11 of w (two pairs).
+template <int BIT, int N>
+__device__ __forceinline__ half8 code_operand(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
+  H8 r;
+  r.u2[0] = pair_entry<BIT>(w, lut, lane_off);
+  r.u2[1] = pair_entry<BIT + 6>(w, lut, lane_off);
+  return r.h;
 }
 
-// B operand of the PV MFMA for column tile D: the 8 tokens of dim 8n + D,
-// bits 24 D .. +23 of the lane's 192 V bits.
-template <int D>
-__device__ __forceinline__ Operand v_operand(const uint32_t (&vw)[6], const uint2* __restrict__ lut, uint32_t l15) {
-  return pair_operand<24 * D>(vw, lut, l15);
+// fp16 pair (x, x) of one value.
+__device__ __forceinline__ uint32_t dup16(float x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x));
+}
+
+// Packed codes and norms of one 32-slot block for this lane.
+struct BlockData {
+  uint32_t kw0[3], kw1[3], vw[6];
+  float4 nk0, nk1, nv0, nv1;
+};
+
+// K tile T row r <-> token 8 (r/4) + 4T + r%4 of the block; this lane loads
+// row n of both tiles (dims 32q .. 32q+31), V tile q (dims 8n .. 8n+7) and
+// the norms of tokens 8q .. 8q+7 (its rows in the score output).
+__device__ __forceinline__ void load_block(const DecodeArgs& a, size_t slot_base, int slot0, int n, int q,
+                                           BlockData& d) {
+  const int tok_a0 = 8 * (n >> 2) + (n & 3);
+  const uint32_t* k0 = reinterpret_cast<const uint32_t*>(a.k_codes + (slot_base + slot0 + tok_a0) * kRowBytes + 12 * q);
+  const uint32_t* k1 = k0 + kRowBytes;   // token + 4: 4 rows of 48 bytes = 48 dwords
+  d.kw0[0] = k0[0]; d.kw0[1] = k0[1]; d.kw0[2] = k0[2];
+  d.kw1[0] = k1[0]; d.kw1[1] = k1[1]; d.kw1[2] = k1[2];
+  const uint2* vp = reinterpret_cast<const uint2*>(a.v_codes + ((slot_base + slot0) / kTile + q) * kTileBytes + 24 * n);
+  const uint2 v0 = vp[0], v1 = vp[1], v2 = vp[2];
+  d.vw[0] = v0.x; d.vw[1] = v0.y; d.vw[2] = v1.x; d.vw[3] = v1.y; d.vw[4] = v2.x; d.vw[5] = v2.y;
+  const float4* nkp = reinterpret_cast<const float4*>(a.k_norms + slot_base + slot0 + 8 * q);
+  const float4* nvp = reinterpret_cast<const float4*>(a.v_norms + slot_base + slot0 + 8 * q);
+  d.nk0 = nkp[0]; d.nk1 = nkp[1]; d.nv0 = nvp[0]; d.nv1 = nvp[1];
+}
+
+// Per-wave running state of the online softmax and the PV accumulators.
+struct WaveState {
+  floatx4 acc[8];      // [dim tile d]: rows 4q + i, column n (dim 8n + d)
+  float m, l;
+};
+
+template <int G>
+struct Consts {
+  H8 qb[8], qb_lo[8];   // query operand per k-step (qb_lo only when G = 16)
+  float fscale;
+  bool lo_lane;
+  uint32_t lane_off;
+  int rel_lo, rel_hi;
+  const char* lut;
+};
+
+template <int G>
+__device__ __forceinline__ void process_block(const BlockData& cur, int slot0, int q, const Consts<G>& c,
+                                              WaveState& st) {
+  constexpr bool kSplitN = (G <= 8);
+  // ---- scores: D_T[i] = row 4q + i of tile T = token 8q + 4T + i, column n ----
+  floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#define IQ_SCORE(KAPPA)                                                        \
+  {                                                                            \
+    const half8 ka = code_operand<12 * KAPPA>(cur.kw0, c.lut, c.lane_off);     \
+    const half8 kb = code_operand<12 * KAPPA>(cur.kw1, c.lut, c.lane_off);     \
+    d0 = mfma16(ka, c.qb[KAPPA].h, d0);                                        \
+    d1 = mfma16(kb, c.qb[KAPPA].h, d1);                                        \
+    if (!kSplitN) {                                                            \
+      d0 = mfma16(ka, c.qb_lo[KAPPA].h, d0);                                   \
+      d1 = mfma16(kb, c.qb_lo[KAPPA].h, d1);                                   \
+    }                                                                          \
+  }
+  IQ_SCORE(0) IQ_SCORE(1) IQ_SCORE(2) IQ_SCORE(3) IQ_SCORE(4) IQ_SCORE(5) IQ_SCORE(6) IQ_SCORE(7)
+#undef IQ_SCORE
+  const float nk[8] = {cur.nk0.x, cur.nk0.y, cur.nk0.z, cur.nk0.w, cur.nk1.x, cur.nk1.y, cur.nk1.z, cur.nk1.w};
+  const float nv[8] = {cur.nv0.x, cur.nv0.y, cur.nv0.z, cur.nv0.w, cur.nv1.x, cur.nv1.y, cur.nv1.z, cur.nv1.w};
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[i] = d0[i];
+    t[4 + i] = d1[i];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (kSplitN) t[k] += dpp_row_ror8(t[k]);
+    t[k] *= nk[k] * c.fscale;             // the score, log2 units
+  }
+  float nvmax;
+  const bool full = slot0 >= c.rel_lo && slot0 + kBlk <= c.rel_hi;   // wave-uniform
+  if (full) {
+    nvmax = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])), fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
+  } else {
+    nvmax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rel = slot0 + 8 * q + k;
+      const bool valid = rel >= c.rel_lo && rel < c.rel_hi;
+      t[k] = valid ? t[k] : -INFINITY;    // 2^-inf = 0 below
+      nvmax = fmaxf(nvmax, valid ? nv[k] : 0.f);
+    }
+  }
+  // ---- online softmax with a lazily raised reference ----
+  const float tmax = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+  const int ex = __builtin_amdgcn_frexp_expf(nvmax);
+  float u = tmax + (ex > 0 ? static_cast<float>(ex) : 0.f);
+  u = fmaxf(u, __shfl_xor(u, 16, 64));
+  u = fmaxf(u, __shfl_xor(u, 32, 64));
+  const bool bump = u > st.m + kLazy;   // same for every lane of one head
+  if (__any(bump)) {
+    const float m_new = bump ? u : st.m;
+    const float alpha = bump ? fast_exp2(st.m - m_new) : 1.f;   // m = -inf gives 0
+    st.l *= alpha;
+    st.m = m_new;
+    // accumulator rows 4q + i belong to head (4q + i) mod 8 (or 4q + i when G = 16)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src = kSplitN ? ((4 * q + i) & 7) : (4 * q + i);
+      const float ar = __shfl(alpha, src, 64);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) st.acc[d][i] *= ar;
+    }
+  }
+  const float mref = (st.m == -INFINITY) ? 0.f : st.m;
+  // weights: token group T = tokens 8q + 4T + i; A slots (2i, 2i+1) both hold token i's weight
+  H8 pa[2], pa_lo[2];
+  float esum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float e = fast_exp2(t[k] - mref);
+    esum += e;
+    const float p = e * nv[k];
+    // hi = p truncated to 11 significant bits (exact in fp16), lo = the rest
+    const float hp = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) & 0xffffe000u);
+    if (kSplitN) {
+      pa[k >> 2].u[k & 3] = dup16(c.lo_lane ? p - hp : hp);
+    } else {
+      pa[k >> 2].u[k & 3] = dup16(hp);
+      pa_lo[k >> 2].u[k & 3] = dup16(p - hp);
+    }
+  }
+  st.l += esum;
+  // ---- PV: B = centroids of dim 8n + D for the 4 tokens 4T..4T+3 of V tile q ----
+#define IQ_PV(D)                                                                     \
+  {                                                                                  \
+    const half8 v0 = code_operand<24 * D>(cur.vw, c.lut, c.lane_off);                \
+    const half8 v1 = code_operand<24 * D + 12>(cur.vw, c.lut, c.lane_off);           \
+    st.acc[D] = mfma16(pa[0].h, v0, st.acc[D]);                                      \
+    st.acc[D] = mfma16(pa[1].h, v1, st.acc[D]);                                      \
+    if (!kSplitN) {                                                                  \
+      st.acc[D] = mfma16(pa_lo[0].h, v0, st.acc[D]);                                 \
+      st.acc[D] = mfma16(pa_lo[1].h, v1, st.acc[D]);                                 \
+    }                                                                                \
+  }
+  IQ_PV(0) IQ_PV(1) IQ_PV(2) IQ_PV(3) IQ_PV(4) IQ_PV(5) IQ_PV(6) IQ_PV(7)
+#undef IQ_PV
 }
 
 template <int G>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr bool kSplitN = (G <= 8);   // hi/lo halves share one MFMA (columns / rows g and g+8)
-  __shared__ uint2 lut[kLutEntries * kLutCopies];
+  __shared__ __align__(16) uint2 lut[kLutEntries * kLutCopies];
   __shared__ __align__(16) float qs[G][kDim];
   __shared__ float qmax[G];
   __shared__ __align__(16) float sm[kBlocks * 16];
@@ -124,19 +268,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
   const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, q = lane >> 4;
-  const uint32_t l15 = lane & 15;
   int start, len;
   const bool ok = seq_ok(a, s, &start, &len);
   const int base = start & ~(kBlk - 1);
   const int nblk = ok ? n_blocks(start, len) : 0;
   const int b_begin = split * a.blocks_per_split;
   const int b_end = min(nblk, b_begin + a.blocks_per_split);
+  const size_t slot_base = static_cast<size_t>(h) * a.capacity + base;   // cache row of block 0, slot 0
+
+  // first block's loads go out before the prologue
+  BlockData buf0, buf1;
+  int b = b_begin + wave;
+  if (b < b_end) load_block(a, slot_base, b * kBlk, n, q, buf0);
 
   // ---- prologue: code-pair table, SO(4) matrices, rotated queries ----
   for (int i = tid; i < kLutEntries * kLutCopies; i += kDecThreads) {
-    const uint32_t p = static_cast<uint32_t>(i) >> 4;
-    lut[i] = make_uint2(centroid_f16<false>(p & 7u, a.cb) | (centroid_f16<false>(p >> 3, a.cb) << 16),
-                        centroid_f16<true>(p & 7u, a.cb) | (centroid_f16<true>(p >> 3, a.cb) << 16));
+    const uint32_t p = static_cast<uint32_t>(i) >> 4, ca = p & 7u, cb = p >> 3;
+    lut[i] = make_uint2(centroid_f16<false>(ca, a.cb) | (centroid_f16<true>(ca, a.cb) << 16),
+                        centroid_f16<false>(cb, a.cb) | (centroid_f16<true>(cb, a.cb) << 16));
   }
   load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
   __syncthreads();
@@ -161,144 +310,57 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
   __syncthreads();
 
   // ---- per-lane constants: query operands, score scale ----
+  Consts<G> c;
   const int g = kSplitN ? (n & 7) : n;     // head of this lane's score column / P row
   const bool gvalid = g < G;
   const float qm = gvalid ? qmax[g] : 0.f;
   const float inv_qm = qm > 0.f ? 1.0f / qm : 0.f;
-  const float fscale = a.qscale * qm * a.cb.inv_alpha;
-  H8 qb[4], qb_lo[4];
+  c.fscale = a.qscale * qm * a.cb.inv_alpha;
+  // k-step kk, slot pair e: dim 32q + 4kk + e (both slots of the pair hold the same value)
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = gvalid ? qs[g][32 * q + 8 * kk + i] * inv_qm : 0.f;
-      const _Float16 hh = static_cast<_Float16>(x);
-      const _Float16 ll = static_cast<_Float16>(x - static_cast<float>(hh));
+    for (int e = 0; e < 4; ++e) {
+      const float x = gvalid ? qs[g][32 * q + 4 * kk + e] * inv_qm : 0.f;
+      const float hx = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xffffe000u);
       if (kSplitN) {
-        qb[kk].h[i] = (n < 8) ? hh : ll;
+        c.qb[kk].u[e] = dup16(n < 8 ? hx : x - hx);
       } else {
-        qb[kk].h[i] = hh;
-        qb_lo[kk].h[i] = ll;
+        c.qb[kk].u[e] = dup16(hx);
+        c.qb_lo[kk].u[e] = dup16(x - hx);
       }
     }
   }
+  c.lo_lane = kSplitN && n >= 8;   // this lane's P row carries the lo half
+  c.lane_off = (lane & 15) * 8;
+  c.rel_lo = start - base;
+  c.rel_hi = start - base + len;
+  c.lut = reinterpret_cast<const char*>(lut);
 
-  floatx4 acc[8];
+  WaveState st;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) acc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int d = 0; d < 8; ++d) st.acc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
 
-  const size_t slot_base = static_cast<size_t>(h) * a.capacity + base;   // cache row of block 0, slot 0
-  const int rel_lo = start - base, rel_hi = start - base + len;          // valid slots relative to base
-  // A-operand rows of the two score tiles: tile T row r <-> token 8 (r/4) + 4 T + r % 4
-  const int tok_a0 = 8 * (n >> 2) + (n & 3);
-
-  for (int b = b_begin + wave; b < b_end; b += kWaves) {
-    const int slot0 = b * kBlk;
-    // ---- loads ----
-    uint32_t kw0[3], kw1[3], vw[6];
-    {
-      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(a.k_codes + (slot_base + slot0 + tok_a0) * kRowBytes + 12 * q);
-      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(a.k_codes + (slot_base + slot0 + tok_a0 + 4) * kRowBytes + 12 * q);
-      kw0[0] = k0[0]; kw0[1] = k0[1]; kw0[2] = k0[2];
-      kw1[0] = k1[0]; kw1[1] = k1[1]; kw1[2] = k1[2];
-      const uint2* vp = reinterpret_cast<const uint2*>(a.v_codes + ((slot_base + slot0) / kTile + q) * kTileBytes + 24 * n);
-      const uint2 v0 = vp[0], v1 = vp[1], v2 = vp[2];
-      vw[0] = v0.x; vw[1] = v0.y; vw[2] = v1.x; vw[3] = v1.y; vw[4] = v2.x; vw[5] = v2.y;
-    }
-    const float4* nkp = reinterpret_cast<const float4*>(a.k_norms + slot_base + slot0 + 8 * q);
-    const float4* nvp = reinterpret_cast<const float4*>(a.v_norms + slot_base + slot0 + 8 * q);
-    const float4 nk0 = nkp[0], nk1 = nkp[1], nv0 = nvp[0], nv1 = nvp[1];
-    const float nk[8] = {nk0.x, nk0.y, nk0.z, nk0.w, nk1.x, nk1.y, nk1.z, nk1.w};
-    const float nv[8] = {nv0.x, nv0.y, nv0.z, nv0.w, nv1.x, nv1.y, nv1.z, nv1.w};
-
-    // ---- scores: D_T[i] = row 4q + i of tile T = token 8q + 4T + i, column n ----
-    floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-    // (c_hi + c_lo)(q_hi + q_lo) without the c_lo q_lo term (~2^-22)
-#define IQ_SCORE(KAPPA)                                                      \
-    {                                                                        \
-      const Operand ka = k_operand<KAPPA>(kw0, lut, l15);                    \
-      const Operand kb = k_operand<KAPPA>(kw1, lut, l15);                    \
-      d0 = mfma16(ka.hi, qb[KAPPA].h, d0);                                   \
-      d1 = mfma16(kb.hi, qb[KAPPA].h, d1);                                   \
-      d0 = mfma16(ka.lo, qb[KAPPA].h, d0);                                   \
-      d1 = mfma16(kb.lo, qb[KAPPA].h, d1);                                   \
-      if (!kSplitN) {                                                        \
-        d0 = mfma16(ka.hi, qb_lo[KAPPA].h, d0);                              \
-        d1 = mfma16(kb.hi, qb_lo[KAPPA].h, d1);                              \
-      }                                                                      \
-    }
-    IQ_SCORE(0) IQ_SCORE(1) IQ_SCORE(2) IQ_SCORE(3)
-#undef IQ_SCORE
-    float sv[8];
-    bool valid[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = d0[i];
-      sv[4 + i] = d1[i];
-    }
-    float mloc = -INFINITY, nvmax = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (kSplitN) sv[k] += dpp_row_ror8(sv[k]);
-      const int rel = slot0 + 8 * q + k;
-      valid[k] = rel >= rel_lo && rel < rel_hi;
-      sv[k] = valid[k] ? sv[k] * fscale * nk[k] : -INFINITY;
-      mloc = fmaxf(mloc, sv[k]);
-      nvmax = fmaxf(nvmax, valid[k] ? nv[k] : 0.f);
-    }
-    // ---- online softmax (reference m bounds s + log2 nV) ----
-    const int ex = __builtin_amdgcn_frexp_expf(nvmax);
-    float u = mloc + (ex > 0 ? static_cast<float>(ex) : 0.f);
-    u = fmaxf(u, __shfl_xor(u, 16, 64));
-    u = fmaxf(u, __shfl_xor(u, 32, 64));
-    const float m_new = fmaxf(m_run, u);
-    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - mref);
-    float esum = 0.f, pv[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float e = exp2f(sv[k] - mref);
-      esum += e;
-      pv[k] = (valid[k] && gvalid) ? e * nv[k] : 0.f;
-    }
-    l_run = l_run * alpha + esum;
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {
-      // accumulator rows 4q + i belong to head (4q + i) mod 8 (or 4q + i when G = 16)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int src = kSplitN ? ((4 * q + i) & 7) : (4 * q + i);
-        const float ar = __shfl(alpha, src, 64);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d][i] *= ar;
-      }
-    }
-    // ---- PV: A row n holds weights of head g for tokens 8q .. 8q+7 ----
-    H8 pa, pa_lo;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const _Float16 hh = static_cast<_Float16>(pv[k]);
-      const _Float16 ll = static_cast<_Float16>(pv[k] - static_cast<float>(hh));
-      if (kSplitN) {
-        pa.h[k] = (n < 8) ? hh : ll;
-      } else {
-        pa.h[k] = hh;
-        pa_lo.h[k] = ll;
-      }
-    }
-#define IQ_PV(D)                                              \
-    {                                                         \
-      const Operand vb = v_operand<D>(vw, lut, l15);          \
-      acc[D] = mfma16(pa.h, vb.hi, acc[D]);                   \
-      acc[D] = mfma16(pa.h, vb.lo, acc[D]);                   \
-      if (!kSplitN) acc[D] = mfma16(pa_lo.h, vb.hi, acc[D]);  \
-    }
-    IQ_PV(0) IQ_PV(1) IQ_PV(2) IQ_PV(3) IQ_PV(4) IQ_PV(5) IQ_PV(6) IQ_PV(7)
-#undef IQ_PV
+  // two buffers, alternating, so the next block's loads are in flight during compute
+  while (b < b_end) {
+    if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
+    process_block<G>(buf0, b * kBlk, q, c, st);
+    b += kWaves;
+    if (b >= b_end) break;
+    if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf0);
+    process_block<G>(buf1, b * kBlk, q, c, st);
+    b += kWaves;
   }
 
   // ---- per-wave totals ----
+  float acc[8][4];
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[d][i] = st.acc[d][i];
+  float l_run = st.l;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (kSplitN) {
@@ -308,7 +370,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
       for (int i = 0; i < 4; ++i) acc[d][i] += __shfl_xor(acc[d][i], 32, 64);   // hi rows + lo rows
   }
   if (q == 0 && n < G) {
-    wm[wave][n] = m_run;
+    wm[wave][n] = st.m;
     wl[wave][n] = l_run;
   }
   if (!kSplitN || q < 2) {
@@ -368,10 +430,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 // out_j = sum_s 2^(m_s - M) o_{s,j} / sum_s 2^(m_s - M) l_s.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeChunk = 32;
+constexpr int kMergeParts = kMergeThreads / kMergeChunk;   // 8 split subsets per dim
 
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float wts[kMaxSplits];
-  __shared__ float red[kMergeThreads / kMergeChunk][kMergeChunk];
+  __shared__ float red[kMergeParts][kMergeChunk];
   __shared__ float rmax[kMergeThreads / 64], rsum[kMergeThreads / 64];
   const int chunk = blockIdx.x, qh = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -404,16 +467,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __syncthreads();
   l = rsum[0] + rsum[1] + rsum[2] + rsum[3];
   const int j = tid & (kMergeChunk - 1), part = tid / kMergeChunk;
-  float acc = 0.f;
-  for (int k = part; k < used; k += kMergeThreads / kMergeChunk)
-    acc += wts[k] * rec[static_cast<size_t>(k) * kRec + 4 + chunk * kMergeChunk + j];
-  red[part][j] = acc;
+  const float* col = rec + 4 + chunk * kMergeChunk + j;
+  // four independent accumulators keep several loads in flight
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int k = part;
+  for (; k + 3 * kMergeParts < used; k += 4 * kMergeParts) {
+    acc0 += wts[k] * col[static_cast<size_t>(k) * kRec];
+    acc1 += wts[k + kMergeParts] * col[static_cast<size_t>(k + kMergeParts) * kRec];
+    acc2 += wts[k + 2 * kMergeParts] * col[static_cast<size_t>(k + 2 * kMergeParts) * kRec];
+    acc3 += wts[k + 3 * kMergeParts] * col[static_cast<size_t>(k + 3 * kMergeParts) * kRec];
+  }
+  for (; k < used; k += kMergeParts) acc0 += wts[k] * col[static_cast<size_t>(k) * kRec];
+  red[part][j] = (acc0 + acc1) + (acc2 + acc3);
   __syncthreads();
   if (tid < kMergeChunk) {
-    float t = 0.f;
+    float tsum = 0.f;
 #pragma unroll
-    for (int p = 0; p < kMergeThreads / kMergeChunk; ++p) t += red[p][tid];
-    out[tid] = t / l;
+    for (int p = 0; p < kMergeParts; ++p) tsum += red[p][tid];
+    out[tid] = tsum / l;
   }
 }
 
