@@ -129,7 +129,7 @@ def main():
     new_v = [synth_kv(1, 20_000 + l) for l in range(L)]
     seq_start = torch.zeros(1, dtype=torch.int32, device=dev)
     seq_len = torch.full((1,), T, dtype=torch.int32, device=dev)
-    ws = torch.empty(iq.iq_decode_workspace_bytes(1, hq, hkv, T), dtype=torch.uint8, device=dev)
+    ws = iq.decode_workspace(1, hq, hkv, T, device=dev)
     outs = [torch.empty((1, hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
 
     n_ev = (args.steps) * L

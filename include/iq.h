@@ -146,7 +146,10 @@ IQ_API size_t iq_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int
  *   scale      softmax scale (1/sqrt(128) for plain attention).
  *   out        device float [n_seqs][num_q_heads][128].
  *   workspace  device memory of at least iq_decode_workspace_bytes() bytes,
- *              16-byte aligned; its contents need no initialisation.
+ *              16-byte aligned, owned by the caller. It holds the split-K
+ *              partial results (no initialisation needed); calls that share a
+ *              workspace must not run concurrently.
+ *   n_seqs     0 .. 65535.
  * Query head g reads KV head g / (num_q_heads / num_kv_heads); the group size
  * must be 1, 2, 4, 8 or 16. A sequence with seq_len = 0 gets a zero output. A sequence
  * whose rows fall outside [0, capacity), or whose length exceeds max_seq_len,

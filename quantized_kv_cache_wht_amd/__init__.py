@@ -230,6 +230,12 @@ def iq_decode_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, 
     return int(lib().iq_decode_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, max_seq_len))
 
 
+def decode_workspace(n_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int, device="cuda"):
+    """A decode workspace for these sizes (its contents need no initialisation)."""
+    need = iq_decode_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, max_seq_len)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def iq_decode_attention(cache: PackedKVCache, q: torch.Tensor, seq_start: torch.Tensor, seq_len: torch.Tensor,
                         max_seq_len: int, scale: float | None = None, out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
@@ -239,7 +245,7 @@ def iq_decode_attention(cache: PackedKVCache, q: torch.Tensor, seq_start: torch.
     out = torch.empty_like(q) if out is None else out
     need = iq_decode_workspace_bytes(n_seqs, hq, cache.num_kv_heads, max_seq_len)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(n_seqs, hq, cache.num_kv_heads, max_seq_len, q.device)
     view = cache.view()
     _check("iq_decode_attention",
            lib().iq_decode_attention(ctypes.byref(view), _dev(q, torch.float32, "q"), hq,

@@ -181,9 +181,7 @@ static bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g 
 
 size_t iq_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
   if (n_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 0) return 0;
-  int32_t bps, n_splits;
-  decode_plan(n_seqs, num_kv_heads, max_seq_len, &bps, &n_splits);
-  return decode_workspace_floats(n_seqs, num_q_heads, n_splits) * sizeof(float);
+  return decode_workspace_bytes(n_seqs, num_q_heads, decode_plan(n_seqs, num_kv_heads, max_seq_len));
 }
 
 iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t num_q_heads,
@@ -199,8 +197,9 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   if (n_seqs == 0) return IQ_OK;
   if (!q || !seq_start || !seq_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 15u) return IQ_ERR_INVALID_ARG;
-  if (workspace_bytes < iq_decode_workspace_bytes(n_seqs, num_q_heads, view->num_kv_heads, max_seq_len))
-    return IQ_ERR_WORKSPACE;
+  if (n_seqs > 65535 || view->num_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;   // grid y / z limits
+  const DecodePlan plan = decode_plan(n_seqs, view->num_kv_heads, max_seq_len);
+  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, plan)) return IQ_ERR_WORKSPACE;
   DecodeArgs a{};
   a.k_codes = view->k_codes;
   a.v_codes = view->v_codes;
@@ -218,7 +217,8 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   a.group = group;
   a.capacity = view->capacity;
   a.max_seq_len = max_seq_len;
-  decode_plan(n_seqs, view->num_kv_heads, max_seq_len, &a.blocks_per_split, &a.n_splits);
+  a.blocks_per_split = plan.blocks_per_split;
+  a.n_splits = plan.n_splits;
   a.qscale = scale * 1.4426950408889634f;   // log2(e): scores kept in base 2
   a.cb = codebook();
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));

@@ -54,9 +54,14 @@ constexpr int kDecThreads = 256;
 constexpr int kWaves = kDecThreads / 64;
 constexpr int kBlk = 32;             // cache slots per wave iteration
 constexpr int kRec = 132;            // floats per partial record: m, l, 2 pad, o[128]
-constexpr int kTargetBlocks = 512;   // split-K occupancy target (work-groups)
-constexpr int kMinBlocksPerSplit = 8;
+constexpr int kTargetBlocks = 512;   // split-K occupancy target (work-groups): 2 per CU
+constexpr int kMinBlocksPerSplit = 4;
+constexpr int kMaxBlocksPerSplit = 64;   // beyond this, more (shorter) splits balance ragged batches
 constexpr int kMaxSplits = 2048;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeLanes = kDim / 4;                    // lanes per record, 4 dims each
+constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by side
+constexpr int kMergeChunk = 4;                           // records per lane per round of loads
 constexpr int kLutEntries = 64;      // all pairs of 3-bit codes
 constexpr int kLutCopies = 16;       // one per lane of a 16-lane group
 constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
@@ -255,6 +260,13 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int slot0, i
 #undef IQ_PV
 }
 
+// Splits of (seq, kv head) that hold at least one block: split k covers
+// blocks [k bps, (k+1) bps), the last one also the block that a start not
+// aligned to 32 adds beyond the plan.
+__device__ __forceinline__ int live_splits(int nblk, int bps, int n_splits) {
+  return nblk > 0 ? min(n_splits, (nblk + bps - 1) / bps) : 0;
+}
+
 template <int G>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr bool kSplitN = (G <= 8);   // hi/lo halves share one MFMA (columns / rows g and g+8)
@@ -262,8 +274,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   __shared__ __align__(16) float qs[G][kDim];
   __shared__ float qmax[G];
   __shared__ __align__(16) float sm[kBlocks * 16];
-  __shared__ float wm[kWaves][G], wl[kWaves][G], mfin[G], lfin[G];
-  __shared__ __align__(16) float wo[kWaves][G][kDim];
+  constexpr int kRows = kSplitN ? 2 * G : G;   // accumulator rows kept per wave (hi and lo halves)
+  __shared__ float wm[kWaves][G], wl[kWaves][G];
+  __shared__ __align__(16) float wo[kWaves][kRows][kDim];
 
   const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -272,29 +285,55 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   const bool ok = seq_ok(a, s, &start, &len);
   const int base = start & ~(kBlk - 1);
   const int nblk = ok ? n_blocks(start, len) : 0;
+  if (split >= live_splits(nblk, a.blocks_per_split, a.n_splits)) return;   // the merge skips this split
   const int b_begin = split * a.blocks_per_split;
-  const int b_end = min(nblk, b_begin + a.blocks_per_split);
+  const int b_end = split == a.n_splits - 1 ? nblk : min(nblk, b_begin + a.blocks_per_split);
   const size_t slot_base = static_cast<size_t>(h) * a.capacity + base;   // cache row of block 0, slot 0
 
-  // first block's loads go out before the prologue
+  // this wave's first two blocks are loaded before the prologue
   BlockData buf0, buf1;
   int b = b_begin + wave;
   if (b < b_end) load_block(a, slot_base, b * kBlk, n, q, buf0);
+  if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
+  // rotation parameters (threads 0..31, one SO(4) block each) and this work-group's
+  // queries (threads 0..4G-1, 32 dims each) are fetched before the first barrier too
+  float rq[8];
+  if (tid < kBlocks) {
+    const float4* rp = reinterpret_cast<const float4*>(a.rot + (static_cast<size_t>(h) * kBlocks + tid) * 8);
+    const float4 r0 = rp[0], r1 = rp[1];
+    rq[0] = r0.x; rq[1] = r0.y; rq[2] = r0.z; rq[3] = r0.w;
+    rq[4] = r1.x; rq[5] = r1.y; rq[6] = r1.z; rq[7] = r1.w;
+  }
+  float xq[kPerLane];
+  if (tid < 4 * G) {
+    const float4* src = reinterpret_cast<const float4*>(
+        a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + (tid >> 2)) * kDim + (tid & 3) * kPerLane);
+#pragma unroll
+    for (int i = 0; i < kPerLane / 4; ++i) {
+      const float4 v = src[i];
+      xq[4 * i] = v.x; xq[4 * i + 1] = v.y; xq[4 * i + 2] = v.z; xq[4 * i + 3] = v.w;
+    }
+  }
 
   // ---- prologue: code-pair table, SO(4) matrices, rotated queries ----
-  for (int i = tid; i < kLutEntries * kLutCopies; i += kDecThreads) {
-    const uint32_t p = static_cast<uint32_t>(i) >> 4, ca = p & 7u, cb = p >> 3;
-    lut[i] = make_uint2(centroid_f16<false>(ca, a.cb) | (centroid_f16<true>(ca, a.cb) << 16),
-                        centroid_f16<false>(cb, a.cb) | (centroid_f16<true>(cb, a.cb) << 16));
+  {
+    // thread t fills copies 4(t%4) .. 4(t%4)+3 of pair t/4
+    const uint32_t p = static_cast<uint32_t>(tid) >> 2, ca = p & 7u, cb = p >> 3;
+    const uint2 e = make_uint2(centroid_f16<false>(ca, a.cb) | (centroid_f16<true>(ca, a.cb) << 16),
+                               centroid_f16<false>(cb, a.cb) | (centroid_f16<true>(cb, a.cb) << 16));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lut[p * kLutCopies + (tid & 3) * 4 + k] = e;
   }
-  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  if (tid < kBlocks) {
+    float m[16];
+    so4_matrix(rq, 0.08838834764831845f, m);   // 1/sqrt(128)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm[tid * 16 + i] = m[i];
+  }
   __syncthreads();
   if (tid < 4 * G) {
     const int g = tid >> 2, part = tid & 3;
-    float x[kPerLane];
-    const float* src = a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + g) * kDim + part * kPerLane;
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) x[i] = src[i];
+    float (&x)[kPerLane] = xq;
     wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
     float mx = 0.f;
@@ -343,48 +382,43 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // two buffers, alternating, so the next block's loads are in flight during compute
+  // two buffers, alternating: a block is computed while the next one is in flight
   while (b < b_end) {
-    if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
     process_block<G>(buf0, b * kBlk, q, c, st);
+    if (b + 2 * kWaves < b_end) load_block(a, slot_base, (b + 2 * kWaves) * kBlk, n, q, buf0);
     b += kWaves;
     if (b >= b_end) break;
-    if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf0);
     process_block<G>(buf1, b * kBlk, q, c, st);
+    if (b + 2 * kWaves < b_end) load_block(a, slot_base, (b + 2 * kWaves) * kBlk, n, q, buf1);
     b += kWaves;
   }
 
   // ---- per-wave totals ----
-  float acc[8][4];
-#pragma unroll
-  for (int d = 0; d < 8; ++d)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[d][i] = st.acc[d][i];
   float l_run = st.l;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (kSplitN) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[d][i] += __shfl_xor(acc[d][i], 32, 64);   // hi rows + lo rows
-  }
   if (q == 0 && n < G) {
     wm[wave][n] = st.m;
     wl[wave][n] = l_run;
   }
-  if (!kSplitN || q < 2) {
+  // accumulator row 4q + i: G <= 8: hi half of head (4q+i) for q < 2, lo half of head (4q+i-8) for q >= 2,
+  // kept as rows g and G + g; G = 16: head 4q+i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gr = 4 * q + i;
-      if (gr < G) {
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * q + i;
+    const int gr = kSplitN ? (m & 7) : m;
+    const int row = (kSplitN && m >= 8) ? G + gr : gr;
+    if (gr < G) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) wo[wave][gr][8 * n + d] = acc[d][i];
-      }
+      for (int d = 0; d < 8; ++d) wo[wave][row][8 * n + d] = st.acc[d][i];
     }
   }
   __syncthreads();
-  // ---- merge the waves ----
+  // ---- merge the waves (and the hi/lo rows) into this split's records ----
+  // record of (seq, head hg, split): m, l, pad, pad, o'[128] with o' still in
+  // the rotated domain (the merge applies the one inverse rotation)
+  float* rec0 = a.ws + ((static_cast<size_t>(s) * a.num_q_heads + h * G) * a.n_splits + split) * kRec;
+  const size_t head_stride = static_cast<size_t>(a.n_splits) * kRec;
   for (int idx = tid; idx < G * kDim; idx += kDecThreads) {
     const int gr = idx >> 7, j = idx & (kDim - 1);
     float mx = -INFINITY;
@@ -393,9 +427,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
     float o = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) o += exp2f(wm[w][gr] - mx) * wo[w][gr][j];
+      for (int w = 0; w < kWaves; ++w) {
+        const float v = kSplitN ? wo[w][gr][j] + wo[w][G + gr][j] : wo[w][gr][j];
+        o += fast_exp2(wm[w][gr] - mx) * v;
+      }
     }
-    wo[0][gr][j] = o * a.cb.inv_alpha;   // the PV operand carried alpha * c
+    rec0[gr * head_stride + 4 + j] = o * a.cb.inv_alpha;   // the PV operand carried alpha * c
   }
   if (tid < G) {
     float mx = -INFINITY;
@@ -406,107 +443,131 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) l += exp2f(wm[w][tid] - mx) * wl[w][tid];
     }
-    mfin[tid] = mx;
-    lfin[tid] = l;
-  }
-  __syncthreads();
-  // ---- rotate back (linear, so the unnormalised sum can be rotated) and store ----
-  if (tid < 4 * G) {
-    const int gr = tid >> 2, part = tid & 3;
-    float x[kPerLane];
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) x[i] = wo[0][gr][part * kPerLane + i];
-    so4_apply_lane<true>(x, sm, part);
-    wht128_quad(x, part);
-    float* rec = a.ws + ((static_cast<size_t>(s) * a.num_q_heads + h * G + gr) * a.n_splits + split) * kRec;
-#pragma unroll
-    for (int i = 0; i < kPerLane; i += 4)
-      *reinterpret_cast<float4*>(rec + 4 + part * kPerLane + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
-    if (part == 0) *reinterpret_cast<float4*>(rec) = make_float4(mfin[gr], lfin[gr], 0.f, 0.f);
+    float* r = rec0 + tid * head_stride;
+    r[0] = mx;
+    r[1] = l;
   }
 }
 
-// Merge the splits of one (sequence, query head, 32-dim chunk):
-// out_j = sum_s 2^(m_s - M) o_{s,j} / sum_s 2^(m_s - M) l_s.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 32;
-constexpr int kMergeParts = kMergeThreads / kMergeChunk;   // 8 split subsets per dim
-
+// One work-group per (seq, query head): merges the live splits' records
+//   M = max m_k, l = sum 2^(m_k - M) l_k, o' = sum 2^(m_k - M) o'_k,
+// then out = Hn B^T (o' / l), the single inverse rotation. Lane t reads dims
+// 4 (t % 32) .. +3 of records t / 32, t / 32 + 32, ...; the 32 rows are then
+// combined in LDS. An empty sequence gives 0, an invalid one NaN.
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ float wts[kMaxSplits];
-  __shared__ float red[kMergeParts][kMergeChunk];
-  __shared__ float rmax[kMergeThreads / 64], rsum[kMergeThreads / 64];
-  const int chunk = blockIdx.x, qh = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float rm[kMergeRows], rl[kMergeRows];
+  __shared__ __align__(16) float ro[kMergeRows][kDim];
+  __shared__ __align__(16) float sm[kBlocks * 16];
+  __shared__ __align__(16) float fin[kDim];
+  const int hq = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
+  const int h = hq / a.group;
   int start, len;
   const bool ok = seq_ok(a, s, &start, &len);
-  float* out = a.out + (static_cast<size_t>(s) * a.num_q_heads + qh) * kDim + chunk * kMergeChunk;
-  if (!ok || len == 0) {
-    if (tid < kMergeChunk) out[tid] = ok ? 0.f : NAN;
-    return;   // uniform
+  const int nblk = ok ? n_blocks(start, len) : 0;
+  const int live = live_splits(nblk, a.blocks_per_split, a.n_splits);
+
+  float rq[8];
+  if (tid < kBlocks) {
+    const float4* rp = reinterpret_cast<const float4*>(a.rot + (static_cast<size_t>(h) * kBlocks + tid) * 8);
+    const float4 r0 = rp[0], r1 = rp[1];
+    rq[0] = r0.x; rq[1] = r0.y; rq[2] = r0.z; rq[3] = r0.w;
+    rq[4] = r1.x; rq[5] = r1.y; rq[6] = r1.z; rq[7] = r1.w;
   }
-  const int used = (n_blocks(start, len) + a.blocks_per_split - 1) / a.blocks_per_split;
-  const float* rec = a.ws + (static_cast<size_t>(s) * a.num_q_heads + qh) * a.n_splits * kRec;
-  float mx = -INFINITY;
-  for (int k = tid; k < used; k += kMergeThreads) mx = fmaxf(mx, rec[static_cast<size_t>(k) * kRec]);
+  const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.n_splits * kRec;
+  float mx = -INFINITY, l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = row; k0 < live; k0 += kMergeRows * kMergeChunk) {
+    float mv[kMergeChunk], lv[kMergeChunk];
+    float4 ov[kMergeChunk];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if (lane == 0) rmax[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
-  float l = 0.f;
-  for (int k = tid; k < used; k += kMergeThreads) {
-    const float* r = rec + static_cast<size_t>(k) * kRec;
-    const float w = exp2f(r[0] - mx);
-    wts[k] = w;
-    l += w * r[1];
+    for (int i = 0; i < kMergeChunk; ++i) {
+      const int k = k0 + i * kMergeRows;
+      const bool in = k < live;
+      const float* r = recs + static_cast<size_t>(in ? k : 0) * kRec;
+      mv[i] = in ? r[0] : -INFINITY;
+      lv[i] = in ? r[1] : 0.f;
+      ov[i] = in ? reinterpret_cast<const float4*>(r + 4)[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float cm = mx;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) cm = fmaxf(cm, mv[i]);
+    if (cm == -INFINITY) continue;   // only records without tokens so far
+    const float f = exp2f(mx - cm);   // mx = -inf gives 0
+    l *= f;
+    o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      const float w = mv[i] == -INFINITY ? 0.f : exp2f(mv[i] - cm);
+      l += w * lv[i];
+      o.x += w * ov[i].x; o.y += w * ov[i].y; o.z += w * ov[i].z; o.w += w * ov[i].w;
+    }
+    mx = cm;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
-  if (lane == 0) rsum[wave] = l;
-  __syncthreads();
-  l = rsum[0] + rsum[1] + rsum[2] + rsum[3];
-  const int j = tid & (kMergeChunk - 1), part = tid / kMergeChunk;
-  const float* col = rec + 4 + chunk * kMergeChunk + j;
-  // four independent accumulators keep several loads in flight
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  int k = part;
-  for (; k + 3 * kMergeParts < used; k += 4 * kMergeParts) {
-    acc0 += wts[k] * col[static_cast<size_t>(k) * kRec];
-    acc1 += wts[k + kMergeParts] * col[static_cast<size_t>(k + kMergeParts) * kRec];
-    acc2 += wts[k + 2 * kMergeParts] * col[static_cast<size_t>(k + 2 * kMergeParts) * kRec];
-    acc3 += wts[k + 3 * kMergeParts] * col[static_cast<size_t>(k + 3 * kMergeParts) * kRec];
+  if (d4 == 0) {
+    rm[row] = mx;
+    rl[row] = l;
   }
-  for (; k < used; k += kMergeParts) acc0 += wts[k] * col[static_cast<size_t>(k) * kRec];
-  red[part][j] = (acc0 + acc1) + (acc2 + acc3);
-  __syncthreads();
-  if (tid < kMergeChunk) {
-    float tsum = 0.f;
+  reinterpret_cast<float4*>(ro[row])[d4] = o;
+  if (tid < kBlocks) {
+    float m[16];
+    so4_matrix(rq, 0.08838834764831845f, m);   // 1/sqrt(128)
 #pragma unroll
-    for (int p = 0; p < kMergeParts; ++p) tsum += red[p][tid];
-    out[tid] = tsum / l;
+    for (int i = 0; i < 16; ++i) sm[tid * 16 + i] = m[i];
+  }
+  __syncthreads();
+  if (tid < kDim) {
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int r = 0; r < kMergeRows; ++r) M = fmaxf(M, rm[r]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int r = 0; r < kMergeRows; ++r) {
+        const float w = exp2f(rm[r] - M);
+        L += w * rl[r];
+        O += w * ro[r][tid];
+      }
+    }
+    fin[tid] = L > 0.f ? O / L : 0.f;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    float x[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) x[i] = fin[tid * kPerLane + i];
+    so4_apply_lane<true>(x, sm, tid);
+    wht128_quad(x, tid);
+    float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + tid * kPerLane);
+#pragma unroll
+    for (int i = 0; i < kPerLane / 4; ++i)
+      dst[i] = ok ? make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3])
+                  : make_float4(NAN, NAN, NAN, NAN);
   }
 }
 
-void decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t* blocks_per_split,
-                 int32_t* n_splits) {
-  const int64_t blocks = (static_cast<int64_t>(max_seq_len) + 2 * kBlk - 2) / kBlk;   // worst-case alignment
+DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  DecodePlan p{};
+  // blocks of a 32-aligned start; a misaligned one adds a block, which the last split takes
+  const int64_t blocks = (static_cast<int64_t>(max_seq_len > 0 ? max_seq_len : 1) + kBlk - 1) / kBlk;
   const int64_t pairs = static_cast<int64_t>(n_seqs > 0 ? n_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int64_t want_splits = (kTargetBlocks + pairs - 1) / pairs;
   int64_t bps = (blocks + want_splits - 1) / want_splits;
   if (bps < kMinBlocksPerSplit) bps = kMinBlocksPerSplit;
+  if (bps > kMaxBlocksPerSplit) bps = kMaxBlocksPerSplit;
   int64_t ns = (blocks + bps - 1) / bps;
   if (ns > kMaxSplits) {
     bps = (blocks + kMaxSplits - 1) / kMaxSplits;
     ns = (blocks + bps - 1) / bps;
   }
   if (ns < 1) ns = 1;
-  *blocks_per_split = static_cast<int32_t>(bps);
-  *n_splits = static_cast<int32_t>(ns);
+  p.blocks_per_split = static_cast<int32_t>(bps);
+  p.n_splits = static_cast<int32_t>(ns);
+  return p;
 }
 
-size_t decode_workspace_floats(int32_t n_seqs, int32_t num_q_heads, int32_t n_splits) {
-  return static_cast<size_t>(n_seqs) * num_q_heads * n_splits * kRec;
+size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodePlan& p) {
+  return static_cast<size_t>(n_seqs) * num_q_heads * p.n_splits * kRec * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
@@ -521,8 +582,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(kDim / kMergeChunk, a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0,
-                     st, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ struct DecodeArgs {
   const int32_t* seq_start;
   const int32_t* seq_len;
   float* out;
-  float* ws;             // partials [n_seqs][Hq][n_splits][132]
+  float* ws;             // split partials [n_seqs][Hq][n_splits][132]
   int32_t n_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -84,9 +84,12 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f16, hipStream_t s);
 
 // split-K plan for decode (shared by the workspace query and the launch)
-void decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t* blocks_per_split,
-                 int32_t* n_splits);
-size_t decode_workspace_floats(int32_t n_seqs, int32_t num_q_heads, int32_t n_splits);
+struct DecodePlan {
+  int32_t blocks_per_split, n_splits;
+};
+DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len);
+// Workspace: one partial record (m, l, 2 pad, o[128] fp32) per (seq, query head, split).
+size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodePlan& p);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace iq

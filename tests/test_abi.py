@@ -76,10 +76,11 @@ def test_decode_validation():
     assert L.iq_decode_attention(*args(ws=need - 1)) == -4
     assert L.iq_decode_attention(*args(n=-1)) == -1
     assert L.iq_decode_attention(*args(n=0)) == 0
+    assert L.iq_decode_attention(*args(n=65536, ws=1 << 40)) == -2   # grid limit
     assert L.iq_decode_workspace_bytes(-1, 8, 2, 100) == 0
     # workspace grows with context and shrinks to one split for short contexts
     assert L.iq_decode_workspace_bytes(1, 32, 4, 32768) >= L.iq_decode_workspace_bytes(1, 32, 4, 1024)
-    assert L.iq_decode_workspace_bytes(1, 32, 8, 1) == 32 * 132 * 4
+    assert L.iq_decode_workspace_bytes(1, 32, 8, 1) == 32 * 132 * 4   # one record per query head
 
 
 def test_dequant_and_rotate_validation():

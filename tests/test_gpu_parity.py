@@ -230,6 +230,8 @@ def _upload(rot, kr, kn, vt, vn):
     (32, 4, [2100]),
     (16, 1, [513, 3]),
     (32, 8, [1024, 77, 4000]),
+    (32, 4, [13, 4096]),          # start 13: one block more than an aligned start, taken by the last split
+    (4, 1, [31, 1024, 1]),
 ])
 def test_decode_matches_oracle(hq, hkv, lens):
     lens = np.array(lens, np.int32)
@@ -268,6 +270,25 @@ def test_decode_is_deterministic():
     a = _np(iq.iq_decode_attention(cache, q, st, ln, 5000))
     b = _np(iq.iq_decode_attention(cache, q, st, ln, 5000))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_decode_reuses_one_workspace_across_shapes():
+    """One uninitialised workspace serves calls of different shapes."""
+    hkv, hq = 4, 32
+    rot, kr, kn, vr, vn = _oracle_cache(41, hkv, 9000)
+    cache = _upload(rot, kr, kn, vr, vn)
+    q = iqinputs.queries(41, 0, 3, hq)
+    ws = iq.decode_workspace(3, hq, hkv, 9000)
+    ws.fill_(0xFF)                                       # NaN bit patterns: nothing may depend on the contents
+    for lens, ml in [([9000], 9000), ([100, 5000, 1], 9000), ([40, 40, 40], 64), ([9000], 9000), ([3000, 0, 2999], 3000)]:
+        lens = np.array(lens, np.int32)
+        starts = np.array([0, 3000, 6000][:len(lens)], np.int32) if len(lens) > 1 else np.array([0], np.int32)
+        qq = q[:len(lens)]
+        got = _np(iq.iq_decode_attention(cache, _t(qq), _t(starts), _t(lens), ml, workspace=ws))
+        fresh = _np(iq.iq_decode_attention(cache, _t(qq), _t(starts), _t(lens), ml))
+        assert np.array_equal(got.view(np.uint32), fresh.view(np.uint32)), list(lens)
+        ref = R.decode_attention(qq, kr, kn, vr, vn, rot, starts, lens, SCALE, C32)
+        _assert_attention_close(got, ref, f"reused workspace lens={list(lens)}")
 
 
 def test_single_head_workload_end_to_end():
