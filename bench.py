@@ -6,7 +6,9 @@ fp16 with four fixed outlier channels x8 (synthetic, seeded). Untimed set-up
 fills every layer's packed cache with 32767 tokens through the library's own
 bulk encode. One timed step = for each of the 48 layers: encode and append
 one new token (K and V) and run decode attention over the full 32768-token
-packed cache.
+packed cache. The 96 launches of a step are captured once as a HIP graph and
+the graph is replayed per step (--eager launches them one by one); every
+replay's outputs are compared with an eager step's, bit for bit.
 
 Printed JSON line: value = packed K/V bytes read by the decode per step /
 step time (GB/s); roofline = the decode launch (split + merge kernels,
@@ -38,6 +40,7 @@ def parse():
     p.add_argument("--workload", default="moe30b_gqa_t32768")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--eager", action="store_true", help="launch the step's kernels one by one instead of a graph")
     return p.parse_args()
 
 
@@ -132,34 +135,60 @@ def main():
     ws = iq.decode_workspace(1, hq, hkv, T, device=dev)
     outs = [torch.empty((1, hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
 
-    n_ev = (args.steps) * L
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-
-    def step(timed_idx=None):
+    def step(st):
         for l in range(L):
-            iq.iq_rotate_quantize_append(caches[l], new_k[l], new_v[l], first_slot=T - 1, stream=stream)
-            if timed_idx is not None:
-                starts[timed_idx * L + l].record(stream)
-            iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws,
-                                   stream=stream)
-            if timed_idx is not None:
-                ends[timed_idx * L + l].record(stream)
+            iq.iq_rotate_quantize_append(caches[l], new_k[l], new_v[l], first_slot=T - 1, stream=st)
+            iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=st)
 
+    # eager reference of one step
+    step(stream)
+    torch.cuda.synchronize()
+    eager = torch.stack(outs).clone()
+
+    # the whole step (48 x (append + decode)) is one HIP graph, replayed per step
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                step(cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+    run = (lambda: graph.replay()) if graph is not None else (lambda: step(stream))
+
+    replays_match = True
     for _ in range(args.warmup):
-        step()
+        for o in outs:
+            o.fill_(float("nan"))
+        run()
+        torch.cuda.synchronize()
+        replays_match &= bool(torch.equal(torch.stack(outs), eager))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    replays_match &= bool(torch.equal(torch.stack(outs), eager))
     ms_per_step = el * 1e3 / args.steps
-    dec_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
     bytes_per_launch = hkv * T * 2 * ROW_BYTES
-    achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
     bytes_per_step = L * bytes_per_launch
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    # decode launches (split + merge kernels) bracketed by HIP events on their stream
+    n_ev = max(1, args.steps // 4) * L
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for i in range(n_ev):
+        l = i % L
+        starts[i].record(stream)
+        iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    dec_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+    achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
 
     res = {
         "metric": "packed-KV decode attention GB/s & % HBM peak; quantize-append tokens/s",
@@ -176,7 +205,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "context": T, "layers": L, "num_q_heads": hq, "num_kv_heads": hkv,
                    "head_dim": 128, "batch": 1, "kv_input": w.dtype,
-                   "step": "per layer: append 1 token (K,V) + decode over the packed cache"},
+                   "step": "per layer: append 1 token (K,V) + decode over the packed cache",
+                   "launch": "eager" if graph is None else "hip_graph"},
+        "graph_replays_match_eager": replays_match,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_launch_us": {"mean": round(float(dec_us.mean()), 3), "median": round(float(np.median(dec_us)), 3),
                              "min": round(float(dec_us.min()), 3)},

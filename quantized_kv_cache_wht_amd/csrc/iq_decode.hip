@@ -273,7 +273,6 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   __shared__ __align__(16) uint2 lut[kLutEntries * kLutCopies];
   __shared__ __align__(16) float qs[G][kDim];
   __shared__ float qmax[G];
-  __shared__ __align__(16) float sm[kBlocks * 16];
   constexpr int kRows = kSplitN ? 2 * G : G;   // accumulator rows kept per wave (hi and lo halves)
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ __align__(16) float wo[kWaves][kRows][kDim];
@@ -295,27 +294,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   int b = b_begin + wave;
   if (b < b_end) load_block(a, slot_base, b * kBlk, n, q, buf0);
   if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
-  // rotation parameters (threads 0..31, one SO(4) block each) and this work-group's
-  // queries (threads 0..4G-1, 32 dims each) are fetched before the first barrier too
-  float rq[8];
-  if (tid < kBlocks) {
-    const float4* rp = reinterpret_cast<const float4*>(a.rot + (static_cast<size_t>(h) * kBlocks + tid) * 8);
-    const float4 r0 = rp[0], r1 = rp[1];
-    rq[0] = r0.x; rq[1] = r0.y; rq[2] = r0.z; rq[3] = r0.w;
-    rq[4] = r1.x; rq[5] = r1.y; rq[6] = r1.z; rq[7] = r1.w;
-  }
-  float xq[kPerLane];
-  if (tid < 4 * G) {
+  // this work-group's queries and rotation parameters, 16 lanes per query
+  // head (8 dims and 2 SO(4) blocks each), are fetched before the prologue too
+  const int pg = tid >> 4, pl = tid & 15;
+  float xq[8], rp[16];
+  if (tid < 16 * G) {
     const float4* src = reinterpret_cast<const float4*>(
-        a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + (tid >> 2)) * kDim + (tid & 3) * kPerLane);
-#pragma unroll
-    for (int i = 0; i < kPerLane / 4; ++i) {
-      const float4 v = src[i];
-      xq[4 * i] = v.x; xq[4 * i + 1] = v.y; xq[4 * i + 2] = v.z; xq[4 * i + 3] = v.w;
-    }
+        a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + pg) * kDim + 8 * pl);
+    const float4 v0 = src[0], v1 = src[1];
+    xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w; xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
+    load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, pl, rp);
   }
 
-  // ---- prologue: code-pair table, SO(4) matrices, rotated queries ----
+  // ---- prologue: code-pair table, rotated queries ----
   {
     // thread t fills copies 4(t%4) .. 4(t%4)+3 of pair t/4
     const uint32_t p = static_cast<uint32_t>(tid) >> 2, ca = p & 7u, cb = p >> 3;
@@ -324,27 +315,23 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
 #pragma unroll
     for (int k = 0; k < 4; ++k) lut[p * kLutCopies + (tid & 3) * 4 + k] = e;
   }
-  if (tid < kBlocks) {
-    float m[16];
-    so4_matrix(rq, 0.08838834764831845f, m);   // 1/sqrt(128)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm[tid * 16 + i] = m[i];
-  }
-  __syncthreads();
-  if (tid < 4 * G) {
-    const int g = tid >> 2, part = tid & 3;
-    float (&x)[kPerLane] = xq;
-    wht128_quad(x, part);
-    so4_apply_lane<false>(x, sm, part);
+  if (tid < 16 * G) {
+    // q' = B Hn q (the 1/sqrt(128) rides in the block matrices)
+    float m[32];
+    so4_matrices_row(rp, m);
+    wht128_row(xq, pl);
+    so4_apply_row<false>(xq, m);
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      qs[g][part * kPerLane + i] = x[i];
-      mx = fmaxf(mx, fabsf(x[i]));
+    for (int i = 0; i < 8; ++i) {
+      qs[pg][8 * pl + i] = xq[i];
+      mx = fmaxf(mx, fabsf(xq[i]));
     }
-    mx = fmaxf(mx, dpp_f32<kQuadXor1>(mx));
-    mx = fmaxf(mx, dpp_f32<kQuadXor2>(mx));
-    if (part == 0) qmax[g] = mx;
+    mx = fmaxf(mx, row_xor<8>(mx));
+    mx = fmaxf(mx, row_xor<4>(mx));
+    mx = fmaxf(mx, row_xor<2>(mx));
+    mx = fmaxf(mx, row_xor<1>(mx));
+    if (pl == 0) qmax[pg] = mx;
   }
   __syncthreads();
 
@@ -449,15 +436,28 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   }
 }
 
+// Sum (or max) over the 32 lanes of a half-wave: four DPP rotations within
+// each row of 16, then one swizzle across the two rows.
+template <bool kMax>
+__device__ __forceinline__ float half_wave_reduce(float x) {
+  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  x = op(x, dpp_f32<0x128>(x));   // row_ror:8
+  x = op(x, dpp_f32<0x124>(x));   // row_ror:4
+  x = op(x, dpp_f32<0x122>(x));   // row_ror:2
+  x = op(x, dpp_f32<0x121>(x));   // row_ror:1
+  return op(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));  // lane ^ 16
+}
+
 // One work-group per (seq, query head): merges the live splits' records
 //   M = max m_k, l = sum 2^(m_k - M) l_k, o' = sum 2^(m_k - M) o'_k,
-// then out = Hn B^T (o' / l), the single inverse rotation. Lane t reads dims
-// 4 (t % 32) .. +3 of records t / 32, t / 32 + 32, ...; the 32 rows are then
-// combined in LDS. An empty sequence gives 0, an invalid one NaN.
+// then out = Hn B^T (o' / l), the single inverse rotation. Lane t first reads
+// dims 4 (t % 32) .. +3 of records t / 32, t / 32 + 32, ... (coalesced), keeps
+// a running merge of them, and parks the result in LDS; the 32 rows are then
+// combined with one row per lane of a half-wave. An empty sequence gives 0,
+// an invalid one NaN.
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float rm[kMergeRows], rl[kMergeRows];
   __shared__ __align__(16) float ro[kMergeRows][kDim];
-  __shared__ __align__(16) float sm[kBlocks * 16];
   __shared__ __align__(16) float fin[kDim];
   const int hq = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
@@ -467,13 +467,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int nblk = ok ? n_blocks(start, len) : 0;
   const int live = live_splits(nblk, a.blocks_per_split, a.n_splits);
 
-  float rq[8];
-  if (tid < kBlocks) {
-    const float4* rp = reinterpret_cast<const float4*>(a.rot + (static_cast<size_t>(h) * kBlocks + tid) * 8);
-    const float4 r0 = rp[0], r1 = rp[1];
-    rq[0] = r0.x; rq[1] = r0.y; rq[2] = r0.z; rq[3] = r0.w;
-    rq[4] = r1.x; rq[5] = r1.y; rq[6] = r1.z; rq[7] = r1.w;
-  }
+  float rp[16];
+  if (tid < 16) load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, tid, rp);
   const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.n_splits * kRec;
   float mx = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -493,12 +488,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i) cm = fmaxf(cm, mv[i]);
     if (cm == -INFINITY) continue;   // only records without tokens so far
-    const float f = exp2f(mx - cm);   // mx = -inf gives 0
+    const float f = fast_exp2(mx - cm);   // mx = -inf gives 0
     l *= f;
     o.x *= f; o.y *= f; o.z *= f; o.w *= f;
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i) {
-      const float w = mv[i] == -INFINITY ? 0.f : exp2f(mv[i] - cm);
+      const float w = fast_exp2(mv[i] - cm);   // -inf gives 0
       l += w * lv[i];
       o.x += w * ov[i].x; o.y += w * ov[i].y; o.z += w * ov[i].z; o.w += w * ov[i].w;
     }
@@ -509,40 +504,36 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     rl[row] = l;
   }
   reinterpret_cast<float4*>(ro[row])[d4] = o;
-  if (tid < kBlocks) {
-    float m[16];
-    so4_matrix(rq, 0.08838834764831845f, m);   // 1/sqrt(128)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm[tid * 16 + i] = m[i];
-  }
+  float m[32];
+  if (tid < 16) so4_matrices_row(rp, m);
   __syncthreads();
-  if (tid < kDim) {
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int r = 0; r < kMergeRows; ++r) M = fmaxf(M, rm[r]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int r = 0; r < kMergeRows; ++r) {
-        const float w = exp2f(rm[r] - M);
-        L += w * rl[r];
-        O += w * ro[r][tid];
-      }
+  {
+    // half-wave: lane = row (0..31), dims 4 c .. 4 c + 3 with c = tid / 32
+    const int r = tid & (kMergeRows - 1), c = tid / kMergeRows;
+    const float m_r = rm[r];
+    const float M = half_wave_reduce<true>(m_r);
+    const float w = M == -INFINITY ? 0.f : fast_exp2(m_r - M);
+    const float4 v = reinterpret_cast<const float4*>(ro[r])[c];
+    const float L = half_wave_reduce<false>(w * rl[r]);
+    const float o0 = half_wave_reduce<false>(w * v.x);
+    const float o1 = half_wave_reduce<false>(w * v.y);
+    const float o2 = half_wave_reduce<false>(w * v.z);
+    const float o3 = half_wave_reduce<false>(w * v.w);
+    if (r == 0) {
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      reinterpret_cast<float4*>(fin)[c] = make_float4(o0 * inv, o1 * inv, o2 * inv, o3 * inv);
     }
-    fin[tid] = L > 0.f ? O / L : 0.f;
   }
   __syncthreads();
-  if (tid < 4) {
-    float x[kPerLane];
+  if (tid < 16) {
+    float x[8];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) x[i] = fin[tid * kPerLane + i];
-    so4_apply_lane<true>(x, sm, tid);
-    wht128_quad(x, tid);
-    float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + tid * kPerLane);
-#pragma unroll
-    for (int i = 0; i < kPerLane / 4; ++i)
-      dst[i] = ok ? make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3])
-                  : make_float4(NAN, NAN, NAN, NAN);
+    for (int i = 0; i < 8; ++i) x[i] = fin[8 * tid + i];
+    so4_apply_row<true>(x, m);
+    wht128_row(x, tid);
+    float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + 8 * tid);
+    dst[0] = ok ? make_float4(x[0], x[1], x[2], x[3]) : make_float4(NAN, NAN, NAN, NAN);
+    dst[1] = ok ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(NAN, NAN, NAN, NAN);
   }
 }
 

@@ -148,6 +148,112 @@ __device__ __forceinline__ void so4_apply_lane(float (&x)[kPerLane], const float
   }
 }
 
+// ------------------------------------------------- 16-lane form ----
+// A 128-vector spread over one DPP row (16 consecutive lanes), 8 dims per
+// lane: lane p holds dims 8p .. 8p+7, i.e. SO(4) blocks 2p and 2p+1. Four
+// times more lanes per vector than the quad form, so a single vector on the
+// critical path (a query, an output) takes a quarter of the steps.
+constexpr int kRowHalfMirror = 0x141;   // lane i of each 8 reads lane 7 - i
+constexpr int kQuadXor3 = 0x1B;         // [3,2,1,0]
+constexpr int kRowRor8 = 0x128;         // lane i reads lane (i + 8) mod 16
+
+// Value of lane (p ^ M) of this lane's row.
+template <int M>
+__device__ __forceinline__ float row_xor(float x) {
+  if constexpr (M == 1) return dpp_f32<kQuadXor1>(x);
+  if constexpr (M == 2) return dpp_f32<kQuadXor2>(x);
+  if constexpr (M == 4) return dpp_f32<kQuadXor3>(dpp_f32<kRowHalfMirror>(x));   // i ^ 7 ^ 3
+  if constexpr (M == 8) return dpp_f32<kRowRor8>(x);
+  return x;
+}
+
+template <int M>
+__device__ __forceinline__ void wht_row_stage(float (&x)[8], int p) {
+  const float s = (p & M) ? -1.0f : 1.0f;   // the lane with the bit set keeps (partner - self)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], s, row_xor<M>(x[i]));
+}
+
+// Unnormalised Sylvester Hadamard transform in the 16-lane form.
+__device__ __forceinline__ void wht128_row(float (&x)[8], int p) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+  wht_row_stage<1>(x, p);
+  wht_row_stage<2>(x, p);
+  wht_row_stage<4>(x, p);
+  wht_row_stage<8>(x, p);
+}
+
+// fp64 value of lane (p ^ M) of this lane's row.
+template <int M>
+__device__ __forceinline__ double row_xor64(double x) {
+  if constexpr (M == 1) return dpp_f64<kQuadXor1>(x);
+  if constexpr (M == 2) return dpp_f64<kQuadXor2>(x);
+  if constexpr (M == 4) return dpp_f64<kQuadXor3>(dpp_f64<kRowHalfMirror>(x));
+  if constexpr (M == 8) return dpp_f64<kRowRor8>(x);
+  return x;
+}
+
+// n = fl32(sqrt(sum y^2)) of the row's vector, the sum in double; the xor
+// butterfly gives every lane of the row the identical value.
+__device__ __forceinline__ float row_norm(const float (&y)[8]) {
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double d = static_cast<double>(y[i]);
+    s = __builtin_fma(d, d, s);
+  }
+  s += row_xor64<8>(s);
+  s += row_xor64<4>(s);
+  s += row_xor64<2>(s);
+  s += row_xor64<1>(s);
+  return __double2float_rn(sqrt(s));
+}
+
+// Row-major matrices of the lane's two SO(4) blocks from their 16 stored
+// parameters, scaled by 1/sqrt(128).
+__device__ __forceinline__ void so4_matrices_row(const float (&p16)[16], float (&m)[32]) {
+  so4_matrix(p16, 0.08838834764831845f, m);
+  so4_matrix(p16 + 8, 0.08838834764831845f, m + 16);
+}
+
+// y_b = M_b y_b (or M_b^T y_b) for the lane's two blocks.
+template <bool kTranspose>
+__device__ __forceinline__ void so4_apply_row(float (&x)[8], const float (&m)[32]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float* mb = m + 16 * b;
+    const float v0 = x[4 * b], v1 = x[4 * b + 1], v2 = x[4 * b + 2], v3 = x[4 * b + 3];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a0 = kTranspose ? mb[0 * 4 + r] : mb[r * 4 + 0];
+      const float a1 = kTranspose ? mb[1 * 4 + r] : mb[r * 4 + 1];
+      const float a2 = kTranspose ? mb[2 * 4 + r] : mb[r * 4 + 2];
+      const float a3 = kTranspose ? mb[3 * 4 + r] : mb[r * 4 + 3];
+      x[4 * b + r] = __builtin_fmaf(a3, v3, __builtin_fmaf(a2, v2, __builtin_fmaf(a1, v1, a0 * v0)));
+    }
+  }
+}
+
+// The 16 stored parameters of the lane's two blocks (four float4 loads).
+__device__ __forceinline__ void load_row_params(const float* rot_head, int p, float (&p16)[16]) {
+  const float4* r = reinterpret_cast<const float4*>(rot_head + 16 * p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 t = r[i];
+    p16[4 * i] = t.x; p16[4 * i + 1] = t.y; p16[4 * i + 2] = t.z; p16[4 * i + 3] = t.w;
+  }
+}
+
 // --------------------------------------------------- norm and codes ----
 // n = fl32(sqrt(sum y^2)), sum in double over the quad. Every lane of the quad
 // gets the same value.

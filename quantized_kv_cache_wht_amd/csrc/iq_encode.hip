@@ -19,6 +19,7 @@ namespace iq {
 
 constexpr int kEncThreads = 256;
 constexpr int kVecPerBlock = kEncThreads / 4;
+constexpr int kRowAppendMax = 64;   // appends of up to this many tokens use the 16-lane kernel
 
 template <typename T>
 __device__ __forceinline__ void load_vec(const T* __restrict__ src, bool ok, float (&x)[kPerLane]);
@@ -114,16 +115,28 @@ __device__ __forceinline__ void tile_quad_bits(const uint32_t (*rows)[12], int r
   }
 }
 
+// Bits of a V tile's dim-quad that belong to the slots NOT set in `mask`.
+__device__ __forceinline__ void tile_keep_bits(uint32_t mask, uint32_t (&keep)[3]) {
+  keep[0] = keep[1] = keep[2] = 0u;
+#pragma unroll
+  for (int r = 0; r < kTile; ++r) {
+    if (!(mask & (1u << r))) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int pos = 24 * d + 3 * r;
+        keep[pos >> 5] |= 7u << (pos & 31);
+        if ((pos & 31) > 29) keep[(pos >> 5) + 1] |= 7u >> (32 - (pos & 31));
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   __shared__ __align__(16) float sm[kBlocks * 16];
   __shared__ __align__(16) uint32_t rows[kVecPerBlock][12];
-  __shared__ int row_ok[kVecPerBlock];
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
-  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
-  __syncthreads();
-
   const T* __restrict__ src = static_cast<const T*>(is_v ? a.v : a.k);
   uint8_t* __restrict__ codes = is_v ? a.v_codes : a.k_codes;
   float* __restrict__ norms = is_v ? a.v_norms : a.k_norms;
@@ -133,12 +146,52 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   const int w0 = scatter ? 0 : (a.first_slot & ~(kTile - 1));   // first window start (slot or token)
   const int span = scatter ? a.n_tokens : (a.first_slot - w0 + a.n_tokens);
   const int n_windows = (span + kVecPerBlock - 1) / kVecPerBlock;
+  // V tile (tt) and dim quad (jq) this thread writes in the contiguous case
+  const int tt = threadIdx.x >> 5, jq = threadIdx.x & 31;
 
-  for (int win = blockIdx.x; win < n_windows; win += gridDim.x) {
-    const int tok = scatter ? win * kVecPerBlock + vec : w0 + win * kVecPerBlock + vec - a.first_slot;
+  // The first window's inputs (and, for V, the tile words a partial tile
+  // keeps) are requested before the rotation matrices are built, so the
+  // three memory round trips of a short append overlap.
+  int win = blockIdx.x;
+  auto token_of = [&](int w) { return scatter ? w * kVecPerBlock + vec : w0 + w * kVecPerBlock + vec - a.first_slot; };
+  auto tile_mask = [&](int w) {   // slots of tile tt that this call writes
+    const int s0 = w0 + w * kVecPerBlock + tt * kTile;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      const int sl = s0 + r;
+      m |= (sl >= a.first_slot && sl - a.first_slot < a.n_tokens && sl < a.capacity) ? (1u << r) : 0u;
+    }
+    return m;
+  };
+  auto tile_dst = [&](int w) {
+    return reinterpret_cast<uint32_t*>(
+        codes + ((static_cast<size_t>(h) * a.capacity + w0 + w * kVecPerBlock + tt * kTile) / kTile) * kTileBytes +
+        12 * jq);
+  };
+  float x[kPerLane];
+  uint32_t old[3] = {0u, 0u, 0u};
+  if (win < n_windows) {
+    const int tok = token_of(win);
     const bool ok = tok >= 0 && tok < a.n_tokens;
-    float x[kPerLane];
     load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
+    if (is_v && !scatter) {
+      const uint32_t m = tile_mask(win);
+      if (m != 0u && m != 0xffu) {
+        const uint32_t* d = tile_dst(win);
+        old[0] = d[0]; old[1] = d[1]; old[2] = d[2];
+      }
+    }
+  }
+  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  __syncthreads();
+
+  for (; win < n_windows; win += gridDim.x) {
+    const int tok = token_of(win);
+    const bool ok = tok >= 0 && tok < a.n_tokens;
+    if (win != static_cast<int>(blockIdx.x)) {
+      load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
+    }
     wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
     uint32_t w[3];
@@ -180,41 +233,137 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     rows[vec][3 * part] = w[0];
     rows[vec][3 * part + 1] = w[1];
     rows[vec][3 * part + 2] = w[2];
-    if (part == 0) row_ok[vec] = in_cap ? 1 : 0;
     __syncthreads();
-    {
-      const int tt = threadIdx.x >> 5, jq = threadIdx.x & 31;     // tile of the window, dims 4jq..4jq+3
-      uint32_t mask = 0u;
-#pragma unroll
-      for (int r = 0; r < kTile; ++r) mask |= row_ok[tt * kTile + r] ? (1u << r) : 0u;
-      if (mask != 0u) {
-        uint32_t bits[3];
-        tile_quad_bits(rows, tt * kTile, jq, bits);
-        const int first_slot_of_tile = w0 + win * kVecPerBlock + tt * kTile;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(
-            codes + ((static_cast<size_t>(h) * a.capacity + first_slot_of_tile) / kTile) * kTileBytes + 12 * jq);
-        if (mask != 0xffu) {
-          uint32_t keep[3] = {0u, 0u, 0u};
-#pragma unroll
-          for (int r = 0; r < kTile; ++r) {
-            if (!(mask & (1u << r))) {
-#pragma unroll
-              for (int d = 0; d < 4; ++d) {
-                const int pos = 24 * d + 3 * r;
-                keep[pos >> 5] |= 7u << (pos & 31);
-                if ((pos & 31) > 29) keep[(pos >> 5) + 1] |= 7u >> (32 - (pos & 31));
-              }
-            }
-          }
-#pragma unroll
-          for (int k = 0; k < 3; ++k) bits[k] = (dst[k] & keep[k]) | (bits[k] & ~keep[k]);
+    const uint32_t mask = tile_mask(win);
+    if (mask != 0u) {
+      uint32_t bits[3];
+      tile_quad_bits(rows, tt * kTile, jq, bits);
+      uint32_t* dst = tile_dst(win);
+      if (mask != 0xffu) {
+        if (win != static_cast<int>(blockIdx.x)) {
+          old[0] = dst[0]; old[1] = dst[1]; old[2] = dst[2];
         }
-        dst[0] = bits[0];
-        dst[1] = bits[1];
-        dst[2] = bits[2];
+        uint32_t keep[3];
+        tile_keep_bits(mask, keep);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) bits[k] = (old[k] & keep[k]) | (bits[k] & ~keep[k]);
       }
+      dst[0] = bits[0];
+      dst[1] = bits[1];
+      dst[2] = bits[2];
     }
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Short appends: one vector per DPP row (16 lanes x 8 dims), so encoding a
+// single token is a short dependent chain rather than the bulk kernel's
+// window pipeline. grid = (ceil(n_tokens / 4), num_kv_heads, 2 [K, V]),
+// 64 threads = 4 vectors. A V code lands in its tile through one atomic XOR
+// per dword that flips only this slot's bits, so tokens sharing a tile (in
+// this work-group or another) never overwrite each other.
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* __restrict__ src, bool ok, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* __restrict__ src, bool ok, float (&x)[8]) {
+  const float4 a = ok ? reinterpret_cast<const float4*>(src)[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 b = ok ? reinterpret_cast<const float4*>(src)[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<_Float16>(const _Float16* __restrict__ src, bool ok, float (&x)[8]) {
+  typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+  half8 v;
+  if (ok) {
+    v = reinterpret_cast<const half8*>(src)[0];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = static_cast<float>(v[j]);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, false));
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int p = threadIdx.x & 15;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 4);
+  const bool ok = tok < a.n_tokens;
+  const int slot = ok ? (a.slots != nullptr ? a.slots[tok] : a.first_slot + tok) : -1;
+  const bool in_cap = slot >= 0 && slot < a.capacity;
+  const size_t row = static_cast<size_t>(h) * a.capacity + (in_cap ? slot : 0);
+
+  // every load is issued before any arithmetic
+  float x[8];
+  load8<T>(static_cast<const T*>(is_v ? a.v : a.k) + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim +
+               8 * p,
+           ok, x);
+  float rp[16];
+  load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, p, rp);
+  // V: this lane's dims 8p .. 8p+7 are the tile's dwords 6p .. 6p+5
+  uint32_t* tile = reinterpret_cast<uint32_t*>(a.v_codes + (row / kTile) * kTileBytes) + 6 * p;
+  uint32_t old[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+  if (is_v && in_cap) {
+    const uint2* t2 = reinterpret_cast<const uint2*>(tile);
+    const uint2 o0 = t2[0], o1 = t2[1], o2 = t2[2];
+    old[0] = o0.x; old[1] = o0.y; old[2] = o1.x; old[3] = o1.y; old[4] = o2.x; old[5] = o2.y;
+  }
+
+  float m[32];
+  so4_matrices_row(rp, m);
+  wht128_row(x, p);
+  so4_apply_row<false>(x, m);
+  const float n = row_norm(x);
+  const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = code_of(x[i], t4, t5, t6);
+  if (!in_cap) return;
+  if (p == 0) (is_v ? a.v_norms : a.k_norms)[row] = n;
+
+  if (!is_v) {
+    // row layout: dim j at bits 3j; lanes 4k .. 4k+3 own 96 bits = 3 dwords
+    uint32_t b24 = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b24 |= c[i] << (3 * i);
+    const uint32_t b1 = dpp_u32<kQuadXor1>(b24), b2 = dpp_u32<kQuadXor2>(b24), b3 = dpp_u32<kQuadXor3>(b24);
+    if ((p & 3) == 0) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + row * kRowBytes) + 3 * (p >> 2);
+      dst[0] = b24 | (b1 << 24);
+      dst[1] = (b1 >> 8) | (b2 << 16);
+      dst[2] = (b2 >> 16) | (b3 << 8);
+    }
+    return;
+  }
+  // tile layout: dim j of slot r at bit 24 j + 3 r, i.e. a 24-bit field per dim
+  const int r3 = 3 * (slot & (kTile - 1));
+  uint32_t nb[6] = {0u, 0u, 0u, 0u, 0u, 0u}, mk[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t f = c[i] << r3, fm = 7u << r3;   // 24-bit fields
+    const int pos = 24 * i, wd = pos >> 5, off = pos & 31;   // compile-time after unrolling
+    nb[wd] |= f << off;
+    mk[wd] |= fm << off;
+    if (off > 8) {
+      nb[wd + 1] |= f >> (32 - off);
+      mk[wd + 1] |= fm >> (32 - off);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const uint32_t delta = (old[k] & mk[k]) ^ nb[k];
+    if (delta != 0u) atomicXor(tile + k, delta);
   }
 }
 
@@ -335,6 +484,14 @@ static int enc_grid_x(int64_t n_vectors_per_y, int64_t y_blocks) {
 }
 
 hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s) {
+  if (a.n_tokens <= kRowAppendMax) {
+    dim3 grid((a.n_tokens + 3) / 4, a.num_kv_heads, 2);
+    if (f16)
+      hipLaunchKernelGGL(append_row_kernel<_Float16>, grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL(append_row_kernel<float>, grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid(enc_grid_x(a.n_tokens, 2LL * a.num_kv_heads), a.num_kv_heads, 2);
   if (f16)
     hipLaunchKernelGGL(append_kernel<_Float16>, grid, dim3(kEncThreads), 0, s, a);

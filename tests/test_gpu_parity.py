@@ -112,7 +112,10 @@ def _encode_ref(x, rot):
 
 
 @pytest.mark.parametrize("wname,n_tok,first", [("single_head_t512", 512, 0), ("dense8b_gqa_t8192", 1000, 37),
-                                               ("moe30b_gqa_t32768", 333, 5)])
+                                               ("moe30b_gqa_t32768", 333, 5),
+                                               # short appends (the 16-lane kernel)
+                                               ("single_head_t512", 1, 511), ("dense8b_gqa_t8192", 5, 35),
+                                               ("moe30b_gqa_t32768", 64, 3), ("dense8b_gqa_t8192", 65, 8)])
 def test_append_matches_oracle(wname, n_tok, first):
     w = iqinputs.WORKLOADS[wname]
     rot = iqinputs.rotation_params(w.seed, 0, w.num_kv_heads)
@@ -137,26 +140,28 @@ def test_append_matches_oracle(wname, n_tok, first):
 
 
 def test_append_v_tiles_keep_neighbours():
-    """Appends that start and end inside V tiles leave the other slots of those tiles intact."""
+    """Appends that start and end inside V tiles leave the other slots of those tiles intact, and
+    the short-append and bulk kernels encode identically."""
     hkv = 2
     rot = iqinputs.rotation_params(21, 0, hkv)
-    x = iqinputs.kv(21, 0, "v", 64, hkv, "student_t6", "f16")
-    cache = iq.PackedKVCache.allocate(hkv, 64, _t(rot))
-    # three calls covering slots 0..63: [0, 13), [13, 14), [14, 64)
-    for a0, a1 in [(0, 13), (13, 14), (14, 64)]:
+    x = iqinputs.kv(21, 0, "v", 224, hkv, "student_t6", "f16")
+    cache = iq.PackedKVCache.allocate(hkv, 224, _t(rot))
+    # calls covering slots 0..223: short ones [0, 13), [13, 14), [150, 151), [151, 224), a bulk one [14, 150)
+    for a0, a1 in [(0, 13), (13, 14), (14, 150), (150, 151), (151, 224)]:
         iq.iq_rotate_quantize_append(cache, _t(x[a0:a1]), _t(x[a0:a1]), first_slot=a0)
-    one = iq.PackedKVCache.allocate(hkv, 64, _t(rot))
+    one = iq.PackedKVCache.allocate(hkv, 224, _t(rot))
     iq.iq_rotate_quantize_append(one, _t(x), _t(x), first_slot=0)
     assert torch.equal(cache.v_codes, one.v_codes) and torch.equal(cache.k_codes, one.k_codes)
     assert torch.equal(cache.v_norms, one.v_norms)
 
 
-def test_append_with_slot_list_and_out_of_range_slots():
+@pytest.mark.parametrize("n", [70, 40])     # bulk kernel, short-append kernel
+def test_append_with_slot_list_and_out_of_range_slots(n):
     hkv = 2
     rot = iqinputs.rotation_params(9, 0, hkv)
-    k = iqinputs.kv(9, 0, "k", 70, hkv, "student_t6", "f16")
-    v = iqinputs.kv(9, 0, "v", 70, hkv, "student_t6", "f16")
-    slots = np.random.default_rng(1).permutation(100)[:70].astype(np.int32)
+    k = iqinputs.kv(9, 0, "k", n, hkv, "student_t6", "f16")
+    v = iqinputs.kv(9, 0, "v", n, hkv, "student_t6", "f16")
+    slots = np.random.default_rng(1).permutation(100)[:n].astype(np.int32)
     slots[3] = -1
     slots[10] = 100                       # == capacity: skipped
     cache = iq.PackedKVCache.allocate(hkv, 100, _t(rot))
