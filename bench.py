@@ -19,6 +19,7 @@ workload. The quantize-append rate is measured on the set-up's bulk encode.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROW_BYTES = 48 + 4          # packed codes + fp32 norm, one (token, KV head, K or V)
+SPIN_CYCLES_PER_LAUNCH = 200_000   # ~80 us of GPU clock per queued launch: more than the host needs
 
 
 def parse():
@@ -41,7 +43,39 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch the step's kernels one by one instead of a graph")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="finish with 3 device-to-device copies of this many MiB (reference for HBM counters)")
     return p.parse_args()
+
+
+def decode_source_digest() -> str:
+    """sha256 over the sources of the decode kernels (the traffic figures belong to one version)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_wht_amd", "csrc")
+    for name in ("iq_decode.hip", "iq_device.h", "iq_launch.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, if it was taken on
+    the current decode sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    if fields.get("decode_source_sha256") != decode_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, budget_s: float):
@@ -177,10 +211,13 @@ def main():
     bytes_per_step = L * bytes_per_launch
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # decode launches (split + merge kernels) bracketed by HIP events on their stream
+    # decode launches (split + merge kernels) bracketed by HIP events on their
+    # stream. A spin kernel queued first keeps the GPU busy while the host
+    # enqueues every launch, so the events time the GPU, not the host's calls.
     n_ev = max(1, args.steps // 4) * L
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * n_ev)
     for i in range(n_ev):
         l = i % L
         starts[i].record(stream)
@@ -189,6 +226,16 @@ def main():
     torch.cuda.synchronize()
     dec_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
     achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
+    traffic = measured_traffic(w.name)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     res = {
         "metric": "packed-KV decode attention GB/s & % HBM peak; quantize-append tokens/s",
@@ -214,7 +261,8 @@ def main():
         "quantize_append_token_layers_per_s": round(append_tok_layers_per_s, 1),
         "quantize_append_bulk_ms": round(enc_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic)},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -48,6 +48,7 @@ union H8 {
   half8 h;
   uint32_t u[4];
   uint2 u2[2];
+  uint4 u4;
 };
 
 constexpr int kDecThreads = 256;
@@ -56,7 +57,11 @@ constexpr int kBlk = 32;             // cache slots per wave iteration
 constexpr int kRec = 132;            // floats per partial record: m, l, 2 pad, o[128]
 constexpr int kTargetBlocks = 512;   // split-K occupancy target (work-groups): 2 per CU
 constexpr int kMinBlocksPerSplit = 4;
-constexpr int kMaxBlocksPerSplit = 64;   // beyond this, more (shorter) splits balance ragged batches
+// Split length cap: a single sequence is cut into about one resident round of
+// work-groups; several sequences (possibly of different lengths) into
+// shorter splits, so the long ones do not leave a tail of lone work-groups.
+constexpr int kMaxBlocksPerSplitOne = 64;
+constexpr int kMaxBlocksPerSplitMany = 32;
 constexpr int kMaxSplits = 2048;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeLanes = kDim / 4;                    // lanes per record, 4 dims each
@@ -150,7 +155,8 @@ struct WaveState {
 
 template <int G>
 struct Consts {
-  H8 qb[8], qb_lo[8];   // query operand per k-step (qb_lo only when G = 16)
+  const uint4* qop;      // this lane's query operand of k-step kk at qop[64 kk] (LDS)
+  const uint4* qop_lo;   // G = 16: the lo halves, same layout
   float fscale;
   bool lo_lane;
   uint32_t lane_off;
@@ -168,11 +174,14 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int slot0, i
   {                                                                            \
     const half8 ka = code_operand<12 * KAPPA>(cur.kw0, c.lut, c.lane_off);     \
     const half8 kb = code_operand<12 * KAPPA>(cur.kw1, c.lut, c.lane_off);     \
-    d0 = mfma16(ka, c.qb[KAPPA].h, d0);                                        \
-    d1 = mfma16(kb, c.qb[KAPPA].h, d1);                                        \
+    H8 qv;                                                                     \
+    qv.u4 = c.qop[64 * KAPPA];                                                 \
+    d0 = mfma16(ka, qv.h, d0);                                                 \
+    d1 = mfma16(kb, qv.h, d1);                                                 \
     if (!kSplitN) {                                                            \
-      d0 = mfma16(ka, c.qb_lo[KAPPA].h, d0);                                   \
-      d1 = mfma16(kb, c.qb_lo[KAPPA].h, d1);                                   \
+      qv.u4 = c.qop_lo[64 * KAPPA];                                            \
+      d0 = mfma16(ka, qv.h, d0);                                               \
+      d1 = mfma16(kb, qv.h, d1);                                               \
     }                                                                          \
   }
   IQ_SCORE(0) IQ_SCORE(1) IQ_SCORE(2) IQ_SCORE(3) IQ_SCORE(4) IQ_SCORE(5) IQ_SCORE(6) IQ_SCORE(7)
@@ -271,13 +280,19 @@ template <int G>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr bool kSplitN = (G <= 8);   // hi/lo halves share one MFMA (columns / rows g and g+8)
   __shared__ __align__(16) uint2 lut[kLutEntries * kLutCopies];
-  __shared__ __align__(16) float qs[G][kDim];
+  // query operand of k-step kk for lane 16 q + n: dims 32 q + 4 kk + e (e = 0..3) of
+  // head n & 7, each value twice (one fp16 pair); hi halves in columns n < 8, lo
+  // halves in n >= 8 (G = 16: hi in qop, lo in qop_lo, column n = head n)
+  __shared__ __align__(16) uint4 qop[8][64];
+  __shared__ __align__(16) uint4 qop_lo[kSplitN ? 1 : 8][64];
   __shared__ float qmax[G];
   constexpr int kRows = kSplitN ? 2 * G : G;   // accumulator rows kept per wave (hi and lo halves)
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ __align__(16) float wo[kWaves][kRows][kDim];
 
-  const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // work-groups go round-robin to the XCDs in launch order; with the split
+  // index slowest, the live splits (short sequences have few) spread evenly
+  const int h = blockIdx.x, s = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, q = lane >> 4;
   int start, len;
@@ -289,13 +304,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   const int b_end = split == a.n_splits - 1 ? nblk : min(nblk, b_begin + a.blocks_per_split);
   const size_t slot_base = static_cast<size_t>(h) * a.capacity + base;   // cache row of block 0, slot 0
 
-  // this wave's first two blocks are loaded before the prologue
-  BlockData buf0, buf1;
-  int b = b_begin + wave;
-  if (b < b_end) load_block(a, slot_base, b * kBlk, n, q, buf0);
-  if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
-  // this work-group's queries and rotation parameters, 16 lanes per query
-  // head (8 dims and 2 SO(4) blocks each), are fetched before the prologue too
+  // This work-group's queries and rotation parameters (16 lanes per query
+  // head: 8 dims and 2 SO(4) blocks each) are requested first, then the wave's
+  // first two blocks: loads complete in order, so the query rotation below
+  // waits only for its own inputs while the blocks are still in flight.
   const int pg = tid >> 4, pl = tid & 15;
   float xq[8], rp[16];
   if (tid < 16 * G) {
@@ -305,6 +317,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
     xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w; xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
     load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, pl, rp);
   }
+  // The two block loads are unconditional (a wave with fewer blocks re-reads
+  // the split's last one and ignores it): a conditional load would make the
+  // compiler's wait for the query inputs also wait for the blocks.
+  BlockData buf0, buf1;
+  int b = b_begin + wave;
+  load_block(a, slot_base, min(b, b_end - 1) * kBlk, n, q, buf0);
+  load_block(a, slot_base, min(b + kWaves, b_end - 1) * kBlk, n, q, buf1);
 
   // ---- prologue: code-pair table, rotated queries ----
   {
@@ -323,40 +342,46 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
     so4_apply_row<false>(xq, m);
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qs[pg][8 * pl + i] = xq[i];
-      mx = fmaxf(mx, fabsf(xq[i]));
-    }
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(xq[i]));
     mx = fmaxf(mx, row_xor<8>(mx));
     mx = fmaxf(mx, row_xor<4>(mx));
     mx = fmaxf(mx, row_xor<2>(mx));
     mx = fmaxf(mx, row_xor<1>(mx));
     if (pl == 0) qmax[pg] = mx;
+    // operands: q' / max|q'| split into fp16 hi (11 significant bits) and lo
+    const float inv = mx > 0.f ? 1.0f / mx : 0.f;
+    uint32_t* qd = reinterpret_cast<uint32_t*>(&qop[0][0]);
+    uint32_t* qd_lo = reinterpret_cast<uint32_t*>(&qop_lo[0][0]);
+    const int qq = pl >> 2;   // this lane's dims 8 pl .. belong to operand lanes 16 qq + ..
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 2 * (pl & 3) + (i >> 2), e = i & 3;
+      const float x = xq[i] * inv;
+      const float hx = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xffffe000u);
+      if (kSplitN) {
+        qd[(kk * 64 + 16 * qq + pg) * 4 + e] = dup16(hx);
+        qd[(kk * 64 + 16 * qq + pg + 8) * 4 + e] = dup16(x - hx);
+      } else {
+        qd[(kk * 64 + 16 * qq + pg) * 4 + e] = dup16(hx);
+        qd_lo[(kk * 64 + 16 * qq + pg) * 4 + e] = dup16(x - hx);
+      }
+    }
+  }
+  if (kSplitN && G < 8) {
+    // columns of heads >= G stay zero
+    for (int idx = tid; idx < 8 * 64; idx += kDecThreads) {
+      if (((idx & 15) & 7) >= G) qop[idx >> 6][idx & 63] = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   __syncthreads();
 
   // ---- per-lane constants: query operands, score scale ----
   Consts<G> c;
   const int g = kSplitN ? (n & 7) : n;     // head of this lane's score column / P row
-  const bool gvalid = g < G;
-  const float qm = gvalid ? qmax[g] : 0.f;
-  const float inv_qm = qm > 0.f ? 1.0f / qm : 0.f;
+  const float qm = g < G ? qmax[g] : 0.f;
   c.fscale = a.qscale * qm * a.cb.inv_alpha;
-  // k-step kk, slot pair e: dim 32q + 4kk + e (both slots of the pair hold the same value)
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = gvalid ? qs[g][32 * q + 4 * kk + e] * inv_qm : 0.f;
-      const float hx = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xffffe000u);
-      if (kSplitN) {
-        c.qb[kk].u[e] = dup16(n < 8 ? hx : x - hx);
-      } else {
-        c.qb[kk].u[e] = dup16(hx);
-        c.qb_lo[kk].u[e] = dup16(x - hx);
-      }
-    }
-  }
+  c.qop = &qop[0][lane];
+  c.qop_lo = &qop_lo[0][lane];
   c.lo_lane = kSplitN && n >= 8;   // this lane's P row carries the lo half
   c.lane_off = (lane & 15) * 8;
   c.rel_lo = start - base;
@@ -369,15 +394,22 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // two buffers, alternating: a block is computed while the next one is in flight
-  while (b < b_end) {
+  // two buffers, alternating: a block is computed while the next one is in
+  // flight. The first block is taken outside the loop so that it is computed
+  // straight from the registers its loads filled (a loop-carried start would
+  // let the compiler copy both buffers first and so wait for both).
+  if (b < b_end) {
     process_block<G>(buf0, b * kBlk, q, c, st);
-    if (b + 2 * kWaves < b_end) load_block(a, slot_base, (b + 2 * kWaves) * kBlk, n, q, buf0);
     b += kWaves;
-    if (b >= b_end) break;
-    process_block<G>(buf1, b * kBlk, q, c, st);
-    if (b + 2 * kWaves < b_end) load_block(a, slot_base, (b + 2 * kWaves) * kBlk, n, q, buf1);
-    b += kWaves;
+    while (b < b_end) {
+      if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf0);
+      process_block<G>(buf1, b * kBlk, q, c, st);
+      b += kWaves;
+      if (b >= b_end) break;
+      if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
+      process_block<G>(buf0, b * kBlk, q, c, st);
+      b += kWaves;
+    }
   }
 
   // ---- per-wave totals ----
@@ -545,7 +577,8 @@ DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len
   const int64_t want_splits = (kTargetBlocks + pairs - 1) / pairs;
   int64_t bps = (blocks + want_splits - 1) / want_splits;
   if (bps < kMinBlocksPerSplit) bps = kMinBlocksPerSplit;
-  if (bps > kMaxBlocksPerSplit) bps = kMaxBlocksPerSplit;
+  const int64_t cap = n_seqs > 1 ? kMaxBlocksPerSplitMany : kMaxBlocksPerSplitOne;
+  if (bps > cap) bps = cap;
   int64_t ns = (blocks + bps - 1) / bps;
   if (ns > kMaxSplits) {
     bps = (blocks + kMaxSplits - 1) / kMaxSplits;
@@ -562,7 +595,7 @@ size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodeP
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.n_splits, a.num_kv_heads, a.n_seqs);
+  dim3 grid(a.num_kv_heads, a.n_seqs, a.n_splits);
   switch (a.group) {
     case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, st, a); break;
     case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kDecThreads), 0, st, a); break;
