@@ -11,8 +11,10 @@ the graph is replayed per step (--eager launches them one by one); every
 replay's outputs are compared with an eager step's, bit for bit.
 
 Printed JSON line: value = packed K/V bytes read by the decode per step /
-step time (GB/s); roofline = the decode launch (split + merge kernels,
-bracketed by HIP events on the launch stream) against the 8 TB/s HBM peak;
+step time (GB/s); roofline = the decode launch (split + merge kernels; HIP
+events on the launch stream around runs of back-to-back launches) against the
+8 TB/s HBM peak, with the HBM traffic per launch from the committed counter
+summary when it matches the decode sources;
 cpu_baseline = the CPU oracle's decode on a bounded sample of the same
 workload. The quantize-append rate is measured on the set-up's bulk encode.
 """
@@ -211,20 +213,20 @@ def main():
     bytes_per_step = L * bytes_per_launch
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # decode launches (split + merge kernels) bracketed by HIP events on their
-    # stream. A spin kernel queued first keeps the GPU busy while the host
-    # enqueues every launch, so the events time the GPU, not the host's calls.
-    n_ev = max(1, args.steps // 4) * L
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * n_ev)
-    for i in range(n_ev):
-        l = i % L
-        starts[i].record(stream)
-        iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
-        ends[i].record(stream)
+    # decode launches (split + merge kernels) timed with HIP events on their
+    # stream: each pair of events brackets one launch per layer, back to back,
+    # and a spin kernel queued first keeps the GPU busy while the host enqueues
+    # them, so the events time the GPU, not the host's calls.
+    reps = max(2, args.steps // 4)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * reps * L)
+    evs[0].record(stream)
+    for r in range(reps):
+        for l in range(L):
+            iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
+        evs[r + 1].record(stream)
     torch.cuda.synchronize()
-    dec_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+    dec_us = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 / L for r in range(reps)])
     achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
 
