@@ -159,6 +159,31 @@ IQ_API iq_status iq_decode_attention(const iq_cache_view* view, const float* q, 
                               int32_t max_seq_len, float scale, float* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Decode attention over a plain fp16 K/V cache: the FP16-KV baseline, and
+ * with iq_dequantize in front of it the unfused path (news article on
+ * RotaryQuant, section on memory savings versus speed: fused against unfused
+ * kernels, FP16 KV against IsoQuant). Same semantics as iq_decode_attention
+ * with K and V given explicitly:
+ *   k, v          device fp16; element (row t, KV head h, dim j) at
+ *                 k[t * token_stride + h * head_stride + j]. Both strides are
+ *                 in elements and multiples of 8; k and v 16-byte aligned.
+ *                 [capacity][Hkv][128] (iq_dequantize's output): token_stride
+ *                 = 128 Hkv, head_stride = 128. [Hkv][capacity][128]:
+ *                 token_stride = 128, head_stride = 128 capacity.
+ *   capacity      rows per KV head, a multiple of 32; rows [0, capacity) of
+ *                 every head must be readable.
+ *   q, seq_start, seq_len, n_seqs, max_seq_len, scale, out: as for
+ *                 iq_decode_attention, rows indexed like the cache's slots.
+ *   workspace     at least iq_decode_workspace_bytes(n_seqs, num_q_heads,
+ *                 num_kv_heads, max_seq_len) bytes, 16-byte aligned.
+ * Query head g reads KV head g / (num_q_heads / num_kv_heads); group sizes 1,
+ * 2, 4, 8, 16. Empty sequences give 0, invalid ones NaN. */
+IQ_API iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t token_stride, int64_t head_stride,
+                                  int32_t num_kv_heads, int32_t capacity, const float* q, int32_t num_q_heads,
+                                  const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                                  int32_t max_seq_len, float scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

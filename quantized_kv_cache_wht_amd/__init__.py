@@ -72,6 +72,11 @@ _SIGNATURES = {
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p]),
+    "iq_decode_attention_f16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                               ctypes.c_void_p]),
 }
 
 
@@ -252,4 +257,39 @@ def iq_decode_attention(cache: PackedKVCache, q: torch.Tensor, seq_start: torch.
                                      _dev(seq_start, torch.int32, "seq_start"), _dev(seq_len, torch.int32, "seq_len"),
                                      n_seqs, max_seq_len, scale, _dev(out, torch.float32, "out"),
                                      _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return out
+
+
+def iq_decode_attention_f16(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, seq_start: torch.Tensor,
+                            seq_len: torch.Tensor, max_seq_len: int, token_major: bool = True,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention over a plain fp16 cache.
+
+    k, v float16, contiguous: [capacity][Hkv][128] when ``token_major`` (the
+    layout iq_dequantize writes), else [Hkv][capacity][128].
+    """
+    if k.shape != v.shape or k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError("k and v must be matching [.., .., 128] tensors")
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, torch.float16, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if token_major:
+        cap, hkv = k.shape[0], k.shape[1]
+        ts, hs = hkv * HEAD_DIM, HEAD_DIM
+    else:
+        hkv, cap = k.shape[0], k.shape[1]
+        ts, hs = HEAD_DIM, cap * HEAD_DIM
+    n_seqs, hq, _ = q.shape
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        workspace = decode_workspace(n_seqs, hq, hkv, max_seq_len, q.device)
+    _check("iq_decode_attention_f16",
+           lib().iq_decode_attention_f16(k.data_ptr(), v.data_ptr(), ts, hs, hkv, cap, _dev(q, torch.float32, "q"),
+                                         hq, _dev(seq_start, torch.int32, "seq_start"),
+                                         _dev(seq_len, torch.int32, "seq_len"), n_seqs, max_seq_len, scale,
+                                         _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
+                                         workspace.numel(), _stream(stream)))
     return out

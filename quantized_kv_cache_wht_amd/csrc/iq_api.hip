@@ -224,4 +224,45 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t token_stride, int64_t head_stride,
+                                  int32_t num_kv_heads, int32_t capacity, const float* q, int32_t num_q_heads,
+                                  const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                                  int32_t max_seq_len, float scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (num_kv_heads < 1 || capacity < 0 || (capacity % 32) != 0) return IQ_ERR_INVALID_ARG;
+  if (token_stride <= 0 || head_stride < 0 || (token_stride % 8) != 0 || (head_stride % 8) != 0)
+    return IQ_ERR_INVALID_ARG;
+  if (n_seqs < 0 || max_seq_len < 0 || num_q_heads < 1) return IQ_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!group_supported(group)) return IQ_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return IQ_OK;
+  if (!k || !v || !q || !seq_start || !seq_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(workspace)) & 15u)
+    return IQ_ERR_INVALID_ARG;
+  if (n_seqs > 65535 || num_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  const DecodePlan plan = decode_plan(n_seqs, num_kv_heads, max_seq_len);
+  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  F16DecodeArgs a{};
+  a.k = static_cast<const _Float16*>(k);
+  a.v = static_cast<const _Float16*>(v);
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.q = q;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.n_seqs = n_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.capacity = capacity;
+  a.max_seq_len = max_seq_len;
+  a.blocks_per_split = plan.blocks_per_split;
+  a.n_splits = plan.n_splits;
+  a.qscale = scale * 1.4426950408889634f;
+  return hip_status(launch_decode_f16(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -34,63 +34,12 @@
 // of nV), raised lazily (only when a block exceeds it by more than 2^8), so
 // p_t nV_t <= 256 and the fp16 operand never overflows while accumulator
 // rescaling is rare.
-#include <math.h>
-
-#include "iq_device.h"
-#include "iq_launch.h"
+#include "iq_decode_common.h"
 
 namespace iq {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-union H8 {
-  half8 h;
-  uint32_t u[4];
-  uint2 u2[2];
-  uint4 u4;
-};
-
-constexpr int kDecThreads = 256;
-constexpr int kWaves = kDecThreads / 64;
-constexpr int kBlk = 32;             // cache slots per wave iteration
-constexpr int kRec = 132;            // floats per partial record: m, l, 2 pad, o[128]
-constexpr int kTargetBlocks = 512;   // split-K occupancy target (work-groups): 2 per CU
-constexpr int kMinBlocksPerSplit = 4;
-// Split length cap: a single sequence is cut into about one resident round of
-// work-groups; several sequences (possibly of different lengths) into
-// shorter splits, so the long ones do not leave a tail of lone work-groups.
-constexpr int kMaxBlocksPerSplitOne = 64;
-constexpr int kMaxBlocksPerSplitMany = 32;
-constexpr int kMaxSplits = 2048;
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeLanes = kDim / 4;                    // lanes per record, 4 dims each
-constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by side
-constexpr int kMergeChunk = 4;                           // records per lane per round of loads
 constexpr int kLutEntries = 64;      // all pairs of 3-bit codes
 constexpr int kLutCopies = 16;       // one per lane of a 16-lane group
-constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
-
-__device__ __forceinline__ bool seq_ok(const DecodeArgs& a, int s, int* start, int* len) {
-  const int st = a.seq_start[s];
-  const int ln = a.seq_len[s];
-  *start = st;
-  *len = ln;
-  return st >= 0 && ln >= 0 && ln <= a.max_seq_len && static_cast<int64_t>(st) + ln <= a.capacity;
-}
-
-// 32-slot blocks covering [start, start + len) from the 32-aligned base.
-__device__ __forceinline__ int n_blocks(int start, int len) {
-  return len > 0 ? ((start - (start & ~(kBlk - 1)) + len + kBlk - 1) / kBlk) : 0;
-}
-
-__device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float dpp_row_ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
-}
 
 // Table entry of the code pair at bit BIT of w: {hi|lo of code a, hi|lo of code b}.
 template <int BIT, int N>
@@ -105,10 +54,6 @@ __device__ __forceinline__ uint2 pair_entry(const uint32_t (&w)[N], const char* 
   return *reinterpret_cast<const uint2*>(lut + addr);
 }
 
-// 2^x on the transcendental unit (results below 2^-126 flush to 0, which the
-// softmax weights tolerate).
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Code operand for the 4 codes at bits BIT .. BIT+11 of w (two pairs).
 template <int BIT, int N>
 __device__ __forceinline__ half8 code_operand(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
@@ -116,11 +61,6 @@ __device__ __forceinline__ half8 code_operand(const uint32_t (&w)[N], const char
   r.u2[0] = pair_entry<BIT>(w, lut, lane_off);
   r.u2[1] = pair_entry<BIT + 6>(w, lut, lane_off);
   return r.h;
-}
-
-// fp16 pair (x, x) of one value.
-__device__ __forceinline__ uint32_t dup16(float x) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x));
 }
 
 // Packed codes and norms of one 32-slot block for this lane.
@@ -146,12 +86,6 @@ __device__ __forceinline__ void load_block(const DecodeArgs& a, size_t slot_base
   const float4* nvp = reinterpret_cast<const float4*>(a.v_norms + slot_base + slot0 + 8 * q);
   d.nk0 = nkp[0]; d.nk1 = nkp[1]; d.nv0 = nvp[0]; d.nv1 = nvp[1];
 }
-
-// Per-wave running state of the online softmax and the PV accumulators.
-struct WaveState {
-  floatx4 acc[8];      // [dim tile d]: rows 4q + i, column n (dim 8n + d)
-  float m, l;
-};
 
 template <int G>
 struct Consts {
@@ -267,13 +201,6 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int slot0, i
   }
   IQ_PV(0) IQ_PV(1) IQ_PV(2) IQ_PV(3) IQ_PV(4) IQ_PV(5) IQ_PV(6) IQ_PV(7)
 #undef IQ_PV
-}
-
-// Splits of (seq, kv head) that hold at least one block: split k covers
-// blocks [k bps, (k+1) bps), the last one also the block that a start not
-// aligned to 32 adds beyond the plan.
-__device__ __forceinline__ int live_splits(int nblk, int bps, int n_splits) {
-  return nblk > 0 ? min(n_splits, (nblk + bps - 1) / bps) : 0;
 }
 
 template <int G>
@@ -468,26 +395,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   }
 }
 
-// Sum (or max) over the 32 lanes of a half-wave: four DPP rotations within
-// each row of 16, then one swizzle across the two rows.
-template <bool kMax>
-__device__ __forceinline__ float half_wave_reduce(float x) {
-  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
-  x = op(x, dpp_f32<0x128>(x));   // row_ror:8
-  x = op(x, dpp_f32<0x124>(x));   // row_ror:4
-  x = op(x, dpp_f32<0x122>(x));   // row_ror:2
-  x = op(x, dpp_f32<0x121>(x));   // row_ror:1
-  return op(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));  // lane ^ 16
-}
-
 // One work-group per (seq, query head): merges the live splits' records
 //   M = max m_k, l = sum 2^(m_k - M) l_k, o' = sum 2^(m_k - M) o'_k,
-// then out = Hn B^T (o' / l), the single inverse rotation. Lane t first reads
+// then out = Hn B^T (o' / l), the single inverse rotation (kRotate; the fp16
+// decode's records are already in the model's basis). Lane t first reads
 // dims 4 (t % 32) .. +3 of records t / 32, t / 32 + 32, ... (coalesced), keeps
 // a running merge of them, and parks the result in LDS; the 32 rows are then
 // combined with one row per lane of a half-wave. An empty sequence gives 0,
 // an invalid one NaN.
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+template <bool kRotate>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
   __shared__ float rm[kMergeRows], rl[kMergeRows];
   __shared__ __align__(16) float ro[kMergeRows][kDim];
   __shared__ __align__(16) float fin[kDim];
@@ -500,7 +417,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int live = live_splits(nblk, a.blocks_per_split, a.n_splits);
 
   float rp[16];
-  if (tid < 16) load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, tid, rp);
+  if (kRotate && tid < 16) load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, tid, rp);
   const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.n_splits * kRec;
   float mx = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -537,7 +454,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   }
   reinterpret_cast<float4*>(ro[row])[d4] = o;
   float m[32];
-  if (tid < 16) so4_matrices_row(rp, m);
+  if (kRotate && tid < 16) so4_matrices_row(rp, m);
   __syncthreads();
   {
     // half-wave: lane = row (0..31), dims 4 c .. 4 c + 3 with c = tid / 32
@@ -561,8 +478,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = fin[8 * tid + i];
-    so4_apply_row<true>(x, m);
-    wht128_row(x, tid);
+    if (kRotate) {
+      so4_apply_row<true>(x, m);
+      wht128_row(x, tid);
+    }
     float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + 8 * tid);
     dst[0] = ok ? make_float4(x[0], x[1], x[2], x[3]) : make_float4(NAN, NAN, NAN, NAN);
     dst[1] = ok ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(NAN, NAN, NAN, NAN);
@@ -606,7 +525,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
+  MergeArgs m{a.rot, a.seq_start, a.seq_len, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group,
+              a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits};
+  return launch_merge(m, st);
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
+  if (a.rot != nullptr)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 

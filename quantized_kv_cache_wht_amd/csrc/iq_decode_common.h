@@ -1,0 +1,97 @@
+// Pieces shared by the decode kernels (packed 3-bit cache and fp16 cache):
+// split-K geometry, the per-wave online-softmax state, the wave-level
+// reductions and the MFMA wrapper.
+#pragma once
+
+#include <math.h>
+
+#include "iq_device.h"
+#include "iq_launch.h"
+
+namespace iq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+union H8 {
+  half8 h;
+  uint32_t u[4];
+  uint2 u2[2];
+  uint4 u4;
+};
+
+constexpr int kDecThreads = 256;
+constexpr int kWaves = kDecThreads / 64;
+constexpr int kBlk = 32;             // cache slots per wave iteration
+constexpr int kRec = 132;            // floats per partial record: m, l, 2 pad, o[128]
+constexpr int kTargetBlocks = 512;   // split-K occupancy target (work-groups): 2 per CU
+constexpr int kMinBlocksPerSplit = 4;
+// Split length cap: a single sequence is cut into about one resident round of
+// work-groups; several sequences (possibly of different lengths) into
+// shorter splits, so the long ones do not leave a tail of lone work-groups.
+constexpr int kMaxBlocksPerSplitOne = 64;
+constexpr int kMaxBlocksPerSplitMany = 32;
+constexpr int kMaxSplits = 2048;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeLanes = kDim / 4;                    // lanes per record, 4 dims each
+constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by side
+constexpr int kMergeChunk = 4;                           // records per lane per round of loads
+constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
+
+template <typename Args>
+__device__ __forceinline__ bool seq_ok(const Args& a, int s, int* start, int* len) {
+  const int st = a.seq_start[s];
+  const int ln = a.seq_len[s];
+  *start = st;
+  *len = ln;
+  return st >= 0 && ln >= 0 && ln <= a.max_seq_len && static_cast<int64_t>(st) + ln <= a.capacity;
+}
+
+// 32-slot blocks covering [start, start + len) from the 32-aligned base.
+__device__ __forceinline__ int n_blocks(int start, int len) {
+  return len > 0 ? ((start - (start & ~(kBlk - 1)) + len + kBlk - 1) / kBlk) : 0;
+}
+
+__device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float dpp_row_ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+
+// 2^x on the transcendental unit (results below 2^-126 flush to 0, which the
+// softmax weights tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp16 pair (x, x) of one value.
+__device__ __forceinline__ uint32_t dup16(float x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x));
+}
+
+// Per-wave running state of the online softmax and the PV accumulators.
+struct WaveState {
+  floatx4 acc[8];      // [dim tile d]: rows 4q + i, column n (dim 8n + d)
+  float m, l;
+};
+
+// Splits of (seq, kv head) that hold at least one block: split k covers
+// blocks [k bps, (k+1) bps), the last one also the block that a start not
+// aligned to 32 adds beyond the plan.
+__device__ __forceinline__ int live_splits(int nblk, int bps, int n_splits) {
+  return nblk > 0 ? min(n_splits, (nblk + bps - 1) / bps) : 0;
+}
+
+// Sum (or max) over the 32 lanes of a half-wave: four DPP rotations within
+// each row of 16, then one swizzle across the two rows.
+template <bool kMax>
+__device__ __forceinline__ float half_wave_reduce(float x) {
+  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  x = op(x, dpp_f32<0x128>(x));   // row_ror:8
+  x = op(x, dpp_f32<0x124>(x));   // row_ror:4
+  x = op(x, dpp_f32<0x122>(x));   // row_ror:2
+  x = op(x, dpp_f32<0x121>(x));   // row_ror:1
+  return op(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));  // lane ^ 16
+}
+
+}  // namespace iq

@@ -78,6 +78,46 @@ struct DecodeArgs {
   Codebook cb;
 };
 
+// Decode over a plain fp16 K/V cache (the baseline and the unfused path):
+// element (token t, KV head h, dim j) at k[t * token_stride + h * head_stride + j].
+struct F16DecodeArgs {
+  const _Float16* k;
+  const _Float16* v;
+  int64_t token_stride;
+  int64_t head_stride;
+  const float* q;
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  float* out;
+  float* ws;
+  int32_t n_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t capacity;
+  int32_t max_seq_len;
+  int32_t blocks_per_split;
+  int32_t n_splits;
+  float qscale;
+};
+
+// Split-K merge of either decode: rot = nullptr for records already in the
+// model's basis (fp16 cache), else the rotation whose inverse is applied once.
+struct MergeArgs {
+  const float* rot;
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  float* out;
+  const float* ws;
+  int32_t n_seqs;
+  int32_t num_q_heads;
+  int32_t group;
+  int32_t capacity;
+  int32_t max_seq_len;
+  int32_t blocks_per_split;
+  int32_t n_splits;
+};
+
 hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s);
 hipError_t launch_rotate(const RotateArgs& a, bool inverse, hipStream_t s);
 hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
@@ -91,5 +131,7 @@ DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len
 // Workspace: one partial record (m, l, 2 pad, o[128] fp32) per (seq, query head, split).
 size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodePlan& p);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace iq

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     h = ctypes.CDLL(iq.library_path())
     for n in names:
         assert hasattr(h, n), n
@@ -81,6 +81,25 @@ def test_decode_validation():
     # workspace grows with context and shrinks to one split for short contexts
     assert L.iq_decode_workspace_bytes(1, 32, 4, 32768) >= L.iq_decode_workspace_bytes(1, 32, 4, 1024)
     assert L.iq_decode_workspace_bytes(1, 32, 8, 1) == 32 * 132 * 4   # one record per query head
+
+
+def test_decode_f16_validation():
+    L = iq.lib()
+    p = ctypes.c_void_p(0x50000)
+    need = L.iq_decode_workspace_bytes(1, 8, 2, 100)
+
+    def call(k=p, ts=256, hs=128, hkv=2, cap=128, hq=8, n=1, ws=need, wsp=p):
+        return L.iq_decode_attention_f16(k, p, ts, hs, hkv, cap, p, hq, p, p, n, 100, 0.1, p, wsp, ws, None)
+    assert call(cap=100) == -1                 # capacity % 32
+    assert call(ts=12) == -1                   # stride % 8
+    assert call(ts=0) == -1
+    assert call(hq=7) == -1                    # Hq % Hkv
+    assert call(hq=6) == -2                    # group 3
+    assert call(ws=need - 1) == -4
+    assert call(k=ctypes.c_void_p(0x50008)) == -1   # alignment
+    assert call(k=None) == -1
+    assert call(n=0) == 0
+    assert call(hkv=0) == -1
 
 
 def test_dequant_and_rotate_validation():
