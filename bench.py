@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch the step's kernels one by one instead of a graph")
+    p.add_argument("--no-compare", action="store_true", help="skip the FP16-KV and unfused comparison timings")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="finish with 3 device-to-device copies of this many MiB (reference for HBM counters)")
     return p.parse_args()
@@ -54,7 +55,7 @@ def decode_source_digest() -> str:
     """sha256 over the sources of the decode kernels (the traffic figures belong to one version)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_wht_amd", "csrc")
-    for name in ("iq_decode.hip", "iq_device.h", "iq_launch.h"):
+    for name in ("iq_decode.hip", "iq_decode_common.h", "iq_device.h", "iq_launch.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -78,6 +79,57 @@ def measured_traffic(workload: str):
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def time_per_call(torch, fn, n_calls, stream):
+    """GPU time per call of fn(i), i = 0 .. n_calls - 1, back to back on one stream."""
+    for i in range(n_calls):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * 2 * n_calls)
+    e0.record(stream)
+    for i in range(n_calls):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n_calls
+
+
+def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, fused_us, n_layers=8):
+    """The pages' comparisons on this workload's decode, over n_layers layers' caches in turn:
+    the same decode over an fp16 K/V cache (FP16-KV baseline, K/V of the same shape and value
+    model), and the unfused path (iq_dequantize of the packed cache to fp16, then that decode)."""
+    import torch
+    k16 = [synth_kv(T, 30_000 + l).transpose(0, 1).contiguous() for l in range(n_layers)]   # [Hkv][T][128]
+    v16 = [synth_kv(T, 40_000 + l).transpose(0, 1).contiguous() for l in range(n_layers)]
+    dk = torch.empty((T, hkv, 128), dtype=torch.float16, device=k16[0].device)
+    dv = torch.empty_like(dk)
+
+    def fp16_decode(i):
+        l = i % n_layers
+        iq.iq_decode_attention_f16(k16[l], v16[l], qs[l], seq_start, seq_len, T, token_major=False, out=outs[l],
+                                   workspace=ws, stream=stream)
+
+    def dequantize(i):
+        iq.iq_dequantize(caches[i % n_layers], 0, T, torch.float16, k_out=dk, v_out=dv, stream=stream)
+
+    def unfused(i):
+        l = i % n_layers
+        dequantize(i)
+        iq.iq_decode_attention_f16(dk, dv, qs[l], seq_start, seq_len, T, token_major=True, out=outs[l],
+                                   workspace=ws, stream=stream)
+
+    n = 4 * n_layers
+    r = {"layers_cycled": n_layers,
+         "fused_packed_decode_us": round(fused_us, 3),
+         "fused_packed_bytes_per_launch": hkv * T * 2 * ROW_BYTES,
+         "fp16_kv_decode_us": round(time_per_call(torch, fp16_decode, n, stream), 3),
+         "fp16_kv_bytes_per_launch": hkv * T * 2 * 256,
+         "dequantize_to_fp16_us": round(time_per_call(torch, dequantize, n, stream), 3),
+         "unfused_decode_us": round(time_per_call(torch, unfused, n, stream), 3)}
+    del k16, v16, dk, dv
+    return r
 
 
 def cpu_baseline(w, budget_s: float):
@@ -229,6 +281,8 @@ def main():
     dec_us = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 / L for r in range(reps)])
     achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
+    comp = None if args.no_compare else comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv,
+                                                     T, hkv, float(dec_us.mean()))
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -265,6 +319,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
+        "comparisons": comp,
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

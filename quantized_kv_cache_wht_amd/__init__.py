@@ -219,15 +219,21 @@ def iq_rotate_quantize_append(cache: PackedKVCache, k: torch.Tensor, v: torch.Te
                                            n_tok, first_slot, sp, _stream(stream)))
 
 
-def iq_dequantize(cache: PackedKVCache, first_slot: int, n_tokens: int, out_dtype=torch.float32, stream=None):
-    """Explicit reconstruction of K and V rows: two tensors [n_tokens][Hkv][128]."""
+def iq_dequantize(cache: PackedKVCache, first_slot: int, n_tokens: int, out_dtype=torch.float32,
+                  k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None, stream=None):
+    """Explicit reconstruction of K and V rows: two tensors [n_tokens][Hkv][128] (given or new)."""
     dt = {torch.float32: IQ_F32, torch.float16: IQ_F16}[out_dtype]
     shape = (n_tokens, cache.num_kv_heads, HEAD_DIM)
-    k_out = torch.empty(shape, dtype=out_dtype, device=cache.k_codes.device)
-    v_out = torch.empty(shape, dtype=out_dtype, device=cache.k_codes.device)
+    dev = cache.k_codes.device
+    k_out = torch.empty(shape, dtype=out_dtype, device=dev) if k_out is None else k_out
+    v_out = torch.empty(shape, dtype=out_dtype, device=dev) if v_out is None else v_out
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
     view = cache.view()
-    _check("iq_dequantize", lib().iq_dequantize(ctypes.byref(view), first_slot, n_tokens, dt, k_out.data_ptr(),
-                                                v_out.data_ptr(), _stream(stream)))
+    _check("iq_dequantize", lib().iq_dequantize(ctypes.byref(view), first_slot, n_tokens, dt,
+                                                _dev(k_out, out_dtype, "k_out"), _dev(v_out, out_dtype, "v_out"),
+                                                _stream(stream)))
     return k_out, v_out
 
 
