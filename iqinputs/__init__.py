@@ -86,6 +86,24 @@ def rotation_params(seed: int, layer: int, num_kv_heads: int) -> np.ndarray:
     return q.reshape(num_kv_heads, N_BLOCKS, 8).astype(np.float32)
 
 
+ROTATION_KINDS = ("wht_so4", "iso", "planar")
+
+
+def rotation_params_kind(seed: int, layer: int, num_kv_heads: int, kind: str) -> np.ndarray:
+    """Random parameters of one rotation kind, float32:
+    ``wht_so4`` [Hkv][32][8] (as ``rotation_params``); ``iso`` [Hkv][32][4], one
+    Haar-random unit quaternion per 4-dim block; ``planar`` [Hkv][64][2], one
+    uniformly random unit vector (cos, sin) per dim pair (two N(0,1) draws
+    normalised in float64)."""
+    if kind == "wht_so4":
+        return rotation_params(seed, layer, num_kv_heads)
+    g = rng(seed, _T_ROT, layer, 1 + ROTATION_KINDS.index(kind))
+    shape = {"iso": (num_kv_heads, N_BLOCKS, 4), "planar": (num_kv_heads, HEAD_DIM // 2, 2)}[kind]
+    x = g.standard_normal(shape)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    return x.astype(np.float32)
+
+
 def _as_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return x.astype(np.float32)

@@ -18,7 +18,9 @@ Sources (titles of the pages; section names in brackets):
   [TQ-essay] zhichai.net essay "压缩与速度的博弈——TurboQuant 和 RotorQuant 的真相",
             sections "Beta 分布的魔力", "Lloyd-Max 最优量化", "真正的瓶颈",
             "为什么压缩 KV 缓存这么难？" (the attention formula).
-  [RQ-blurb] sd114.wiki RotorQuant page, section "V 缓存的逆旋转修复".
+  [RQ-blurb] sd114.wiki RotorQuant page, sections "V 缓存的逆旋转修复" and
+            "绕过蝴蝶网络" (the Givens / quaternion variants).
+  [TQ-essay] also section "三种变体" (the variant table).
 
 Readings taken where the pages are silent or garbled (each is also listed in
 the design notes of the repository):
@@ -49,6 +51,10 @@ the design notes of the repository):
     the code of dimension j of the token at position r sits at bits
     [24j + 3r, 24j + 3r + 3). The pages only say the codes are packed; this
     dim-major order keeps the eight codes of one dimension together.
+  * Rotation variants ([TQ-essay] "三种变体"): the single-quaternion IsoQuant
+    is read as the left-isoclinic map v -> q (x) v per 4-dim block (128
+    parameters, 512 FMA, no WHT); PlanarQuant as one Givens rotation per dim
+    pair (2i, 2i+1) stored as (cos, sin) (128 parameters, 256 FMA, no WHT).
   * Dequantization: x_hat = n . R^-1 c[code], R^-1 = Hn . B^T ([RQ-blurb]:
     the inverse rotation must be applied when reconstructing V).
   * Attention: softmax(scale . q K_hat^T) V_hat per query head
@@ -196,13 +202,64 @@ def so4_block_matrices(rot: np.ndarray) -> np.ndarray:
     return m
 
 
+# Rotation variants ([TQ-essay] "三种变体"; [RQ-blurb] section on bypassing the
+# butterfly network: independent 2-D Givens rotations per pair or 4-D
+# quaternion rotations per group, no WHT, 128 parameters each). The kind of a
+# head's parameters follows from their shape:
+#   [32, 8]  WHT then SO(4) with (qL, qR) per block  (the IsoQuant of [RQ-abs])
+#   [32, 4]  one unit quaternion q per block, v -> q (x) v, no WHT  (a left-
+#            isoclinic SO(4) rotation; 32 x 16 = 512 FMA)
+#   [64, 2]  one Givens rotation per dim pair (2i, 2i+1), stored (cos, sin),
+#            no WHT  (64 x 4 = 256 FMA)
+ROT_WHT_SO4, ROT_ISO, ROT_PLANAR = 0, 1, 2
+
+
+def rotation_kind(rot: np.ndarray) -> int:
+    shape = tuple(np.shape(rot)[-2:])
+    kinds = {(N_BLOCKS, 8): ROT_WHT_SO4, (N_BLOCKS, 4): ROT_ISO, (D // 2, 2): ROT_PLANAR}
+    if shape not in kinds:
+        raise ValueError(f"rotation parameters of shape {shape} match no rotation kind")
+    return kinds[shape]
+
+
+def iso_apply(y: np.ndarray, rot: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Per block v -> q (x) v (inverse: conj(q) (x) v); rot [32, 4] renormalised."""
+    q = np.asarray(rot, np.float64)
+    q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    v = np.asarray(y, np.float64).reshape(y.shape[:-1] + (N_BLOCKS, 4))
+    out = quat_mul(quat_conj(q) if inverse else q, v)
+    return out.reshape(y.shape)
+
+
+def givens_apply(y: np.ndarray, rot: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Per pair (x, y) -> (c x - s y, s x + c y) (inverse: the transpose); rot [64, 2] = (c, s) renormalised."""
+    cs = np.asarray(rot, np.float64)
+    cs = cs / np.linalg.norm(cs, axis=-1, keepdims=True)
+    c, s = cs[:, 0], (-cs[:, 1] if inverse else cs[:, 1])
+    v = np.asarray(y, np.float64).reshape(y.shape[:-1] + (D // 2, 2))
+    out = np.stack([c * v[..., 0] - s * v[..., 1], s * v[..., 0] + c * v[..., 1]], axis=-1)
+    return out.reshape(y.shape)
+
+
 def rotate(x: np.ndarray, rot: np.ndarray) -> np.ndarray:
-    """y = B . Hn . x in float64 for [..., 128] vectors of one head."""
+    """y = R x in float64 for [..., 128] vectors of one head: B . Hn . x for the
+    WHT + SO(4) kind, the block map alone for the two others."""
+    kind = rotation_kind(rot)
+    if kind == ROT_ISO:
+        return iso_apply(x, rot)
+    if kind == ROT_PLANAR:
+        return givens_apply(x, rot)
     return so4_apply(wht(x), rot)
 
 
 def inverse_rotate(y: np.ndarray, rot: np.ndarray) -> np.ndarray:
-    """x = Hn . B^T . y in float64 (Hn is symmetric and its own inverse)."""
+    """x = R^-1 y in float64 (Hn . B^T . y for the WHT + SO(4) kind: Hn is symmetric
+    and its own inverse)."""
+    kind = rotation_kind(rot)
+    if kind == ROT_ISO:
+        return iso_apply(y, rot, inverse=True)
+    if kind == ROT_PLANAR:
+        return givens_apply(y, rot, inverse=True)
     return wht(so4_apply(y, rot, inverse=True))
 
 

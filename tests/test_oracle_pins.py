@@ -131,6 +131,68 @@ def test_parameter_and_fma_counts():
     assert wht_ops + so4_fma == 1408 and 128 * 128 == 16384
 
 
+# ------------------------------------------------- rotation variants ----
+# The essay's variant table ("三种变体") and the RotorQuant page: PlanarQuant,
+# one 2-D Givens rotation per dim pair (128 parameters, 256 FMA); the
+# single-quaternion IsoQuant, one 4-D quaternion rotation per 4 dims
+# (128 parameters, 512 FMA); neither has a WHT.
+def _rot_kind(kind, seed=11, heads=1):
+    return iqinputs.rotation_params_kind(seed, 0, heads, kind)
+
+
+def _is_rotation_without_mixing(m, block):
+    """m (columns = images of e_i) orthogonal, det +1, and zero outside its diagonal blocks."""
+    assert np.allclose(m @ m.T, np.eye(128), atol=1e-13) and np.linalg.det(m) > 0
+    mask = np.kron(np.eye(128 // block), np.ones((block, block))).astype(bool)
+    assert np.all(m[~mask] == 0)
+
+
+def check_planar_rotation():
+    rot = _rot_kind("planar")[0]
+    assert rot.shape == (64, 2) and rot.size == 128
+    m = R.rotate(np.eye(128), rot).T
+    _is_rotation_without_mixing(m, 2)
+    theta = np.arctan2(rot[:, 1].astype(np.float64), rot[:, 0].astype(np.float64))
+    for i in range(64):
+        ref = Rotation.from_euler("z", theta[i]).as_matrix()[:2, :2]      # library 2-D rotation
+        assert np.allclose(m[2 * i:2 * i + 2, 2 * i:2 * i + 2], ref, atol=1e-12)
+    x = np.random.default_rng(2).standard_normal((6, 128))
+    assert np.allclose(R.inverse_rotate(R.rotate(x, rot), rot), x, atol=1e-13)
+    assert 64 * 4 == 256                          # 2 x 2 matrix per pair: the table's 256 FMA
+
+
+def test_planar_rotation_is_givens_per_pair():
+    check_planar_rotation()
+
+
+def check_iso_rotation():
+    rot = _rot_kind("iso")[0]
+    assert rot.shape == (32, 4) and rot.size == 128
+    m = R.rotate(np.eye(128), rot).T
+    _is_rotation_without_mixing(m, 4)
+    # worked example of the convention, by the Hamilton rules (ij = k):
+    # (cos a + i sin a) (x) j = j cos a + k sin a
+    a = 0.3
+    q = np.tile([math.cos(a), math.sin(a), 0.0, 0.0], (32, 1))
+    v = np.zeros(128)
+    v[2::4] = 1.0
+    y = R.rotate(v, q).reshape(32, 4)
+    assert np.allclose(y, np.tile([0.0, 0.0, math.cos(a), math.sin(a)], (32, 1)), atol=1e-15)
+    # isoclinic: every vector of a block turns by the same angle, cos = q_w
+    qn = rot.astype(np.float64) / np.linalg.norm(rot.astype(np.float64), axis=1, keepdims=True)
+    x = np.random.default_rng(4).standard_normal((7, 128))
+    y = R.rotate(x, rot)
+    dots = np.einsum("nbi,nbi->nb", x.reshape(7, 32, 4), y.reshape(7, 32, 4))
+    assert np.allclose(dots, qn[None, :, 0] * np.sum(x.reshape(7, 32, 4) ** 2, axis=2), atol=1e-12)
+    assert np.allclose(R.rotate(x, np.tile([1.0, 0, 0, 0], (32, 1))), x, atol=0)
+    assert np.allclose(R.inverse_rotate(y, rot), x, atol=1e-13)
+    assert 32 * 16 == 512                         # 4 x 4 matrix per block: the table's 512 FMA
+
+
+def test_iso_rotation_is_left_isoclinic_per_block():
+    check_iso_rotation()
+
+
 # ------------------------------------------------------------ codebook ----
 def _golden_max():
     th, lv, mse = [], [], None
@@ -329,10 +391,10 @@ def test_rotation_isotropizes_outlier_channels():
 
 
 # -------------------------------------------------------- attention ----
-def _small_cache(codebook, n_tok=304, hkv=2, hq=4, seed=11, lens=(300,)):
+def _small_cache(codebook, n_tok=304, hkv=2, hq=4, seed=11, lens=(300,), kind="wht_so4"):
     c32, t32, _ = codebook
     g = np.random.default_rng(seed)
-    rot = _rot(seed=seed, heads=hkv)
+    rot = iqinputs.rotation_params_kind(seed, 0, hkv, kind)
     k = g.standard_normal((n_tok, hkv, 128))
     v = g.standard_normal((n_tok, hkv, 128))
     kr, kn = R.encode_tokens(k, rot, t32)
@@ -342,9 +404,10 @@ def _small_cache(codebook, n_tok=304, hkv=2, hq=4, seed=11, lens=(300,)):
     return q, kr, kn, vr, vn, rot, starts, np.array(lens, np.int32)
 
 
-def test_attention_packed_domain_equals_brute_force(codebook):
+@pytest.mark.parametrize("kind", iqinputs.ROTATION_KINDS)
+def test_attention_packed_domain_equals_brute_force(codebook, kind):
     c32 = codebook[0]
-    args = _small_cache(codebook, n_tok=304, lens=(120, 0, 1, 179))
+    args = _small_cache(codebook, n_tok=304, lens=(120, 0, 1, 179), kind=kind)
     scale = 1 / math.sqrt(128)
     a = R.decode_attention(*args, scale, c32)
     b = R.decode_attention_rotated(*args, scale, c32)
@@ -432,3 +495,19 @@ def test_mutation_quantize_ge_instead_of_gt(monkeypatch, codebook):
         return np.sum(y32[..., :, None] >= thr[..., None, :], axis=-1).astype(np.uint8), n
     monkeypatch.setattr(R, "quantize", bad)
     _expect_fail(check_quantize, codebook)
+
+
+def test_mutation_givens_transposed(monkeypatch):
+    good = R.givens_apply
+    monkeypatch.setattr(R, "givens_apply", lambda y, rot, inverse=False: good(y, rot, not inverse))
+    _expect_fail(check_planar_rotation)
+
+
+def test_mutation_quaternion_multiplied_on_the_right(monkeypatch):
+    def bad(y, rot, inverse=False):
+        q = np.asarray(rot, np.float64)
+        q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+        v = np.asarray(y, np.float64).reshape(y.shape[:-1] + (32, 4))
+        return R.quat_mul(v, R.quat_conj(q) if inverse else q).reshape(y.shape)
+    monkeypatch.setattr(R, "iso_apply", bad)
+    _expect_fail(check_iso_rotation)
