@@ -69,6 +69,21 @@ typedef enum {
 
 typedef enum { IQ_F32 = 0, IQ_F16 = 1 } iq_dtype;
 
+/* The rotation applied before quantization (arXiv 2608.08081 abstract for the
+ * first; zhichai.net essay, section "三种变体", and the sd114.wiki RotorQuant
+ * page, section on bypassing the butterfly network, for the two variants).
+ * Parameters per KV head, float32, stored quaternions / pairs renormalised on
+ * use:
+ *   IQ_ROT_WHT_SO4  normalised Walsh-Hadamard transform, then per 4-dim block
+ *                   b: v -> qL (x) v (x) conj(qR); rot [Hkv][32][8] = (qL, qR)
+ *                   as (w, x, y, z) each: 256 per head.
+ *   IQ_ROT_ISO      no WHT; per 4-dim block v -> q (x) v (left-isoclinic);
+ *                   rot [Hkv][32][4]: 128 per head.
+ *   IQ_ROT_PLANAR   no WHT; per dim pair (2i, 2i+1) the Givens rotation
+ *                   (x, y) -> (c x - s y, s x + c y); rot [Hkv][64][2] = (c, s):
+ *                   128 per head. */
+typedef enum { IQ_ROT_WHT_SO4 = 0, IQ_ROT_ISO = 1, IQ_ROT_PLANAR = 2 } iq_rotation;
+
 /* One layer of the packed cache. All pointers are device memory. */
 typedef struct {
   int32_t head_dim;       /* must be 128 */
@@ -79,7 +94,8 @@ typedef struct {
   uint8_t* v_codes;       /* [num_kv_heads][capacity/8][384] V tiles, 16-byte aligned */
   float* k_norms;         /* [num_kv_heads][capacity] */
   float* v_norms;         /* [num_kv_heads][capacity] */
-  const float* rot;       /* [num_kv_heads][32][8] */
+  const float* rot;       /* rotation parameters, layout per `rotation` */
+  int32_t rotation;       /* iq_rotation; K and V of a head share it */
 } iq_cache_view;
 
 /* Human-readable name of a status code (static string). */
@@ -93,10 +109,10 @@ IQ_API iq_status iq_codebook(float centroids[8], float thresholds[7]);
 
 /* Rotate fp32 vectors with the per-head rotation (the first half of the
  * encode; the same transform is applied to queries before scoring).
- *   x, y   device float [n_tokens][num_heads][128]; y may equal x.
- *   rot    device float [num_heads][32][8].
- *   inverse = 0: y = B . Hn . x;  inverse = 1: y = Hn . B^T . x.           */
-IQ_API iq_status iq_rotate(const float* rot, int32_t num_heads, const float* x, float* y,
+ *   x, y      device float [n_tokens][num_heads][128]; y may equal x.
+ *   rot       device float, layout of `rotation` (see iq_rotation).
+ *   inverse = 0: y = R x (B . Hn . x for IQ_ROT_WHT_SO4); inverse = 1: y = R^-1 x. */
+IQ_API iq_status iq_rotate(const float* rot, int32_t rotation, int32_t num_heads, const float* x, float* y,
                     int32_t n_tokens, int32_t inverse, void* stream);
 
 /* Quantize and pack vectors that are already rotated (the second half of the

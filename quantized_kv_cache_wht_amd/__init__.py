@@ -23,6 +23,18 @@ TILE = 8                    # V tiles: 8 slots, dim-major
 TILE_BYTES = TILE * ROW_BYTES
 CAPACITY_MULTIPLE = 32      # cache capacity must be a multiple of this
 ROT_PARAMS_PER_HEAD = 256
+# iq_rotation: the kind follows from the parameters' per-head shape
+IQ_ROT_WHT_SO4, IQ_ROT_ISO, IQ_ROT_PLANAR = 0, 1, 2
+_ROT_SHAPES = {(32, 8): IQ_ROT_WHT_SO4, (32, 4): IQ_ROT_ISO, (64, 2): IQ_ROT_PLANAR}
+
+
+def rotation_kind(rot: torch.Tensor) -> int:
+    """iq_rotation of per-head parameters [Hkv][32][8] (WHT + SO(4)), [Hkv][32][4] (one quaternion per
+    block) or [Hkv][64][2] (one Givens rotation per dim pair)."""
+    kind = _ROT_SHAPES.get(tuple(rot.shape[-2:]))
+    if kind is None or rot.dim() != 3:
+        raise ValueError(f"rotation parameters of shape {tuple(rot.shape)} match no rotation kind")
+    return kind
 
 IQ_OK = 0
 IQ_F32 = 0
@@ -51,14 +63,15 @@ class CacheView(ctypes.Structure):
         ("k_norms", ctypes.c_void_p),
         ("v_norms", ctypes.c_void_p),
         ("rot", ctypes.c_void_p),
+        ("rotation", ctypes.c_int32),
     ]
 
 
 _SIGNATURES = {
     "iq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "iq_codebook": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
-    "iq_rotate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "iq_rotate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "iq_quantize_pack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p]),
     "iq_rotate_quantize_append": (ctypes.c_int, [ctypes.POINTER(CacheView), ctypes.c_void_p, ctypes.c_void_p,
@@ -144,7 +157,7 @@ class PackedKVCache:
     v_codes: torch.Tensor     # uint8 [Hkv][capacity / 8][384]
     k_norms: torch.Tensor     # float32 [Hkv][capacity]
     v_norms: torch.Tensor
-    rot: torch.Tensor         # float32 [Hkv][32][8]
+    rot: torch.Tensor         # float32 [Hkv][32][8], [Hkv][32][4] or [Hkv][64][2] (see rotation_kind)
 
     @classmethod
     def allocate(cls, num_kv_heads: int, capacity: int, rot: torch.Tensor, device="cuda") -> "PackedKVCache":
@@ -152,8 +165,9 @@ class PackedKVCache:
         cap = -(-capacity // CAPACITY_MULTIPLE) * CAPACITY_MULTIPLE
         zf = lambda: torch.zeros((num_kv_heads, cap), dtype=torch.float32, device=device)
         rot = rot.to(device=device, dtype=torch.float32).contiguous()
-        if tuple(rot.shape) != (num_kv_heads, 32, 8):
-            raise ValueError("rot must be [num_kv_heads][32][8]")
+        rotation_kind(rot)
+        if rot.shape[0] != num_kv_heads:
+            raise ValueError("rot must hold num_kv_heads heads")
         return cls(torch.zeros((num_kv_heads, cap, ROW_BYTES), dtype=torch.uint8, device=device),
                    torch.zeros((num_kv_heads, cap // TILE, TILE_BYTES), dtype=torch.uint8, device=device),
                    zf(), zf(), rot)
@@ -173,15 +187,16 @@ class PackedKVCache:
             _dev(getattr(self, name), torch.float32, name)
         return CacheView(HEAD_DIM, self.num_kv_heads, self.capacity, self.k_codes.data_ptr(),
                          self.v_codes.data_ptr(), self.k_norms.data_ptr(), self.v_norms.data_ptr(),
-                         self.rot.data_ptr())
+                         self.rot.data_ptr(), rotation_kind(self.rot))
 
 
 def iq_rotate(rot: torch.Tensor, x: torch.Tensor, inverse: bool = False, out: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:
-    """y = B Hn x (or Hn B^T x) for x float32 [n_tokens][num_heads][128]."""
+    """y = R x (or R^-1 x) for x float32 [n_tokens][num_heads][128]; the kind of R follows from rot's shape."""
     n_tok, heads, d = x.shape
     out = torch.empty_like(x) if out is None else out
-    _check("iq_rotate", lib().iq_rotate(_dev(rot, torch.float32, "rot"), heads, _dev(x, torch.float32, "x"),
+    _check("iq_rotate", lib().iq_rotate(_dev(rot, torch.float32, "rot"), rotation_kind(rot), heads,
+                                        _dev(x, torch.float32, "x"),
                                         _dev(out, torch.float32, "out"), n_tok, int(bool(inverse)),
                                         _stream(stream)))
     return out

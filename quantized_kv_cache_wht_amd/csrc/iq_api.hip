@@ -95,6 +95,8 @@ static iq_status check_view(const iq_cache_view* v) {
   if (v->head_dim != kDim) return IQ_ERR_UNSUPPORTED;
   if (v->num_kv_heads < 1 || v->capacity < 0 || v->capacity % 32 != 0) return IQ_ERR_INVALID_ARG;
   if (!v->k_codes || !v->v_codes || !v->k_norms || !v->v_norms || !v->rot) return IQ_ERR_INVALID_ARG;
+  if (v->rotation != IQ_ROT_WHT_SO4 && v->rotation != IQ_ROT_ISO && v->rotation != IQ_ROT_PLANAR)
+    return IQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(v->k_codes) | reinterpret_cast<uintptr_t>(v->v_codes) |
        reinterpret_cast<uintptr_t>(v->k_norms) | reinterpret_cast<uintptr_t>(v->v_norms)) & 15u)
     return IQ_ERR_INVALID_ARG;
@@ -127,13 +129,14 @@ iq_status iq_codebook(float centroids[8], float thresholds[7]) {
   return IQ_OK;
 }
 
-iq_status iq_rotate(const float* rot, int32_t num_heads, const float* x, float* y, int32_t n_tokens,
-                    int32_t inverse, void* stream) {
+iq_status iq_rotate(const float* rot, int32_t rotation, int32_t num_heads, const float* x, float* y,
+                    int32_t n_tokens, int32_t inverse, void* stream) {
   if (!rot || !x || !y || num_heads < 1 || n_tokens < 0 || (inverse != 0 && inverse != 1))
     return IQ_ERR_INVALID_ARG;
+  if (rotation != IQ_ROT_WHT_SO4 && rotation != IQ_ROT_ISO && rotation != IQ_ROT_PLANAR) return IQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) return IQ_ERR_INVALID_ARG;
   if (n_tokens == 0) return IQ_OK;
-  RotateArgs a{x, y, rot, n_tokens, num_heads};
+  RotateArgs a{rotation, x, y, rot, n_tokens, num_heads};
   return hip_status(launch_rotate(a, inverse != 0, static_cast<hipStream_t>(stream)));
 }
 
@@ -158,7 +161,7 @@ iq_status iq_rotate_quantize_append(const iq_cache_view* view, const void* k, co
   if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) return IQ_ERR_INVALID_ARG;
   if (!slots && (first_slot < 0 || static_cast<int64_t>(first_slot) + n_tokens > view->capacity))
     return IQ_ERR_CAPACITY;
-  AppendArgs a{k, v, slots, view->rot, view->k_codes, view->v_codes, view->k_norms, view->v_norms,
+  AppendArgs a{view->rotation, k, v, slots, view->rot, view->k_codes, view->v_codes, view->k_norms, view->v_norms,
                n_tokens, first_slot, view->num_kv_heads, view->capacity, codebook()};
   return hip_status(launch_append(a, in_dtype == IQ_F16, static_cast<hipStream_t>(stream)));
 }
@@ -172,7 +175,7 @@ iq_status iq_dequantize(const iq_cache_view* view, int32_t first_slot, int32_t n
   if (first_slot < 0 || static_cast<int64_t>(first_slot) + n_tokens > view->capacity) return IQ_ERR_CAPACITY;
   if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15u) return IQ_ERR_INVALID_ARG;
   if (n_tokens == 0 || (!k_out && !v_out)) return IQ_OK;
-  DequantArgs a{view->k_codes, view->v_codes, view->k_norms, view->v_norms, view->rot, k_out, v_out,
+  DequantArgs a{view->rotation, view->k_codes, view->v_codes, view->k_norms, view->v_norms, view->rot, k_out, v_out,
                 first_slot, n_tokens, view->num_kv_heads, view->capacity, codebook()};
   return hip_status(launch_dequant(a, out_dtype == IQ_F16, static_cast<hipStream_t>(stream)));
 }
@@ -206,6 +209,7 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   a.k_norms = view->k_norms;
   a.v_norms = view->v_norms;
   a.rot = view->rot;
+  a.rot_kind = view->rotation;
   a.q = q;
   a.seq_start = seq_start;
   a.seq_len = seq_len;

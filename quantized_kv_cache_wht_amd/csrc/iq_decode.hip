@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
         a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + pg) * kDim + 8 * pl);
     const float4 v0 = src[0], v1 = src[1];
     xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w; xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
-    load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, pl, rp);
+    load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, pl, rp);
   }
   // The two block loads are unconditional (a wave with fewer blocks re-reads
   // the split's last one and ignores it): a conditional load would make the
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   if (tid < 16 * G) {
     // q' = B Hn q (the 1/sqrt(128) rides in the block matrices)
     float m[32];
-    so4_matrices_row(rp, m);
-    wht128_row(xq, pl);
+    so4_matrices_row(a.rot_kind, rp, m);
+    if (a.rot_kind == kRotWhtSo4) wht128_row(xq, pl);
     so4_apply_row<false>(xq, m);
     float mx = 0.f;
 #pragma unroll
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   const int live = live_splits(nblk, a.blocks_per_split, a.n_splits);
 
   float rp[16];
-  if (kRotate && tid < 16) load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, tid, rp);
+  if (kRotate && tid < 16) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid, rp);
   const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.n_splits * kRec;
   float mx = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   }
   reinterpret_cast<float4*>(ro[row])[d4] = o;
   float m[32];
-  if (kRotate && tid < 16) so4_matrices_row(rp, m);
+  if (kRotate && tid < 16) so4_matrices_row(a.rot_kind, rp, m);
   __syncthreads();
   {
     // half-wave: lane = row (0..31), dims 4 c .. 4 c + 3 with c = tid / 32
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
     for (int i = 0; i < 8; ++i) x[i] = fin[8 * tid + i];
     if (kRotate) {
       so4_apply_row<true>(x, m);
-      wht128_row(x, tid);
+      if (a.rot_kind == kRotWhtSo4) wht128_row(x, tid);
     }
     float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + 8 * tid);
     dst[0] = ok ? make_float4(x[0], x[1], x[2], x[3]) : make_float4(NAN, NAN, NAN, NAN);
@@ -525,7 +525,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{a.rot, a.seq_start, a.seq_len, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group,
+  MergeArgs m{a.rot_kind, a.rot, a.seq_start, a.seq_len, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group,
               a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits};
   return launch_merge(m, st);
 }

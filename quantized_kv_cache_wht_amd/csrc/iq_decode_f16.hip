@@ -352,7 +352,7 @@ hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{nullptr, a.seq_start, a.seq_len, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group,
+  MergeArgs m{kRotWhtSo4, nullptr, a.seq_start, a.seq_len, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group,
               a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits};
   return launch_merge(m, st);
 }

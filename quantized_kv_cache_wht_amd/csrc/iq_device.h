@@ -115,13 +115,72 @@ __device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m
   }
 }
 
-// Fill LDS with the 32 block matrices of one head (row-major, scaled by
-// 1/sqrt(128)). Must be called by all threads of the block; threads 0..31 work.
-__device__ __forceinline__ void load_head_matrices(const float* __restrict__ rot_head, float* sm) {
+// ------------------------------------------------- rotation kinds ----
+// (include/iq.h, iq_rotation) Every kind is applied as 32 block-diagonal 4x4
+// matrices, after the WHT for the first kind only:
+//   WHT + SO(4): qL (x) v (x) conj(qR) per block, scaled by 1/sqrt(128) (the
+//                WHT's normalisation), 8 parameters per block;
+//   ISO:         q (x) v per block (left-isoclinic), 4 parameters per block;
+//   PLANAR:      Givens (c, s) on dims (4b, 4b+1) and (4b+2, 4b+3), 4
+//                parameters per block (the 2x2 blocks of a 4x4 matrix).
+constexpr int kRotWhtSo4 = 0, kRotIso = 1, kRotPlanar = 2;
+
+__host__ __device__ constexpr int rot_params_per_block(int kind) { return kind == kRotWhtSo4 ? 8 : 4; }
+
+__device__ __forceinline__ const float* rot_of_head(const float* rot, int kind, int h) {
+  return rot + static_cast<size_t>(h) * kBlocks * rot_params_per_block(kind);
+}
+
+// Row-major matrix of v -> q (x) v from 4 stored parameters (q renormalised).
+__device__ __forceinline__ void iso_matrix(const float* p4, float m[16]) {
+  float q[4];
+  float nq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[i] = p4[i];
+    nq += q[i] * q[i];
+  }
+  nq = 1.0f / sqrtf(nq);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] *= nq;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float e[4] = {0.f, 0.f, 0.f, 0.f};
+    e[c] = 1.0f;
+    float col[4];
+    qmul(q, e, col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[r];
+  }
+}
+
+// Row-major matrix of two Givens rotations (c0, s0), (c1, s1) (each pair renormalised).
+__device__ __forceinline__ void givens_matrix(const float* p4, float m[16]) {
+  const float n0 = 1.0f / sqrtf(p4[0] * p4[0] + p4[1] * p4[1]);
+  const float n1 = 1.0f / sqrtf(p4[2] * p4[2] + p4[3] * p4[3]);
+  const float c0 = p4[0] * n0, s0 = p4[1] * n0, c1 = p4[2] * n1, s1 = p4[3] * n1;
+  const float r[16] = {c0, -s0, 0.f, 0.f, s0, c0, 0.f, 0.f, 0.f, 0.f, c1, -s1, 0.f, 0.f, s1, c1};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m[i] = r[i];
+}
+
+__device__ __forceinline__ void block_matrix(int kind, const float* p, float m[16]) {
+  if (kind == kRotIso) {
+    iso_matrix(p, m);
+  } else if (kind == kRotPlanar) {
+    givens_matrix(p, m);
+  } else {
+    so4_matrix(p, 0.08838834764831845f, m);   // 1/sqrt(128)
+  }
+}
+
+// Fill LDS with the 32 block matrices of one head (row-major). Must be called
+// by all threads of the block; threads 0..31 work.
+__device__ __forceinline__ void load_head_matrices(const float* __restrict__ rot_head, int kind, float* sm) {
   const int t = threadIdx.x;
   if (t < kBlocks) {
     float m[16];
-    so4_matrix(rot_head + t * 8, 0.08838834764831845f, m);   // 1/sqrt(128)
+    block_matrix(kind, rot_head + t * rot_params_per_block(kind), m);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sm[t * 16 + i] = m[i];
   }
@@ -219,11 +278,11 @@ __device__ __forceinline__ float row_norm(const float (&y)[8]) {
   return __double2float_rn(sqrt(s));
 }
 
-// Row-major matrices of the lane's two SO(4) blocks from their 16 stored
-// parameters, scaled by 1/sqrt(128).
-__device__ __forceinline__ void so4_matrices_row(const float (&p16)[16], float (&m)[32]) {
-  so4_matrix(p16, 0.08838834764831845f, m);
-  so4_matrix(p16 + 8, 0.08838834764831845f, m + 16);
+// Row-major matrices of the lane's two blocks from their stored parameters
+// (p16 as load_row_params leaves it).
+__device__ __forceinline__ void so4_matrices_row(int kind, const float (&p16)[16], float (&m)[32]) {
+  block_matrix(kind, p16, m);
+  block_matrix(kind, p16 + rot_params_per_block(kind), m + 16);
 }
 
 // y_b = M_b y_b (or M_b^T y_b) for the lane's two blocks.
@@ -244,12 +303,14 @@ __device__ __forceinline__ void so4_apply_row(float (&x)[8], const float (&m)[32
   }
 }
 
-// The 16 stored parameters of the lane's two blocks (four float4 loads).
-__device__ __forceinline__ void load_row_params(const float* rot_head, int p, float (&p16)[16]) {
-  const float4* r = reinterpret_cast<const float4*>(rot_head + 16 * p);
+// The stored parameters of the lane's two blocks: 16 floats (four float4
+// loads) for the WHT + SO(4) kind, 8 (two) for the others.
+__device__ __forceinline__ void load_row_params(const float* rot_head, int kind, int p, float (&p16)[16]) {
+  const int per = 2 * rot_params_per_block(kind);
+  const float4* r = reinterpret_cast<const float4*>(rot_head + per * p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float4 t = r[i];
+    const float4 t = (i < 2 || kind == kRotWhtSo4) ? r[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     p16[4 * i] = t.x; p16[4 * i + 1] = t.y; p16[4 * i + 2] = t.z; p16[4 * i + 3] = t.w;
   }
 }

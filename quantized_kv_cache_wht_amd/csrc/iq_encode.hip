@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
       }
     }
   }
-  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  load_head_matrices(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, sm);
   __syncthreads();
 
   for (; win < n_windows; win += gridDim.x) {
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     if (win != static_cast<int>(blockIdx.x)) {
       load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
     }
-    wht128_quad(x, part);
+    if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
     uint32_t w[3];
     const float n = quantize_pack_lane(x, a.cb, w);
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
                8 * p,
            ok, x);
   float rp[16];
-  load_row_params(a.rot + static_cast<size_t>(h) * kBlocks * 8, p, rp);
+  load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, p, rp);
   // V: this lane's dims 8p .. 8p+7 are the tile's dwords 6p .. 6p+5
   uint32_t* tile = reinterpret_cast<uint32_t*>(a.v_codes + (row / kTile) * kTileBytes) + 6 * p;
   uint32_t old[6] = {0u, 0u, 0u, 0u, 0u, 0u};
@@ -321,8 +321,8 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
   }
 
   float m[32];
-  so4_matrices_row(rp, m);
-  wht128_row(x, p);
+  so4_matrices_row(a.rot_kind, rp, m);
+  if (a.rot_kind == kRotWhtSo4) wht128_row(x, p);
   so4_apply_row<false>(x, m);
   const float n = row_norm(x);
   const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
@@ -368,14 +368,16 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Rotate fp32 vectors: y = B Hn x (forward) or x = Hn B^T y (inverse).
+// Rotate fp32 vectors: y = R x (forward) or x = R^-1 y (inverse); for the
+// WHT + SO(4) kind R = B Hn and R^-1 = Hn B^T.
 // grid = (token blocks, num_heads)
 template <bool kInverse>
 __global__ __launch_bounds__(kEncThreads) void rotate_kernel(RotateArgs a) {
   __shared__ __align__(16) float sm[kBlocks * 16];
   const int h = blockIdx.y;
-  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  load_head_matrices(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, sm);
   __syncthreads();
+  const bool wht = a.rot_kind == kRotWhtSo4;
   const int part = threadIdx.x & 3;
   const int vec = threadIdx.x >> 2;
   for (int tok0 = blockIdx.x * kVecPerBlock; tok0 < a.n_tokens; tok0 += gridDim.x * kVecPerBlock) {
@@ -386,9 +388,9 @@ __global__ __launch_bounds__(kEncThreads) void rotate_kernel(RotateArgs a) {
     load_vec<float>(a.x + off, ok, x);
     if (kInverse) {
       so4_apply_lane<true>(x, sm, part);
-      wht128_quad(x, part);
+      if (wht) wht128_quad(x, part);
     } else {
-      wht128_quad(x, part);
+      if (wht) wht128_quad(x, part);
       so4_apply_lane<false>(x, sm, part);
     }
     if (ok) store_vec<float>(a.y + off, x);
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
   const bool is_v = blockIdx.z != 0;
   T* __restrict__ out = static_cast<T*>(is_v ? a.v_out : a.k_out);
   if (out == nullptr) return;   // uniform across the block
-  load_head_matrices(a.rot + static_cast<size_t>(h) * kBlocks * 8, sm);
+  load_head_matrices(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, sm);
   __syncthreads();
   const uint8_t* __restrict__ codes = is_v ? a.v_codes : a.k_codes;
   const float* __restrict__ norms = is_v ? a.v_norms : a.k_norms;
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) x[i] = centroid(code_at(w, i), a.cb);
     so4_apply_lane<true>(x, sm, part);
-    wht128_quad(x, part);
+    if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) x[i] *= n;
     if (ok) store_vec<T>(out + (static_cast<size_t>(tok) * a.num_kv_heads + h) * kDim + part * kPerLane, x);

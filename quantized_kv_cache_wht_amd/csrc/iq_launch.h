@@ -9,6 +9,7 @@
 namespace iq {
 
 struct AppendArgs {
+  int32_t rot_kind;      // iq_rotation
   const void* k;
   const void* v;
   const int32_t* slots;
@@ -25,6 +26,7 @@ struct AppendArgs {
 };
 
 struct RotateArgs {
+  int32_t rot_kind;      // iq_rotation
   const float* x;
   float* y;
   const float* rot;
@@ -41,6 +43,7 @@ struct QuantArgs {
 };
 
 struct DequantArgs {
+  int32_t rot_kind;      // iq_rotation
   const uint8_t* k_codes;
   const uint8_t* v_codes;
   const float* k_norms;
@@ -56,6 +59,7 @@ struct DequantArgs {
 };
 
 struct DecodeArgs {
+  int32_t rot_kind;      // iq_rotation
   const uint8_t* k_codes;
   const uint8_t* v_codes;
   const float* k_norms;
@@ -104,6 +108,7 @@ struct F16DecodeArgs {
 // Split-K merge of either decode: rot = nullptr for records already in the
 // model's basis (fp16 cache), else the rotation whose inverse is applied once.
 struct MergeArgs {
+  int32_t rot_kind;      // iq_rotation
   const float* rot;
   const int32_t* seq_start;
   const int32_t* seq_len;

@@ -41,8 +41,8 @@ def test_status_strings():
     assert iq.status_string(-99) == "unknown status"
 
 
-def _view(head_dim=128, hkv=2, cap=128, ptr=0x10000):
-    return iq.CacheView(head_dim, hkv, cap, ptr, ptr + 0x1000, ptr + 0x2000, ptr + 0x3000, ptr + 0x4000)
+def _view(head_dim=128, hkv=2, cap=128, ptr=0x10000, rotation=0):
+    return iq.CacheView(head_dim, hkv, cap, ptr, ptr + 0x1000, ptr + 0x2000, ptr + 0x3000, ptr + 0x4000, rotation)
 
 
 def test_append_validation():
@@ -61,6 +61,8 @@ def test_append_validation():
     assert L.iq_rotate_quantize_append(ctypes.byref(v), p, p, 1, 0, 0, None, None) == 0       # no-op
     bad = _view(ptr=0x10008)                                                                # misaligned arrays
     assert L.iq_rotate_quantize_append(ctypes.byref(bad), p, p, 1, 4, 0, None, None) == -1
+    assert L.iq_rotate_quantize_append(ctypes.byref(_view(rotation=3)), p, p, 1, 4, 0, None, None) == -1
+    assert L.iq_rotate_quantize_append(ctypes.byref(_view(rotation=2)), p, p, 1, 0, 0, None, None) == 0
 
 
 def test_decode_validation():
@@ -109,11 +111,22 @@ def test_dequant_and_rotate_validation():
     assert L.iq_dequantize(ctypes.byref(v), 120, 20, 0, p, p, None) == -3
     assert L.iq_dequantize(ctypes.byref(v), 0, 20, 3, p, p, None) == -1
     assert L.iq_dequantize(ctypes.byref(v), 0, 20, 0, None, None, None) == 0
-    assert L.iq_rotate(None, 1, p, p, 4, 0, None) == -1
-    assert L.iq_rotate(p, 1, p, p, 4, 2, None) == -1
-    assert L.iq_rotate(p, 0, p, p, 4, 0, None) == -1
+    assert L.iq_rotate(None, 0, 1, p, p, 4, 0, None) == -1
+    assert L.iq_rotate(p, 0, 1, p, p, 4, 2, None) == -1
+    assert L.iq_rotate(p, 0, 0, p, p, 4, 0, None) == -1
+    assert L.iq_rotate(p, 3, 1, p, p, 4, 0, None) == -1        # unknown rotation kind
+    assert L.iq_rotate(p, 2, 1, p, p, 0, 0, None) == 0
     assert L.iq_quantize_pack(p, -1, p, p, None) == -1
     assert L.iq_quantize_pack(p, 0, p, p, None) == 0
+
+
+def test_binding_rotation_kinds_follow_parameter_shapes():
+    import torch
+    assert iq.rotation_kind(torch.zeros(3, 32, 8)) == iq.IQ_ROT_WHT_SO4
+    assert iq.rotation_kind(torch.zeros(3, 32, 4)) == iq.IQ_ROT_ISO
+    assert iq.rotation_kind(torch.zeros(3, 64, 2)) == iq.IQ_ROT_PLANAR
+    with pytest.raises(ValueError):
+        iq.rotation_kind(torch.zeros(3, 16, 8))
 
 
 def test_binding_refuses_host_tensors():

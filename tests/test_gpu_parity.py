@@ -23,9 +23,10 @@ from parity_util import C32, T32, SCALE, DEV, _t, _np, _assert_attention_close, 
 
 
 # ------------------------------------------------------------- rotation ----
+@pytest.mark.parametrize("kind", iqinputs.ROTATION_KINDS)
 @pytest.mark.parametrize("n_tok,heads", [(1, 1), (300, 3), (4096, 8)])
-def test_rotate_matches_oracle(n_tok, heads):
-    rot = iqinputs.rotation_params(101, n_tok, heads)
+def test_rotate_matches_oracle(n_tok, heads, kind):
+    rot = iqinputs.rotation_params_kind(101, n_tok, heads, kind)
     x = np.random.default_rng(n_tok).standard_normal((n_tok, heads, 128)).astype(np.float32) * 5
     y = _np(iq.iq_rotate(_t(rot), _t(x)))
     ref = np.stack([R.rotate(x[:, h].astype(np.float64), rot[h]) for h in range(heads)], axis=1)
@@ -171,10 +172,10 @@ def test_dequantize_matches_oracle(out_dtype):
 
 
 # ---------------------------------------------------------------- decode ----
-def _oracle_cache(seed, hkv, total, outliers="student_t6", dtype="f16"):
+def _oracle_cache(seed, hkv, total, outliers="student_t6", dtype="f16", kind="wht_so4"):
     """Oracle-encoded cache of ``total`` slots rounded up to a multiple of 32 (padding slots encode zeros)."""
     cap = -(-max(total, 1) // 32) * 32
-    rot = iqinputs.rotation_params(seed, 0, hkv)
+    rot = iqinputs.rotation_params_kind(seed, 0, hkv, kind)
     k = np.zeros((cap, hkv, 128), np.float16 if dtype == "f16" else np.float32)
     v = np.zeros_like(k)
     k[:total] = iqinputs.kv(seed, 0, "k", total, hkv, outliers, dtype)
@@ -274,3 +275,53 @@ def test_single_head_workload_end_to_end():
     vr, vn = R.encode_tokens_v(inp["v"], inp["rot"], T32)
     ref = R.decode_attention(inp["q"], kr, kn, vr, vn, inp["rot"], inp["seq_start"], inp["seq_len"], SCALE, C32)
     _assert_attention_close(out, ref, "single_head_t512 end to end")
+
+
+# ------------------------------------------------------ rotation variants ----
+@pytest.mark.parametrize("kind", ["iso", "planar"])
+@pytest.mark.parametrize("n_tok,first", [(700, 13), (1, 500), (40, 21)])   # bulk and short appends
+def test_append_variants_match_oracle(kind, n_tok, first):
+    hkv = 4
+    rot = iqinputs.rotation_params_kind(17, 0, hkv, kind)
+    k = iqinputs.kv(17, 0, "k", n_tok, hkv, "fixed_x8", "f16")
+    v = iqinputs.kv(17, 0, "v", n_tok, hkv, "fixed_x8", "f16")
+    cache = iq.PackedKVCache.allocate(hkv, first + n_tok, _t(rot))
+    iq.iq_rotate_quantize_append(cache, _t(k), _t(v), first_slot=first)
+    for name, x, unpack in (("k", k, R.unpack), ("v", v, R.unpack_tiles)):
+        codes_ref, n_ref, y_ref = _encode_ref(x, rot)
+        got = unpack(_np(getattr(cache, f"{name}_codes")))
+        _boundary_mismatch_ok(got[:, first:first + n_tok], codes_ref, y_ref, n_ref)
+        norms = _np(getattr(cache, f"{name}_norms"))[:, first:first + n_tok]
+        assert np.max(np.abs(norms - n_ref) / n_ref) < 2e-6
+
+
+@pytest.mark.parametrize("kind", ["iso", "planar"])
+@pytest.mark.parametrize("hq,hkv,lens", [(32, 4, [2100]), (8, 2, [0, 700, 1300]), (32, 8, [13, 4096])])
+def test_decode_variants_match_oracle(kind, hq, hkv, lens):
+    lens = np.array(lens, np.int32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    rot, kr, kn, vr, vn = _oracle_cache(hq * 7 + hkv, hkv, int(lens.sum()) + 3, kind=kind)
+    cache = _upload(rot, kr, kn, vr, vn)
+    q = iqinputs.queries(hq, 2, len(lens), hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), int(lens.max())))
+    ref = R.decode_attention(q, kr, kn, vr, vn, rot, starts, lens, SCALE, C32)
+    _assert_attention_close(out, ref, f"{kind} hq={hq} hkv={hkv} lens={list(lens)}")
+
+
+@pytest.mark.parametrize("kind", ["iso", "planar"])
+def test_dequantize_variants_match_oracle(kind):
+    hkv, n = 2, 256
+    rot = iqinputs.rotation_params_kind(23, 0, hkv, kind)
+    x = iqinputs.kv(23, 0, "k", n, hkv, "fixed_x8", "f32")
+    codes, norms = R.encode_codes(x, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, n, _t(rot))
+    cache.k_codes.copy_(_t(R.pack(codes)))
+    cache.v_codes.copy_(_t(R.pack_tiles(codes)))
+    cache.k_norms.copy_(_t(norms))
+    cache.v_norms.copy_(_t(norms))
+    k_out, v_out = iq.iq_dequantize(cache, 0, n)
+    k_out, v_out = _np(k_out).astype(np.float64), _np(v_out).astype(np.float64)
+    for h in range(hkv):
+        ref = R.dequantize_codes(codes[h], norms[h], rot[h], C32)
+        assert np.max(np.abs(k_out[:, h] - ref) / norms[h, :, None]) < 2e-6
+        assert np.max(np.abs(v_out[:, h] - ref) / norms[h, :, None]) < 2e-6
