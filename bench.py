@@ -121,15 +121,47 @@ def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, 
                                    workspace=ws, stream=stream)
 
     n = 4 * n_layers
+    variants = rotation_variants(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
     r = {"layers_cycled": n_layers,
          "fused_packed_decode_us": round(fused_us, 3),
          "fused_packed_bytes_per_launch": hkv * T * 2 * ROW_BYTES,
          "fp16_kv_decode_us": round(time_per_call(torch, fp16_decode, n, stream), 3),
          "fp16_kv_bytes_per_launch": hkv * T * 2 * 256,
          "dequantize_to_fp16_us": round(time_per_call(torch, dequantize, n, stream), 3),
-         "unfused_decode_us": round(time_per_call(torch, unfused, n, stream), 3)}
+         "unfused_decode_us": round(time_per_call(torch, unfused, n, stream), 3),
+         "rotation_variants": variants}
     del k16, v16, dk, dv
     return r
+
+
+def rotation_variants(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, n_layers=24):
+    """Decode and one-token append per rotation kind, each over n_layers caches of this workload's
+    shape (more bytes than the last-level cache holds), the default kind's being the main caches."""
+    import torch
+    import iqinputs
+    res = {}
+    for kind in iqinputs.ROTATION_KINDS:
+        if kind == "wht_so4":
+            cs = caches[:n_layers]
+        else:
+            cs = []
+            for l in range(n_layers):
+                rot = torch.from_numpy(iqinputs.rotation_params_kind(7, l, hkv, kind)).to(caches[0].k_codes.device)
+                c = iq.PackedKVCache.allocate(hkv, T, rot, device=rot.device)
+                iq.iq_rotate_quantize_append(c, synth_kv(T, 50_000 + l), synth_kv(T, 60_000 + l), first_slot=0,
+                                             stream=stream)
+                cs.append(c)
+        k1, v1 = synth_kv(1, 70_000), synth_kv(1, 70_001)
+
+        def dec(i, cs=cs):
+            l = i % n_layers
+            iq.iq_decode_attention(cs[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
+
+        def app(i, cs=cs):
+            iq.iq_rotate_quantize_append(cs[i % n_layers], k1, v1, first_slot=T - 1, stream=stream)
+        res[kind] = {"decode_us": round(time_per_call(torch, dec, 2 * n_layers, stream), 3),
+                     "append_1_token_us": round(time_per_call(torch, app, 2 * n_layers, stream), 3)}
+    return res
 
 
 def cpu_baseline(w, budget_s: float):
