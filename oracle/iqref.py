@@ -407,6 +407,33 @@ def decode_attention(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_l
     return out
 
 
+def decode_attention_deferred(q, k16, v16, prefix_start, prefix_len, k_rows, k_norms, v_tiles, v_norms, rot,
+                              seq_start, seq_len, scale, centroids32):
+    """Decode attention over a cache whose first tokens stayed fp16 (deferred
+    quantization: [RQ-blurb] "延迟量化策略"; [TQ-essay] "延迟量化"), float64.
+
+    Sequence s attends to its fp16 prefix k16/v16 [rows][Hkv][128], rows
+    prefix_start[s] .. + prefix_len[s], followed by its packed suffix, cache
+    slots seq_start[s] .. + seq_len[s], dequantized explicitly. Plain softmax
+    attention over the concatenation.
+    """
+    n_seqs, hq, _ = q.shape
+    hkv = k_rows.shape[0]
+    g = hq // hkv
+    out = np.zeros((n_seqs, hq, D))
+    for s in range(n_seqs):
+        pa, pn = int(prefix_start[s]), int(prefix_len[s])
+        a, n = int(seq_start[s]), int(seq_len[s])
+        for h in range(hkv):
+            kh = np.concatenate([np.asarray(k16[pa:pa + pn, h], np.float64),
+                                 dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], centroids32)])
+            vh = np.concatenate([np.asarray(v16[pa:pa + pn, h], np.float64),
+                                 dequantize_codes(v_codes_range(v_tiles[h], a, n), v_norms[h, a:a + n], rot[h],
+                                                  centroids32)])
+            out[s, h * g:(h + 1) * g] = attention(q[s, h * g:(h + 1) * g], kh, vh, scale)
+    return out
+
+
 def decode_attention_rotated(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_len, scale,
                              centroids32):
     """The packed-domain algorithm, step by step in float64 ([RQ-news], [RQ-abs]).

@@ -435,6 +435,36 @@ def test_attention_special_cases(codebook):
     assert np.allclose(R.softmax(s), scipy.special.softmax(s, axis=-1), atol=1e-15)
 
 
+def test_deferred_attention_reduces_to_its_parts(codebook):
+    """fp16 prefix + packed suffix: with no prefix it is the packed decode, with no suffix
+    plain attention over the fp16 rows, and in general brute force over the concatenation."""
+    c32 = codebook[0]
+    q, kr, kn, vr, vn, rot, st, ln = _small_cache(codebook, n_tok=304, lens=(120, 0, 1, 179))
+    g = np.random.default_rng(21)
+    k16 = g.standard_normal((90, 2, 128)).astype(np.float16)
+    v16 = g.standard_normal((90, 2, 128)).astype(np.float16)
+    scale = 1 / math.sqrt(128)
+    pst = np.array([0, 10, 50, 70], np.int32)
+    none = np.zeros(4, np.int32)
+    assert np.allclose(R.decode_attention_deferred(q, k16, v16, pst, none, kr, kn, vr, vn, rot, st, ln, scale, c32),
+                       R.decode_attention(q, kr, kn, vr, vn, rot, st, ln, scale, c32), atol=1e-13)
+    pln = np.array([10, 40, 20, 20], np.int32)
+    only = R.decode_attention_deferred(q, k16, v16, pst, pln, kr, kn, vr, vn, rot, st, none, scale, c32)
+    for s in range(4):
+        for h in range(2):
+            sl = slice(pst[s], pst[s] + pln[s])
+            ref = scipy.special.softmax(scale * q[s, 2 * h:2 * h + 2].astype(np.float64)
+                                        @ k16[sl, h].astype(np.float64).T, axis=-1) @ v16[sl, h].astype(np.float64)
+            assert np.allclose(only[s, 2 * h:2 * h + 2], ref, atol=1e-13)
+    both = R.decode_attention_deferred(q, k16, v16, pst, pln, kr, kn, vr, vn, rot, st, ln, scale, c32)
+    s, h = 3, 1
+    kh = np.concatenate([k16[70:90, h].astype(np.float64), R.dequantize(kr[h, 121:300], kn[h, 121:300], rot[h], c32)])
+    vh = np.concatenate([v16[70:90, h].astype(np.float64),
+                         R.dequantize_codes(R.unpack_tiles(vr[h])[121:300], vn[h, 121:300], rot[h], c32)])
+    w = scipy.special.softmax(scale * q[s, 2:4].astype(np.float64) @ kh.T, axis=-1)
+    assert np.allclose(both[s, 2:4], w @ vh, atol=1e-13)
+
+
 def test_needle_is_recovered(codebook):
     """A key planted as 4x the query wins the attention (moe30b shape, shortened)."""
     c32, t32, _ = codebook
