@@ -200,6 +200,35 @@ IQ_API iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t t
                                   int32_t max_seq_len, float scale, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace iq_decode_attention_deferred needs (0 if invalid). */
+IQ_API size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t max_prefix_len, int32_t max_seq_len);
+
+/* Decode attention over a deferred-quantization cache (sd114.wiki RotorQuant
+ * page, deferred-quantization strategy; zhichai.net essay, section
+ * "延迟量化"): the prompt's K/V stay fp16, tokens added later are packed.
+ * Sequence s attends to its fp16 prefix followed by its packed suffix:
+ *   view, seq_start, seq_len, max_seq_len: the packed suffix, as for
+ *                 iq_decode_attention (seq_len may be 0).
+ *   k16, v16, token_stride, head_stride, capacity16: the fp16 prefix cache,
+ *                 as for iq_decode_attention_f16; it shares the view's KV
+ *                 heads (and its rotation, which the prefix's partial results
+ *                 are rotated by so that both merge in one basis).
+ *   prefix_start, prefix_len (device int32 [n_seqs]), max_prefix_len: the
+ *                 prefix rows of each sequence (prefix_len may be 0).
+ *   q, num_q_heads, n_seqs, scale, out: as for iq_decode_attention.
+ *   workspace     at least iq_decode_deferred_workspace_bytes() bytes,
+ *                 16-byte aligned.
+ * A sequence with no tokens gets 0; one whose prefix or suffix rows are
+ * invalid gets NaN. */
+IQ_API iq_status iq_decode_attention_deferred(const iq_cache_view* view, const int32_t* seq_start,
+                                       const int32_t* seq_len, int32_t max_seq_len, const void* k16,
+                                       const void* v16, int64_t token_stride, int64_t head_stride,
+                                       int32_t capacity16, const int32_t* prefix_start, const int32_t* prefix_len,
+                                       int32_t max_prefix_len, const float* q, int32_t num_q_heads, int32_t n_seqs,
+                                       float scale, float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -85,6 +85,14 @@ _SIGNATURES = {
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p]),
+    "iq_decode_deferred_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                             ctypes.c_int32, ctypes.c_int32]),
+    "iq_decode_attention_deferred": (ctypes.c_int, [ctypes.POINTER(CacheView), ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_size_t, ctypes.c_void_p]),
     "iq_decode_attention_f16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -313,4 +321,53 @@ def iq_decode_attention_f16(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, s
                                          _dev(seq_len, torch.int32, "seq_len"), n_seqs, max_seq_len, scale,
                                          _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
                                          workspace.numel(), _stream(stream)))
+    return out
+
+
+def _f16_strides(k: torch.Tensor, v: torch.Tensor, token_major: bool):
+    if k.shape != v.shape or k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError("k and v must be matching [.., .., 128] tensors")
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, torch.float16, name)
+    if token_major:
+        cap, hkv = k.shape[0], k.shape[1]
+        return cap, hkv, hkv * HEAD_DIM, HEAD_DIM
+    hkv, cap = k.shape[0], k.shape[1]
+    return cap, hkv, HEAD_DIM, cap * HEAD_DIM
+
+
+def iq_decode_deferred_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, max_prefix_len: int,
+                                       max_seq_len: int) -> int:
+    return int(lib().iq_decode_deferred_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, max_prefix_len,
+                                                        max_seq_len))
+
+
+def iq_decode_attention_deferred(cache: PackedKVCache, seq_start: torch.Tensor, seq_len: torch.Tensor,
+                                 max_seq_len: int, k16: torch.Tensor, v16: torch.Tensor, prefix_start: torch.Tensor,
+                                 prefix_len: torch.Tensor, max_prefix_len: int, q: torch.Tensor,
+                                 token_major: bool = True, scale: float | None = None,
+                                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                 stream=None) -> torch.Tensor:
+    """Decode over an fp16 prefix (k16/v16, layout as for iq_decode_attention_f16) followed by the
+    packed suffix in ``cache``."""
+    cap16, hkv, ts, hs = _f16_strides(k16, v16, token_major)
+    if hkv != cache.num_kv_heads:
+        raise ValueError("the fp16 prefix and the packed cache must have the same KV heads")
+    n_seqs, hq, _ = q.shape
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        need = iq_decode_deferred_workspace_bytes(n_seqs, hq, hkv, max_prefix_len, max_seq_len)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    view = cache.view()
+    _check("iq_decode_attention_deferred",
+           lib().iq_decode_attention_deferred(ctypes.byref(view), _dev(seq_start, torch.int32, "seq_start"),
+                                              _dev(seq_len, torch.int32, "seq_len"), max_seq_len, k16.data_ptr(),
+                                              v16.data_ptr(), ts, hs, cap16,
+                                              _dev(prefix_start, torch.int32, "prefix_start"),
+                                              _dev(prefix_len, torch.int32, "prefix_len"), max_prefix_len,
+                                              _dev(q, torch.float32, "q"), hq, n_seqs, scale,
+                                              _dev(out, torch.float32, "out"),
+                                              _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                              _stream(stream)))
     return out

@@ -223,6 +223,8 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   a.max_seq_len = max_seq_len;
   a.blocks_per_split = plan.blocks_per_split;
   a.n_splits = plan.n_splits;
+  a.rec_offset = 0;
+  a.rec_splits = plan.n_splits;
   a.qscale = scale * 1.4426950408889634f;   // log2(e): scores kept in base 2
   a.cb = codebook();
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));
@@ -265,8 +267,97 @@ iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t token_st
   a.max_seq_len = max_seq_len;
   a.blocks_per_split = plan.blocks_per_split;
   a.n_splits = plan.n_splits;
+  a.rec_offset = 0;
+  a.rec_splits = plan.n_splits;
   a.qscale = scale * 1.4426950408889634f;
   return hip_status(launch_decode_f16(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t max_prefix_len, int32_t max_seq_len) {
+  if (n_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_prefix_len < 0 || max_seq_len < 0) return 0;
+  const DecodePlan pre = decode_plan(n_seqs, num_kv_heads, max_prefix_len);
+  const DecodePlan suf = decode_plan(n_seqs, num_kv_heads, max_seq_len);
+  return static_cast<size_t>(n_seqs) * num_q_heads * (pre.n_splits + suf.n_splits) * 132 * sizeof(float);
+}
+
+iq_status iq_decode_attention_deferred(const iq_cache_view* view, const int32_t* seq_start, const int32_t* seq_len,
+                                       int32_t max_seq_len, const void* k16, const void* v16, int64_t token_stride,
+                                       int64_t head_stride, int32_t capacity16, const int32_t* prefix_start,
+                                       const int32_t* prefix_len, int32_t max_prefix_len, const float* q,
+                                       int32_t num_q_heads, int32_t n_seqs, float scale, float* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  iq_status st = check_view(view);
+  if (st != IQ_OK) return st;
+  const int32_t hkv = view->num_kv_heads;
+  if (capacity16 < 0 || (capacity16 % 32) != 0) return IQ_ERR_INVALID_ARG;
+  if (token_stride <= 0 || head_stride < 0 || (token_stride % 8) != 0 || (head_stride % 8) != 0)
+    return IQ_ERR_INVALID_ARG;
+  if (n_seqs < 0 || max_seq_len < 0 || max_prefix_len < 0 || num_q_heads < 1) return IQ_ERR_INVALID_ARG;
+  if (num_q_heads % hkv != 0) return IQ_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / hkv;
+  if (!group_supported(group)) return IQ_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return IQ_OK;
+  if (!k16 || !v16 || !prefix_start || !prefix_len || !q || !seq_start || !seq_len || !out || !workspace)
+    return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k16) | reinterpret_cast<uintptr_t>(v16) | reinterpret_cast<uintptr_t>(workspace)) &
+      15u)
+    return IQ_ERR_INVALID_ARG;
+  if (n_seqs > 65535 || hkv > 65535) return IQ_ERR_UNSUPPORTED;
+  const DecodePlan pp = decode_plan(n_seqs, hkv, max_prefix_len);
+  const DecodePlan sp = decode_plan(n_seqs, hkv, max_seq_len);
+  if (workspace_bytes < iq_decode_deferred_workspace_bytes(n_seqs, num_q_heads, hkv, max_prefix_len, max_seq_len))
+    return IQ_ERR_WORKSPACE;
+  const int32_t total = pp.n_splits + sp.n_splits;
+  const float qscale = scale * 1.4426950408889634f;
+  F16DecodeArgs pre{};
+  pre.rot_kind = view->rotation;
+  pre.rot = view->rot;
+  pre.k = static_cast<const _Float16*>(k16);
+  pre.v = static_cast<const _Float16*>(v16);
+  pre.token_stride = token_stride;
+  pre.head_stride = head_stride;
+  pre.q = q;
+  pre.seq_start = prefix_start;
+  pre.seq_len = prefix_len;
+  pre.out = out;
+  pre.ws = static_cast<float*>(workspace);
+  pre.n_seqs = n_seqs;
+  pre.num_q_heads = num_q_heads;
+  pre.num_kv_heads = hkv;
+  pre.group = group;
+  pre.capacity = capacity16;
+  pre.max_seq_len = max_prefix_len;
+  pre.blocks_per_split = pp.blocks_per_split;
+  pre.n_splits = pp.n_splits;
+  pre.rec_offset = 0;
+  pre.rec_splits = total;
+  pre.qscale = qscale;
+  DecodeArgs suf{};
+  suf.k_codes = view->k_codes;
+  suf.v_codes = view->v_codes;
+  suf.k_norms = view->k_norms;
+  suf.v_norms = view->v_norms;
+  suf.rot = view->rot;
+  suf.rot_kind = view->rotation;
+  suf.q = q;
+  suf.seq_start = seq_start;
+  suf.seq_len = seq_len;
+  suf.out = out;
+  suf.ws = static_cast<float*>(workspace);
+  suf.n_seqs = n_seqs;
+  suf.num_q_heads = num_q_heads;
+  suf.num_kv_heads = hkv;
+  suf.group = group;
+  suf.capacity = view->capacity;
+  suf.max_seq_len = max_seq_len;
+  suf.blocks_per_split = sp.blocks_per_split;
+  suf.n_splits = sp.n_splits;
+  suf.rec_offset = pp.n_splits;
+  suf.rec_splits = total;
+  suf.qscale = qscale;
+  suf.cb = codebook();
+  return hip_status(launch_decode_deferred(pre, suf, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

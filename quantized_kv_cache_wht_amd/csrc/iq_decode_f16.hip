@@ -17,6 +17,7 @@
 //     lane, so each wave writes its V block to LDS transposed (dim-major,
 //     rows padded to 72 bytes against bank conflicts) and reads it back.
 #include "iq_decode_common.h"
+#include "iq_decode_packed.h"
 
 namespace iq {
 
@@ -181,22 +182,37 @@ __device__ __forceinline__ void f16_softmax_pv(floatx4 d0, floatx4 d1, const _Fl
   }
 }
 
+// LDS of one fp16 split work-group.
 template <int G>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16DecodeArgs a) {
-  constexpr bool kSplitN = (G <= 8);
+struct F16Smem {
+  static constexpr bool kSplitN = (G <= 8);
+  static constexpr int kRows = kSplitN ? 2 * G : G;
+  // per wave: the transposed V block during the loop, then the wave's accumulator rows
+  _Float16 vts[kWaves][kVtWave];
   // query operand of k-step kk for lane 16 q + n: dims 32 kk + 8 q .. +7 of head
   // n & 7, hi halves in columns n < 8 and lo halves in n >= 8 (G = 16: hi in qop,
   // lo in qop_lo, column n = head n)
-  __shared__ __align__(16) uint4 qop[4][64];
-  __shared__ __align__(16) uint4 qop_lo[kSplitN ? 1 : 4][64];
-  __shared__ float qmax[G];
-  constexpr int kRows = kSplitN ? 2 * G : G;
-  __shared__ float wm[kWaves][G], wl[kWaves][G];
-  // per wave: the transposed V block during the loop, then the wave's accumulator rows
+  uint4 qop[4][64];
+  uint4 qop_lo[kSplitN ? 1 : 4][64];
+  float orec[G][kDim];   // merged output before the forward rotation (deferred decode)
+  float qmax[G];
+  float wm[kWaves][G], wl[kWaves][G];
   static_assert(kRows * kDim * sizeof(float) <= kVtWave * sizeof(_Float16), "accumulators fit the V block");
-  __shared__ __align__(16) _Float16 vts[kWaves][kVtWave];
+};
 
-  const int h = blockIdx.x, s = blockIdx.y, split = blockIdx.z;
+// One split of the fp16 decode: work-group (h = KV head, s = sequence, split).
+// Records go to split index a.rec_offset + split of a.rec_splits; with a.rot
+// they are rotated forward (o' = R o) so that they merge with packed records.
+template <int G>
+__device__ __forceinline__ void f16_split(const F16DecodeArgs& a, F16Smem<G>& sm, int split) {
+  constexpr bool kSplitN = F16Smem<G>::kSplitN;
+  auto& qop = sm.qop;
+  auto& qop_lo = sm.qop_lo;
+  float* qmax = sm.qmax;
+  auto& wm = sm.wm;
+  auto& wl = sm.wl;
+  auto& vts = sm.vts;
+  const int h = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, q = lane >> 4;
   int start, len;
@@ -211,12 +227,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16Dec
 
   // query loads (16 lanes per head, 8 dims each) first, then the wave's first block
   const int pg = tid >> 4, pl = tid & 15;
-  float xq[8];
+  float xq[8], rp[16];
   if (tid < 16 * G) {
     const float4* src = reinterpret_cast<const float4*>(
         a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + pg) * kDim + 8 * pl);
     const float4 v0 = src[0], v1 = src[1];
     xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w; xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
+    if (a.rot != nullptr) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, pl, rp);
   }
   int b = b_begin + wave;
   F16Block cur;
@@ -305,8 +322,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16Dec
   }
   __syncthreads();
   // ---- merge the waves (and the hi/lo rows) into this split's records ----
-  float* rec0 = a.ws + ((static_cast<size_t>(s) * a.num_q_heads + h * G) * a.n_splits + split) * kRec;
-  const size_t head_stride = static_cast<size_t>(a.n_splits) * kRec;
+  float* rec0 = a.ws + ((static_cast<size_t>(s) * a.num_q_heads + h * G) * a.rec_splits + a.rec_offset + split) * kRec;
+  const size_t head_stride = static_cast<size_t>(a.rec_splits) * kRec;
+  const bool rotate = a.rot != nullptr;
   for (int idx = tid; idx < G * kDim; idx += kDecThreads) {
     const int gr = idx >> 7, j = idx & (kDim - 1);
     float mx = -INFINITY;
@@ -321,7 +339,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16Dec
         o += fast_exp2(wm[w][gr] - mx) * v;
       }
     }
-    rec0[gr * head_stride + 4 + j] = o;
+    if (rotate) {
+      sm.orec[gr][j] = o;
+    } else {
+      rec0[gr * head_stride + 4 + j] = o;
+    }
   }
   if (tid < G) {
     float mx = -INFINITY;
@@ -336,9 +358,69 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16Dec
     r[0] = mx;
     r[1] = l;
   }
+  if (rotate) {
+    // o' = R o per query head, 16 lanes per head (R linear: the unnormalised sum rotates)
+    __syncthreads();
+    if (tid < 16 * G) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = sm.orec[pg][8 * pl + i];
+      float m[32];
+      so4_matrices_row(a.rot_kind, rp, m);
+      if (a.rot_kind == kRotWhtSo4) wht128_row(x, pl);
+      so4_apply_row<false>(x, m);
+      float4* dst = reinterpret_cast<float4*>(rec0 + pg * head_stride + 4 + 8 * pl);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16DecodeArgs a) {
+  __shared__ F16Smem<G> sm;
+  f16_split<G>(a, sm, blockIdx.z);
+}
+
+// Deferred quantization (RotorQuant page, deferred-quantization strategy;
+// essay section "延迟量化"): the prompt's K/V stay fp16, generated tokens are
+// packed. One launch holds both parts' splits, the prefix's first (grid z <
+// pre.n_splits); their records meet in one merge.
+template <int G>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_deferred_split_kernel(F16DecodeArgs pre, DecodeArgs suf) {
+  __shared__ union {
+    F16Smem<G> f;
+    PackedSmem<G> p;
+  } sm;
+  const int z = blockIdx.z;
+  if (z < pre.n_splits) {
+    f16_split<G>(pre, sm.f, z);
+  } else {
+    packed_split<G>(suf, sm.p, z - pre.n_splits);
+  }
 }
 
 }  // namespace
+
+hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t st) {
+  dim3 grid(suf.num_kv_heads, suf.n_seqs, pre.n_splits + suf.n_splits);
+  switch (suf.group) {
+    case 1: hipLaunchKernelGGL(decode_deferred_split_kernel<1>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 2: hipLaunchKernelGGL(decode_deferred_split_kernel<2>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 4: hipLaunchKernelGGL(decode_deferred_split_kernel<4>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 8: hipLaunchKernelGGL(decode_deferred_split_kernel<8>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 16: hipLaunchKernelGGL(decode_deferred_split_kernel<16>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeArgs m{suf.rot_kind, suf.rot, suf.out, suf.ws, suf.n_seqs, suf.num_q_heads, suf.group, suf.rec_splits, 2, {}};
+  m.seg[0] = MergeSegment{pre.seq_start, pre.seq_len, pre.capacity, pre.max_seq_len, pre.blocks_per_split,
+                          pre.n_splits, 0};
+  m.seg[1] = MergeSegment{suf.seq_start, suf.seq_len, suf.capacity, suf.max_seq_len, suf.blocks_per_split,
+                          suf.n_splits, pre.n_splits};
+  return launch_merge(m, st);
+}
 
 hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.num_kv_heads, a.n_seqs, a.n_splits);
@@ -352,8 +434,8 @@ hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{kRotWhtSo4, nullptr, a.seq_start, a.seq_len, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group,
-              a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits};
+  MergeArgs m{kRotWhtSo4, nullptr, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, {}};
+  m.seg[0] = MergeSegment{a.seq_start, a.seq_len, a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits, 0};
   return launch_merge(m, st);
 }
 

@@ -78,6 +78,8 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t blocks_per_split;   // 32-slot blocks per split
   int32_t n_splits;           // splits per (seq, kv head) at max_seq_len
+  int32_t rec_offset;         // record index of split 0 ...
+  int32_t rec_splits;         // ... among this many records per (seq, query head)
   float qscale;               // softmax scale * log2(e)
   Codebook cb;
 };
@@ -85,6 +87,8 @@ struct DecodeArgs {
 // Decode over a plain fp16 K/V cache (the baseline and the unfused path):
 // element (token t, KV head h, dim j) at k[t * token_stride + h * head_stride + j].
 struct F16DecodeArgs {
+  int32_t rot_kind;          // with rot: records are rotated forward (deferred decode)
+  const float* rot;          // nullptr: records stay in the model's basis
   const _Float16* k;
   const _Float16* v;
   int64_t token_stride;
@@ -102,25 +106,38 @@ struct F16DecodeArgs {
   int32_t max_seq_len;
   int32_t blocks_per_split;
   int32_t n_splits;
+  int32_t rec_offset;
+  int32_t rec_splits;
   float qscale;
 };
 
-// Split-K merge of either decode: rot = nullptr for records already in the
-// model's basis (fp16 cache), else the rotation whose inverse is applied once.
+// One group of split records: the splits of a token range planned with its
+// own block count (records split_offset .. split_offset + n_splits - 1).
+struct MergeSegment {
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  int32_t capacity;
+  int32_t max_seq_len;
+  int32_t blocks_per_split;
+  int32_t n_splits;
+  int32_t split_offset;
+};
+
+// Split-K merge: rot = nullptr for records already in the model's basis (fp16
+// cache), else the rotation whose inverse is applied once. Records of
+// (seq, query head) are rec_splits apart; 1 or 2 segments (deferred decode:
+// the fp16 prefix's splits, then the packed suffix's).
 struct MergeArgs {
   int32_t rot_kind;      // iq_rotation
   const float* rot;
-  const int32_t* seq_start;
-  const int32_t* seq_len;
   float* out;
   const float* ws;
   int32_t n_seqs;
   int32_t num_q_heads;
   int32_t group;
-  int32_t capacity;
-  int32_t max_seq_len;
-  int32_t blocks_per_split;
-  int32_t n_splits;
+  int32_t rec_splits;
+  int32_t n_segments;
+  MergeSegment seg[2];
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s);
@@ -137,6 +154,8 @@ DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len
 size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodePlan& p);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t s);
+// fp16 prefix and packed suffix in one split launch, then the merge
+hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace iq

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     h = ctypes.CDLL(iq.library_path())
     for n in names:
         assert hasattr(h, n), n
@@ -102,6 +102,24 @@ def test_decode_f16_validation():
     assert call(k=None) == -1
     assert call(n=0) == 0
     assert call(hkv=0) == -1
+
+
+def test_decode_deferred_validation():
+    L = iq.lib()
+    v = _view(hkv=2)
+    p = ctypes.c_void_p(0x60000)
+    need = L.iq_decode_deferred_workspace_bytes(1, 8, 2, 300, 100)
+    assert need >= L.iq_decode_workspace_bytes(1, 8, 2, 100)
+
+    def call(hq=8, ws=need, cap16=320, ts=256, n=1):
+        return L.iq_decode_attention_deferred(ctypes.byref(v), p, p, 100, p, p, ts, 128, cap16, p, p, 300,
+                                              p, hq, n, 0.1, p, p, ws, None)
+    assert call(ws=need - 1) == -4
+    assert call(cap16=300) == -1
+    assert call(ts=4) == -1
+    assert call(hq=6) == -2
+    assert call(n=0) == 0
+    assert L.iq_decode_deferred_workspace_bytes(1, 8, 2, -1, 100) == 0
 
 
 def test_dequant_and_rotate_validation():

@@ -85,3 +85,37 @@ def test_unfused_path_matches_fused_and_oracle():
     _assert_attention_close(fused, ref, "fused packed decode")
     # the unfused path rounds the reconstruction to fp16 first: its error is that rounding's
     _assert_attention_close(unfused, ref, "unfused: dequantize to fp16 + fp16 decode")
+
+
+# ------------------------------------------------- deferred quantization ----
+@pytest.mark.parametrize("kind", ["wht_so4", "planar"])
+@pytest.mark.parametrize("pre,suf", [([700, 0, 33], [40, 1, 0]), ([0, 0], [300, 12]), ([2100], [0]),
+                                     ([3000, 5], [257, 64])])
+def test_deferred_decode_matches_oracle(kind, pre, suf):
+    hq, hkv = 32, 4
+    pre, suf = np.array(pre, np.int32), np.array(suf, np.int32)
+    n_seqs = len(pre)
+    pst = (np.concatenate([[0], np.cumsum(pre)[:-1]]) + 7).astype(np.int32)
+    sst = (np.concatenate([[0], np.cumsum(suf)[:-1]]) + 3).astype(np.int32)
+    cap16 = -(-(int(pst[-1] + pre[-1]) + 1) // 32) * 32
+    cap = -(-(int(sst[-1] + suf[-1]) + 1) // 32) * 32
+    seed = int(pre.sum() + suf.sum())
+    rot = iqinputs.rotation_params_kind(seed, 0, hkv, kind)
+    k16 = iqinputs.kv(seed, 1, "k", cap16, hkv, "student_t6", "f16")
+    v16 = iqinputs.kv(seed, 1, "v", cap16, hkv, "student_t6", "f16")
+    k = iqinputs.kv(seed, 2, "k", cap, hkv, "student_t6", "f16")
+    v = iqinputs.kv(seed, 2, "v", cap, hkv, "student_t6", "f16")
+    kr, kn = R.encode_tokens(k, rot, T32)
+    vt, vn = R.encode_tokens_v(v, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot))
+    cache.k_codes.copy_(_t(kr))
+    cache.v_codes.copy_(_t(vt))
+    cache.k_norms.copy_(_t(kn))
+    cache.v_norms.copy_(_t(vn))
+    q = iqinputs.queries(seed, 3, n_seqs, hq)
+    out = _np(iq.iq_decode_attention_deferred(cache, _t(sst), _t(suf), int(suf.max()), _t(k16), _t(v16), _t(pst),
+                                              _t(pre), int(pre.max()), _t(q)))
+    ref = R.decode_attention_deferred(q, k16, v16, pst, pre, kr, kn, vt, vn, rot, sst, suf, SCALE, C32)
+    _assert_attention_close(out, ref, f"deferred {kind} prefix={list(pre)} suffix={list(suf)}")
+    for s in np.nonzero((pre + suf) == 0)[0]:
+        assert np.all(out[s] == 0)
