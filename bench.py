@@ -55,7 +55,8 @@ def decode_source_digest() -> str:
     """sha256 over the sources of the decode kernels (the traffic figures belong to one version)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_wht_amd", "csrc")
-    for name in ("iq_decode.hip", "iq_decode_common.h", "iq_device.h", "iq_launch.h"):
+    for name in ("iq_decode.hip", "iq_decode_common.h", "iq_decode_packed.h", "iq_decode_packed_body.inc",
+                 "iq_device.h", "iq_launch.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

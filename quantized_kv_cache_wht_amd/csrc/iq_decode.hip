@@ -43,7 +43,8 @@ namespace iq {
 template <int G>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a) {
   __shared__ PackedSmem<G> sm;
-  packed_split<G>(a, sm, blockIdx.z);
+  const int split = blockIdx.z;
+#include "iq_decode_packed_body.inc"
 }
 
 // One work-group per (seq, query head): merges the live splits' records
@@ -62,7 +63,23 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   const int hq = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
   const int h = hq / a.group;
-  // live records of each segment; the merged list is segment 0's, then segment 1's
+  float rp[16];
+  if (kRotate && tid < 16) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid, rp);
+  // Record positions: segment 0 at [0, n_splits0), segment 1 (if any) from
+  // split_offset on. The first round of record loads goes out before the
+  // sequence bounds are read (two round trips would otherwise follow each
+  // other); records past a segment's live splits are stale and masked out.
+  const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.rec_splits * kRec;
+  float mv[kMergeChunk], lv[kMergeChunk];
+  float4 ov[kMergeChunk];
+#pragma unroll
+  for (int i = 0; i < kMergeChunk; ++i) {
+    const int p = row + i * kMergeRows;
+    const float* r = recs + static_cast<size_t>(p < a.rec_splits ? p : 0) * kRec;
+    mv[i] = r[0];
+    lv[i] = r[1];
+    ov[i] = reinterpret_cast<const float4*>(r + 4)[d4];
+  }
   bool ok = true;
   int live0 = 0, live1 = 0;
 #pragma unroll
@@ -75,25 +92,29 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
     const int live = live_splits(okg ? n_blocks(start, len) : 0, sg.blocks_per_split, sg.n_splits);
     if (g == 0) live0 = live; else live1 = live;
   }
-  const int live = live0 + live1;
-  const int off1 = a.n_segments > 1 ? a.seg[1].split_offset : 0;
-  float rp[16];
-  if (kRotate && tid < 16) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid, rp);
-  const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.rec_splits * kRec;
+  const int off1 = a.n_segments > 1 ? a.seg[1].split_offset : a.rec_splits;
+  auto live_at = [&](int p) { return p < live0 || (p >= off1 && p - off1 < live1); };
   float mx = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = row; k0 < live; k0 += kMergeRows * kMergeChunk) {
-    float mv[kMergeChunk], lv[kMergeChunk];
-    float4 ov[kMergeChunk];
+  for (int p0 = row;; p0 += kMergeRows * kMergeChunk) {
+    if (p0 != row) {
+      if (p0 >= a.rec_splits) break;
+#pragma unroll
+      for (int i = 0; i < kMergeChunk; ++i) {
+        const int p = p0 + i * kMergeRows;
+        const float* r = recs + static_cast<size_t>(p < a.rec_splits ? p : 0) * kRec;
+        mv[i] = r[0];
+        lv[i] = r[1];
+        ov[i] = reinterpret_cast<const float4*>(r + 4)[d4];
+      }
+    }
+    // selects, not products, so stale non-finite values cannot leak in
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i) {
-      const int k = k0 + i * kMergeRows;
-      const bool in = k < live;
-      const int rec = k < live0 ? k : off1 + (k - live0);
-      const float* r = recs + static_cast<size_t>(in ? rec : 0) * kRec;
-      mv[i] = in ? r[0] : -INFINITY;
-      lv[i] = in ? r[1] : 0.f;
-      ov[i] = in ? reinterpret_cast<const float4*>(r + 4)[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool in = live_at(p0 + i * kMergeRows);
+      mv[i] = in ? mv[i] : -INFINITY;
+      lv[i] = in ? lv[i] : 0.f;
+      ov[i] = in ? ov[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float cm = mx;
 #pragma unroll

@@ -191,190 +191,8 @@ struct PackedSmem {
 // split). Records go to split index a.rec_offset + split of a.rec_splits.
 template <int G>
 __device__ __forceinline__ void packed_split(const DecodeArgs& a, PackedSmem<G>& sm, int split) {
-  constexpr bool kSplitN = PackedSmem<G>::kSplitN;
-  constexpr int kRows = PackedSmem<G>::kRows;
-  uint2* lut = sm.lut;
-  auto& qop = sm.qop;
-  auto& qop_lo = sm.qop_lo;
-  float* qmax = sm.qmax;
-  auto& wm = sm.wm;
-  auto& wl = sm.wl;
-  auto& wo = sm.wo;
-  (void)kRows;
-  const int h = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 15, q = lane >> 4;
-  int start, len;
-  const bool ok = seq_ok(a, s, &start, &len);
-  const int base = start & ~(kBlk - 1);
-  const int nblk = ok ? n_blocks(start, len) : 0;
-  if (split >= live_splits(nblk, a.blocks_per_split, a.n_splits)) return;   // the merge skips this split
-  const int b_begin = split * a.blocks_per_split;
-  const int b_end = split == a.n_splits - 1 ? nblk : min(nblk, b_begin + a.blocks_per_split);
-  const size_t slot_base = static_cast<size_t>(h) * a.capacity + base;   // cache row of block 0, slot 0
+#include "iq_decode_packed_body.inc"
 
-  // This work-group's queries and rotation parameters (16 lanes per query
-  // head: 8 dims and 2 SO(4) blocks each) are requested first, then the wave's
-  // first two blocks: loads complete in order, so the query rotation below
-  // waits only for its own inputs while the blocks are still in flight.
-  const int pg = tid >> 4, pl = tid & 15;
-  float xq[8], rp[16];
-  if (tid < 16 * G) {
-    const float4* src = reinterpret_cast<const float4*>(
-        a.q + (static_cast<size_t>(s) * a.num_q_heads + h * G + pg) * kDim + 8 * pl);
-    const float4 v0 = src[0], v1 = src[1];
-    xq[0] = v0.x; xq[1] = v0.y; xq[2] = v0.z; xq[3] = v0.w; xq[4] = v1.x; xq[5] = v1.y; xq[6] = v1.z; xq[7] = v1.w;
-    load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, pl, rp);
-  }
-  // The two block loads are unconditional (a wave with fewer blocks re-reads
-  // the split's last one and ignores it): a conditional load would make the
-  // compiler's wait for the query inputs also wait for the blocks.
-  BlockData buf0, buf1;
-  int b = b_begin + wave;
-  load_block(a, slot_base, min(b, b_end - 1) * kBlk, n, q, buf0);
-  load_block(a, slot_base, min(b + kWaves, b_end - 1) * kBlk, n, q, buf1);
-
-  // ---- prologue: code-pair table, rotated queries ----
-  {
-    // thread t fills copies 4(t%4) .. 4(t%4)+3 of pair t/4
-    const uint32_t p = static_cast<uint32_t>(tid) >> 2, ca = p & 7u, cb = p >> 3;
-    const uint2 e = make_uint2(centroid_f16<false>(ca, a.cb) | (centroid_f16<true>(ca, a.cb) << 16),
-                               centroid_f16<false>(cb, a.cb) | (centroid_f16<true>(cb, a.cb) << 16));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) lut[p * kLutCopies + (tid & 3) * 4 + k] = e;
-  }
-  if (tid < 16 * G) {
-    // q' = B Hn q (the 1/sqrt(128) rides in the block matrices)
-    float m[32];
-    so4_matrices_row(a.rot_kind, rp, m);
-    if (a.rot_kind == kRotWhtSo4) wht128_row(xq, pl);
-    so4_apply_row<false>(xq, m);
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(xq[i]));
-    mx = fmaxf(mx, row_xor<8>(mx));
-    mx = fmaxf(mx, row_xor<4>(mx));
-    mx = fmaxf(mx, row_xor<2>(mx));
-    mx = fmaxf(mx, row_xor<1>(mx));
-    if (pl == 0) qmax[pg] = mx;
-    // operands: q' / max|q'| split into fp16 hi (11 significant bits) and lo
-    const float inv = mx > 0.f ? 1.0f / mx : 0.f;
-    uint32_t* qd = reinterpret_cast<uint32_t*>(&qop[0][0]);
-    uint32_t* qd_lo = reinterpret_cast<uint32_t*>(&qop_lo[0][0]);
-    const int qq = pl >> 2;   // this lane's dims 8 pl .. belong to operand lanes 16 qq + ..
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = 2 * (pl & 3) + (i >> 2), e = i & 3;
-      const float x = xq[i] * inv;
-      const float hx = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xffffe000u);
-      if (kSplitN) {
-        qd[(kk * 64 + 16 * qq + pg) * 4 + e] = dup16(hx);
-        qd[(kk * 64 + 16 * qq + pg + 8) * 4 + e] = dup16(x - hx);
-      } else {
-        qd[(kk * 64 + 16 * qq + pg) * 4 + e] = dup16(hx);
-        qd_lo[(kk * 64 + 16 * qq + pg) * 4 + e] = dup16(x - hx);
-      }
-    }
-  }
-  if (kSplitN && G < 8) {
-    // columns of heads >= G stay zero
-    for (int idx = tid; idx < 8 * 64; idx += kDecThreads) {
-      if (((idx & 15) & 7) >= G) qop[idx >> 6][idx & 63] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  __syncthreads();
-
-  // ---- per-lane constants: query operands, score scale ----
-  Consts<G> c;
-  const int g = kSplitN ? (n & 7) : n;     // head of this lane's score column / P row
-  const float qm = g < G ? qmax[g] : 0.f;
-  c.fscale = a.qscale * qm * a.cb.inv_alpha;
-  c.qop = &qop[0][lane];
-  c.qop_lo = &qop_lo[0][lane];
-  c.lo_lane = kSplitN && n >= 8;   // this lane's P row carries the lo half
-  c.lane_off = (lane & 15) * 8;
-  c.rel_lo = start - base;
-  c.rel_hi = start - base + len;
-  c.lut = reinterpret_cast<const char*>(lut);
-
-  WaveState st;
-#pragma unroll
-  for (int d = 0; d < 8; ++d) st.acc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
-
-  // two buffers, alternating: a block is computed while the next one is in
-  // flight. The first block is taken outside the loop so that it is computed
-  // straight from the registers its loads filled (a loop-carried start would
-  // let the compiler copy both buffers first and so wait for both).
-  if (b < b_end) {
-    process_block<G>(buf0, b * kBlk, q, c, st);
-    b += kWaves;
-    while (b < b_end) {
-      if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf0);
-      process_block<G>(buf1, b * kBlk, q, c, st);
-      b += kWaves;
-      if (b >= b_end) break;
-      if (b + kWaves < b_end) load_block(a, slot_base, (b + kWaves) * kBlk, n, q, buf1);
-      process_block<G>(buf0, b * kBlk, q, c, st);
-      b += kWaves;
-    }
-  }
-
-  // ---- per-wave totals ----
-  float l_run = st.l;
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (q == 0 && n < G) {
-    wm[wave][n] = st.m;
-    wl[wave][n] = l_run;
-  }
-  // accumulator row 4q + i: G <= 8: hi half of head (4q+i) for q < 2, lo half of head (4q+i-8) for q >= 2,
-  // kept as rows g and G + g; G = 16: head 4q+i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * q + i;
-    const int gr = kSplitN ? (m & 7) : m;
-    const int row = (kSplitN && m >= 8) ? G + gr : gr;
-    if (gr < G) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) wo[wave][row][8 * n + d] = st.acc[d][i];
-    }
-  }
-  __syncthreads();
-  // ---- merge the waves (and the hi/lo rows) into this split's records ----
-  // record of (seq, head hg, split): m, l, pad, pad, o'[128] with o' still in
-  // the rotated domain (the merge applies the one inverse rotation)
-  float* rec0 = a.ws + ((static_cast<size_t>(s) * a.num_q_heads + h * G) * a.rec_splits + a.rec_offset + split) * kRec;
-  const size_t head_stride = static_cast<size_t>(a.rec_splits) * kRec;
-  for (int idx = tid; idx < G * kDim; idx += kDecThreads) {
-    const int gr = idx >> 7, j = idx & (kDim - 1);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, wm[w][gr]);
-    float o = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float v = kSplitN ? wo[w][gr][j] + wo[w][G + gr][j] : wo[w][gr][j];
-        o += fast_exp2(wm[w][gr] - mx) * v;
-      }
-    }
-    rec0[gr * head_stride + 4 + j] = o * a.cb.inv_alpha;   // the PV operand carried alpha * c
-  }
-  if (tid < G) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, wm[w][tid]);
-    float l = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) l += exp2f(wm[w][tid] - mx) * wl[w][tid];
-    }
-    float* r = rec0 + tid * head_stride;
-    r[0] = mx;
-    r[1] = l;
-  }
 }
 
 }  // namespace iq
