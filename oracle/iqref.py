@@ -45,6 +45,10 @@ the design notes of the repository):
   * Code numbering: code c is the c-th centroid in ascending order.
   * Packing of K: code j occupies bits [3j, 3j+3) of a 384-bit little-endian
     bitstream (48 bytes per token row); bytes 3i..3i+2 hold codes 8i..8i+7.
+    With 4-bit K (the asymmetric split of [TQ-essay] "K 和 V 的非对称需求":
+    K gets more bits than V), K uses the 16-level Lloyd-Max codebook of the
+    same N(0, 1/d) and code j occupies bits [4j, 4j+4) (64-byte rows); V
+    stays 3-bit.
   * Packing of V: tokens are grouped in tiles of 8 consecutive cache slots
     (slot s in tile s // 8, position s % 8); a tile is a 3072-bit
     little-endian bitstream (384 bytes, the same 48 bytes per token) in which
@@ -128,11 +132,19 @@ def quantizer_mse_unit_gaussian(c: np.ndarray, t: np.ndarray) -> float:
     return total
 
 
-def codebook(d: int = D):
-    """Codebook for N(0, 1/d): (centroids float32[8], thresholds float32[7], centroids float64[8])."""
-    c, t = lloyd_max_unit_gaussian()
+def codebook(d: int = D, levels: int = N_LEVELS):
+    """Codebook for N(0, 1/d): (centroids float32[L], thresholds float32[L-1], centroids float64[L]),
+    L = 8 (3-bit, the default) or 16 (4-bit K of the asymmetric K/V split, [TQ-essay] "K 和 V 的非对称需求")."""
+    c, t = lloyd_max_unit_gaussian(levels)
     s = 1.0 / math.sqrt(d)
     return (c * s).astype(np.float32), (t * s).astype(np.float32), c * s
+
+
+def bits_of(table: np.ndarray) -> int:
+    """Code width of a codebook's centroids (L entries) or thresholds (L - 1 entries)."""
+    n = len(table)
+    levels = n if n in (8, 16) else n + 1
+    return {8: 3, 16: 4}[levels]
 
 
 # --------------------------------------------------------------------------
@@ -278,19 +290,26 @@ def quantize(y32: np.ndarray, thresholds32: np.ndarray):
     return codes, norm
 
 
-def pack(codes: np.ndarray) -> np.ndarray:
-    """[..., 128] codes -> [..., 48] bytes; code j at bits [3j, 3j+3), little-endian."""
+def pack(codes: np.ndarray, bits: int = BITS) -> np.ndarray:
+    """[..., 128] codes -> [..., 16 bits] bytes; code j at bits [bits j, bits (j+1)), little-endian
+    (48-byte rows for 3-bit codes, 64-byte rows for 4-bit)."""
     codes = np.asarray(codes, np.uint8)
-    bits = np.stack([(codes >> b) & 1 for b in range(BITS)], axis=-1)       # [..., 128, 3]
-    bits = bits.reshape(codes.shape[:-1] + (D * BITS,))
-    return np.packbits(bits, axis=-1, bitorder="little")
+    b = np.stack([(codes >> i) & 1 for i in range(bits)], axis=-1)          # [..., 128, bits]
+    b = b.reshape(codes.shape[:-1] + (D * bits,))
+    return np.packbits(b, axis=-1, bitorder="little")
 
 
 def unpack(rows: np.ndarray) -> np.ndarray:
-    """[..., 48] bytes -> [..., 128] codes (inverse of ``pack``)."""
-    bits = np.unpackbits(np.asarray(rows, np.uint8), axis=-1, bitorder="little")
-    bits = bits.reshape(rows.shape[:-1] + (D, BITS)).astype(np.uint8)
-    return bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
+    """[..., 48] or [..., 64] bytes -> [..., 128] codes (inverse of ``pack``; the width follows from
+    the row length)."""
+    rows = np.asarray(rows, np.uint8)
+    bits = rows.shape[-1] * 8 // D
+    b = np.unpackbits(rows, axis=-1, bitorder="little")
+    b = b.reshape(rows.shape[:-1] + (D, bits)).astype(np.uint8)
+    out = np.zeros(b.shape[:-1], np.uint8)
+    for i in range(bits):
+        out |= b[..., i] << i
+    return out
 
 
 TILE = 8                    # tokens per V tile
@@ -322,7 +341,7 @@ def rotate_quantize(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
     """Full encode of [..., 128] vectors of one head: (packed rows, norms, float32 y)."""
     y32 = rotate(np.asarray(x, np.float64), rot).astype(np.float32)
     codes, norm = quantize(y32, thresholds32)
-    return pack(codes), norm, y32
+    return pack(codes, bits_of(thresholds32)), norm, y32
 
 
 def dequantize_codes(codes: np.ndarray, norms: np.ndarray, rot: np.ndarray, centroids32: np.ndarray) -> np.ndarray:
@@ -351,9 +370,10 @@ def encode_codes(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
 
 
 def encode_tokens(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
-    """Encode [n_tok][Hkv][128] -> K rows [Hkv][n_tok][48], norms [Hkv][n_tok]."""
+    """Encode [n_tok][Hkv][128] -> K rows [Hkv][n_tok][48] (3-bit thresholds) or [..][64] (4-bit),
+    norms [Hkv][n_tok]."""
     codes, norms = encode_codes(x, rot, thresholds32)
-    return pack(codes), norms
+    return pack(codes, bits_of(thresholds32)), norms
 
 
 def encode_tokens_v(x: np.ndarray, rot: np.ndarray, thresholds32: np.ndarray):
@@ -385,15 +405,17 @@ def v_codes_range(v_tiles: np.ndarray, a: int, n: int) -> np.ndarray:
 
 
 def decode_attention(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_len, scale, centroids32,
-                     seqs=None, heads=None):
+                     seqs=None, heads=None, k_centroids32=None):
     """Decode attention straight from the definition, in float64.
 
     q [n_seqs][Hq][128]; k_rows [Hkv][cap][48]; v_tiles [Hkv][cap/8][384];
     norms [Hkv][cap]; rot [Hkv][32][8]. The packed K and V of each sequence
     are dequantized explicitly and ordinary softmax attention is taken over
     them. ``seqs`` and ``heads`` restrict the computation to a sample; other
-    outputs stay NaN.
+    outputs stay NaN. ``k_centroids32``: K's own codebook when K has more bits
+    than V (16 levels for 4-bit K rows of 64 bytes).
     """
+    kc = centroids32 if k_centroids32 is None else k_centroids32
     n_seqs, hq, _ = q.shape
     hkv = k_rows.shape[0]
     g = hq // hkv
@@ -401,14 +423,14 @@ def decode_attention(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_l
     for s in (range(n_seqs) if seqs is None else seqs):
         a, n = int(seq_start[s]), int(seq_len[s])
         for h in (range(hkv) if heads is None else heads):
-            kh = dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], centroids32)
+            kh = dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], kc)
             vh = dequantize_codes(v_codes_range(v_tiles[h], a, n), v_norms[h, a:a + n], rot[h], centroids32)
             out[s, h * g:(h + 1) * g] = attention(q[s, h * g:(h + 1) * g], kh, vh, scale)
     return out
 
 
 def decode_attention_deferred(q, k16, v16, prefix_start, prefix_len, k_rows, k_norms, v_tiles, v_norms, rot,
-                              seq_start, seq_len, scale, centroids32):
+                              seq_start, seq_len, scale, centroids32, k_centroids32=None):
     """Decode attention over a cache whose first tokens stayed fp16 (deferred
     quantization: [RQ-blurb] "延迟量化策略"; [TQ-essay] "延迟量化"), float64.
 
@@ -417,6 +439,7 @@ def decode_attention_deferred(q, k16, v16, prefix_start, prefix_len, k_rows, k_n
     slots seq_start[s] .. + seq_len[s], dequantized explicitly. Plain softmax
     attention over the concatenation.
     """
+    kc = centroids32 if k_centroids32 is None else k_centroids32
     n_seqs, hq, _ = q.shape
     hkv = k_rows.shape[0]
     g = hq // hkv
@@ -426,7 +449,7 @@ def decode_attention_deferred(q, k16, v16, prefix_start, prefix_len, k_rows, k_n
         a, n = int(seq_start[s]), int(seq_len[s])
         for h in range(hkv):
             kh = np.concatenate([np.asarray(k16[pa:pa + pn, h], np.float64),
-                                 dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], centroids32)])
+                                 dequantize(k_rows[h, a:a + n], k_norms[h, a:a + n], rot[h], kc)])
             vh = np.concatenate([np.asarray(v16[pa:pa + pn, h], np.float64),
                                  dequantize_codes(v_codes_range(v_tiles[h], a, n), v_norms[h, a:a + n], rot[h],
                                                   centroids32)])
@@ -435,7 +458,7 @@ def decode_attention_deferred(q, k16, v16, prefix_start, prefix_len, k_rows, k_n
 
 
 def decode_attention_rotated(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_start, seq_len, scale,
-                             centroids32):
+                             centroids32, k_centroids32=None):
     """The packed-domain algorithm, step by step in float64 ([RQ-news], [RQ-abs]).
 
     Rotate each query once (q' = R q), score every packed key as
@@ -447,6 +470,7 @@ def decode_attention_rotated(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_star
     hkv = k_rows.shape[0]
     g = hq // hkv
     c = centroids32.astype(np.float64)
+    ck = c if k_centroids32 is None else k_centroids32.astype(np.float64)
     out = np.zeros((n_seqs, hq, D))
     for s in range(n_seqs):
         a, n = int(seq_start[s]), int(seq_len[s])
@@ -454,7 +478,7 @@ def decode_attention_rotated(q, k_rows, k_norms, v_tiles, v_norms, rot, seq_star
             continue
         for h in range(hkv):
             qr = rotate(q[s, h * g:(h + 1) * g].astype(np.float64), rot[h])         # [g][128]
-            kc = c[unpack(k_rows[h, a:a + n])] * k_norms[h, a:a + n, None].astype(np.float64)
+            kc = ck[unpack(k_rows[h, a:a + n])] * k_norms[h, a:a + n, None].astype(np.float64)
             vc = c[v_codes_range(v_tiles[h], a, n)] * v_norms[h, a:a + n, None].astype(np.float64)
             p = softmax(scale * (qr @ kc.T))
             out[s, h * g:(h + 1) * g] = inverse_rotate(p @ vc, rot[h])

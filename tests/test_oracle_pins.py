@@ -247,6 +247,109 @@ def test_codebook_matches_kmeans_on_samples():
     assert np.allclose(np.sort(km.cluster_centers_.ravel()), c, atol=0.02)
 
 
+# ------------------------------------------ 4-bit K (asymmetric K/V) ----
+# The essay's "K 和 V 的非对称需求": K needs more bits than V. 4-bit K uses the
+# 16-level Lloyd-Max quantizer of the same N(0, 1/d); V stays 3-bit.
+def check_codebook16():
+    c, t = R.lloyd_max_unit_gaussian(16)
+    assert c.shape == (16,) and t.shape == (15,)
+    assert np.allclose(c, -c[::-1], atol=1e-12) and abs(t[7]) < 1e-12           # symmetric
+    assert np.all(np.diff(c) > 0)
+    edges = [-np.inf] + list(t) + [np.inf]
+    for k in range(16):                                                         # centroid condition
+        mass = scipy.integrate.quad(scipy.stats.norm.pdf, edges[k], edges[k + 1], epsabs=1e-14)[0]
+        mom = scipy.integrate.quad(lambda x: x * scipy.stats.norm.pdf(x), edges[k], edges[k + 1], epsabs=1e-14)[0]
+        assert abs(mom / mass - c[k]) < 1e-9
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), atol=0)                      # midpoint condition
+    d = R.quantizer_mse_unit_gaussian(c, t)
+    quad_mse = sum(scipy.integrate.quad(lambda x, ck=c[k]: (x - ck) ** 2 * scipy.stats.norm.pdf(x),
+                                        edges[k], edges[k + 1], epsabs=1e-14)[0] for k in range(16))
+    assert abs(quad_mse - d) < 1e-9
+    assert 4.0 ** -4 <= d <= 2.7 * 4.0 ** -4                                  # within ~2.7x of 2^(-2b)
+    assert d < R.quantizer_mse_unit_gaussian(*R.lloyd_max_unit_gaussian(8)) / 3   # one more bit: ~4x less
+    c32, t32, _ = R.codebook(levels=16)
+    assert np.array_equal(c32, (c / math.sqrt(128)).astype(np.float32)) and R.bits_of(c32) == 4
+
+
+def test_codebook16_is_lloyd_max_gaussian():
+    check_codebook16()
+
+
+def test_codebook16_matches_kmeans_on_samples():
+    from sklearn.cluster import KMeans
+    x = np.random.default_rng(16).standard_normal(500_000)
+    x = np.concatenate([x, -x]).reshape(-1, 1)                 # symmetrised sample: less noise in the tails
+    km = KMeans(n_clusters=16, n_init=1, init=np.linspace(-2.5, 2.5, 16).reshape(-1, 1), max_iter=1000,
+                tol=1e-12).fit(x)
+    c, _ = R.lloyd_max_unit_gaussian(16)
+    assert np.allclose(np.sort(km.cluster_centers_.ravel()), c, atol=0.03)
+
+
+def test_pack4_nibbles_and_round_trip():
+    codes = np.tile(np.arange(16, dtype=np.uint8), 8)                          # 0, 1, ..., 15, 0, 1, ...
+    row = R.pack(codes, 4)
+    assert row.shape == (64,)
+    assert list(row[:8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]    # low nibble = even dim
+    for pos in range(128):
+        for v in (1, 7, 8, 15):
+            c = np.zeros(128, np.uint8)
+            c[pos] = v
+            r = R.pack(c, 4)
+            assert r[pos // 2] == (v << (4 * (pos % 2))) and r.sum() == r[pos // 2]
+            assert np.array_equal(R.unpack(r), c)
+    rnd = np.random.default_rng(17).integers(0, 16, (50, 128)).astype(np.uint8)
+    assert np.array_equal(R.unpack(R.pack(rnd, 4)), rnd)
+
+
+def test_quantize16_is_nearest_centroid():
+    c32, t32, _ = R.codebook(levels=16)
+    g = np.random.default_rng(18)
+    y = (g.standard_normal((2000, 128)) * g.uniform(0.1, 30, (2000, 1))).astype(np.float32)
+    codes, n = R.quantize(y, t32)
+    u = y.astype(np.float64) / n[:, None].astype(np.float64)
+    nearest = np.argmin(np.abs(u[..., None] - c32.astype(np.float64)), axis=-1)
+    diff = nearest != codes
+    if diff.any():
+        gap = np.min(np.abs(u[diff][:, None] - t32.astype(np.float64)), axis=-1)
+        assert np.all(gap < 1e-6)
+    assert diff.mean() < 1e-5 and codes.max() == 15 and codes.min() == 0
+
+
+def test_distortion16_isotropic_inputs():
+    c32, t32, _ = R.codebook(levels=16)
+    c, t = R.lloyd_max_unit_gaussian(16)
+    rot = _rot(heads=1)[0]
+    x = np.random.default_rng(19).standard_normal((20000, 128))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    rows, n, _ = R.rotate_quantize(x, rot, t32)
+    assert rows.shape == (20000, 64)
+    d = np.mean(np.sum((x - R.dequantize(rows, n, rot, c32)) ** 2, axis=1))
+    assert abs(d - R.quantizer_mse_unit_gaussian(c, t)) < 0.05 * d
+
+
+def test_attention_with_4bit_k_packed_domain_equals_brute_force(codebook):
+    c32, t32, _ = codebook
+    c16, t16, _ = R.codebook(levels=16)
+    g = np.random.default_rng(20)
+    rot = _rot(seed=20, heads=2)
+    k = g.standard_normal((304, 2, 128))
+    v = g.standard_normal((304, 2, 128))
+    kr, kn = R.encode_tokens(k, rot, t16)
+    vr, vn = R.encode_tokens_v(v, rot, t32)
+    assert kr.shape == (2, 304, 64)
+    q = g.standard_normal((3, 4, 128)).astype(np.float32)
+    st, ln = np.array([0, 100, 300], np.int32), np.array([100, 200, 4], np.int32)
+    a = R.decode_attention(q, kr, kn, vr, vn, rot, st, ln, 0.09, c32, k_centroids32=c16)
+    b = R.decode_attention_rotated(q, kr, kn, vr, vn, rot, st, ln, 0.09, c32, k_centroids32=c16)
+    assert np.allclose(a, b, atol=1e-12, rtol=0)
+    # the 4-bit keys are closer to the exact ones than the 3-bit keys
+    exact = np.concatenate([R.attention(q[0, 2 * h:2 * h + 2].astype(np.float64), k[:100, h], R.dequantize_codes(
+        R.unpack_tiles(vr[h])[:100], vn[h, :100], rot[h], c32), 0.09) for h in range(2)])
+    kr3, kn3 = R.encode_tokens(k, rot, t32)
+    a3 = R.decode_attention(q, kr3, kn3, vr, vn, rot, st, ln, 0.09, c32)
+    assert np.linalg.norm(a[0] - exact) < np.linalg.norm(a3[0] - exact)
+
+
 # --------------------------------------------------------- quantizer ----
 def check_quantize(codebook):
     c32, t32, _ = codebook
@@ -541,3 +644,9 @@ def test_mutation_quaternion_multiplied_on_the_right(monkeypatch):
         return R.quat_mul(v, R.quat_conj(q) if inverse else q).reshape(y.shape)
     monkeypatch.setattr(R, "iso_apply", bad)
     _expect_fail(check_iso_rotation)
+
+
+def test_mutation_codebook16_one_iteration(monkeypatch):
+    good = R.lloyd_max_unit_gaussian
+    monkeypatch.setattr(R, "lloyd_max_unit_gaussian", lambda levels=8, **k: good(levels, max_iter=1))
+    _expect_fail(check_codebook16)
