@@ -90,12 +90,14 @@ typedef struct {
   int32_t num_kv_heads;   /* Hkv >= 1 */
   int32_t capacity;       /* slots per KV head (one flat token axis shared by all
                              sequences); a multiple of 32 */
-  uint8_t* k_codes;       /* [num_kv_heads][capacity][48] K rows, 16-byte aligned */
+  uint8_t* k_codes;       /* [num_kv_heads][capacity][16 * k_bits] K rows, 16-byte aligned */
   uint8_t* v_codes;       /* [num_kv_heads][capacity/8][384] V tiles, 16-byte aligned */
   float* k_norms;         /* [num_kv_heads][capacity] */
   float* v_norms;         /* [num_kv_heads][capacity] */
   const float* rot;       /* rotation parameters, layout per `rotation` */
   int32_t rotation;       /* iq_rotation; K and V of a head share it */
+  int32_t k_bits;         /* 3, or 4 for 4-bit K (16-level codebook, code j at
+                             bits [4j, 4j+4) of a 64-byte row); V is 3-bit */
 } iq_cache_view;
 
 /* Human-readable name of a status code (static string). */
@@ -106,6 +108,11 @@ IQ_API const char* iq_status_string(iq_status s);
  * to float (zhichai.net essay, section "Lloyd-Max 最优量化"). Both arrays are
  * host memory written by the call. */
 IQ_API iq_status iq_codebook(float centroids[8], float thresholds[7]);
+
+/* Host only. The codebook of `levels` = 8 (3-bit) or 16 (4-bit K, zhichai.net
+ * essay, section "K 和 V 的非对称需求": K needs more bits than V) Lloyd-Max
+ * levels of N(0, 1/128), ascending, and its levels - 1 midpoints. */
+IQ_API iq_status iq_codebook_levels(int32_t levels, float* centroids, float* thresholds);
 
 /* Rotate fp32 vectors with the per-head rotation (the first half of the
  * encode; the same transform is applied to queries before scoring).

@@ -64,12 +64,14 @@ class CacheView(ctypes.Structure):
         ("v_norms", ctypes.c_void_p),
         ("rot", ctypes.c_void_p),
         ("rotation", ctypes.c_int32),
+        ("k_bits", ctypes.c_int32),
     ]
 
 
 _SIGNATURES = {
     "iq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "iq_codebook": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "iq_codebook_levels": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "iq_rotate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "iq_quantize_pack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -146,11 +148,15 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
 
 
 # --------------------------------------------------------------------------
-def iq_codebook():
-    """(centroids float32[8], thresholds float32[7]) as the library computes them (host call)."""
-    c = np.zeros(8, np.float32)
-    t = np.zeros(7, np.float32)
-    _check("iq_codebook", lib().iq_codebook(c.ctypes.data, t.ctypes.data))
+def iq_codebook(levels: int = 8):
+    """(centroids float32[L], thresholds float32[L-1]) as the library computes them (host call);
+    L = 8 (3-bit) or 16 (4-bit K)."""
+    c = np.zeros(levels, np.float32)
+    t = np.zeros(levels - 1, np.float32)
+    if levels == 8:
+        _check("iq_codebook", lib().iq_codebook(c.ctypes.data, t.ctypes.data))
+    else:
+        _check("iq_codebook_levels", lib().iq_codebook_levels(levels, c.ctypes.data, t.ctypes.data))
     return c, t
 
 
@@ -158,17 +164,18 @@ def iq_codebook():
 class PackedKVCache:
     """Device buffers of one layer of the packed cache (allocated with torch).
 
-    K is stored as one 48-byte row per slot; V as 384-byte tiles of 8 slots
+    K is stored as one row per slot (48 bytes, or 64 for 4-bit K); V as 384-byte tiles of 8 slots
     (dim-major: code of dim j of the slot at tile position r at bits 24j + 3r).
     """
-    k_codes: torch.Tensor     # uint8 [Hkv][capacity][48]
+    k_codes: torch.Tensor     # uint8 [Hkv][capacity][16 * k_bits]
     v_codes: torch.Tensor     # uint8 [Hkv][capacity / 8][384]
     k_norms: torch.Tensor     # float32 [Hkv][capacity]
     v_norms: torch.Tensor
     rot: torch.Tensor         # float32 [Hkv][32][8], [Hkv][32][4] or [Hkv][64][2] (see rotation_kind)
 
     @classmethod
-    def allocate(cls, num_kv_heads: int, capacity: int, rot: torch.Tensor, device="cuda") -> "PackedKVCache":
+    def allocate(cls, num_kv_heads: int, capacity: int, rot: torch.Tensor, device="cuda",
+                 k_bits: int = 3) -> "PackedKVCache":
         """Zeroed cache with at least ``capacity`` slots (rounded up to a multiple of 32)."""
         cap = -(-capacity // CAPACITY_MULTIPLE) * CAPACITY_MULTIPLE
         zf = lambda: torch.zeros((num_kv_heads, cap), dtype=torch.float32, device=device)
@@ -176,7 +183,9 @@ class PackedKVCache:
         rotation_kind(rot)
         if rot.shape[0] != num_kv_heads:
             raise ValueError("rot must hold num_kv_heads heads")
-        return cls(torch.zeros((num_kv_heads, cap, ROW_BYTES), dtype=torch.uint8, device=device),
+        if k_bits not in (3, 4):
+            raise ValueError("k_bits must be 3 or 4")
+        return cls(torch.zeros((num_kv_heads, cap, 16 * k_bits), dtype=torch.uint8, device=device),
                    torch.zeros((num_kv_heads, cap // TILE, TILE_BYTES), dtype=torch.uint8, device=device),
                    zf(), zf(), rot)
 
@@ -188,6 +197,10 @@ class PackedKVCache:
     def capacity(self) -> int:
         return self.k_codes.shape[1]
 
+    @property
+    def k_bits(self) -> int:
+        return self.k_codes.shape[2] // 16
+
     def view(self) -> CacheView:
         for name in ("k_codes", "v_codes"):
             _dev(getattr(self, name), torch.uint8, name)
@@ -195,7 +208,7 @@ class PackedKVCache:
             _dev(getattr(self, name), torch.float32, name)
         return CacheView(HEAD_DIM, self.num_kv_heads, self.capacity, self.k_codes.data_ptr(),
                          self.v_codes.data_ptr(), self.k_norms.data_ptr(), self.v_norms.data_ptr(),
-                         self.rot.data_ptr(), rotation_kind(self.rot))
+                         self.rot.data_ptr(), rotation_kind(self.rot), self.k_bits)
 
 
 def iq_rotate(rot: torch.Tensor, x: torch.Tensor, inverse: bool = False, out: torch.Tensor | None = None,

@@ -16,38 +16,45 @@ namespace iq {
 // of its cell, iterated to a fixed point (zhichai.net essay, section
 // "Lloyd-Max 最优量化": assign to the nearest level, move each level to the
 // mean of what it received, repeat).
-static void lloyd_max_positive_half(double level[4], double bound[3]) {
+template <int N>
+static void lloyd_max_positive_half(double (&level)[N], double (&bound)[N - 1]) {
   const double inv_sqrt_2pi = 0.39894228040143267794;
   auto pdf = [&](double x) { return isinf(x) ? 0.0 : inv_sqrt_2pi * exp(-0.5 * x * x); };
   auto upper_tail = [](double x) { return isinf(x) ? 0.0 : 0.5 * erfc(x * 0.70710678118654752440); };
-  double y[4] = {0.25, 0.75, 1.25, 2.0};
-  for (int it = 0; it < 200000; ++it) {
-    const double e[5] = {0.0, 0.5 * (y[0] + y[1]), 0.5 * (y[1] + y[2]), 0.5 * (y[2] + y[3]), INFINITY};
-    double ny[4];
-    for (int k = 0; k < 4; ++k) ny[k] = (pdf(e[k]) - pdf(e[k + 1])) / (upper_tail(e[k]) - upper_tail(e[k + 1]));
+  double y[N];
+  for (int k = 0; k < N; ++k) y[k] = (k + 0.5) * 2.5 / N;   // spread over (0, 2.5)
+  for (int it = 0; it < 1000000; ++it) {
+    double e[N + 1];
+    e[0] = 0.0;
+    e[N] = INFINITY;
+    for (int k = 1; k < N; ++k) e[k] = 0.5 * (y[k - 1] + y[k]);
+    double ny[N];
+    for (int k = 0; k < N; ++k) ny[k] = (pdf(e[k]) - pdf(e[k + 1])) / (upper_tail(e[k]) - upper_tail(e[k + 1]));
     bool same = true;
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < N; ++k) {
       if (ny[k] != y[k]) same = false;
       y[k] = ny[k];
     }
     if (same) break;
   }
-  for (int k = 0; k < 4; ++k) level[k] = y[k];
-  for (int k = 0; k < 3; ++k) bound[k] = 0.5 * (y[k] + y[k + 1]);
+  for (int k = 0; k < N; ++k) level[k] = y[k];
+  for (int k = 0; k < N - 1; ++k) bound[k] = 0.5 * (y[k] + y[k + 1]);
 }
 
 // fp16 form of the centroids for the matrix-core contractions: alpha * c is
 // split into an fp16 hi part and an fp16 remainder, together good to ~2^-22.
 // alpha in [8, 16) is searched (2^-20 grid) so that the hi part alone is as
-// close as possible (worst ~2e-5 relative), which keeps the remainders small.
-static void centroid_fp16(Codebook& cb) {
+// close as possible (worst ~2e-5 relative for 8 levels), which keeps the
+// remainders small. pos = the N positive centroids.
+template <int N>
+static float centroid_fp16(const float* pos, uint16_t* h16, uint16_t* l16) {
   double best = 1e30, best_a = 8.0;
   const int steps = 1 << 20;
   for (int i = 0; i < steps; ++i) {
     const double al = 8.0 + 8.0 * i / steps;
     double worst = 0.0;
-    for (int k = 4; k < 8; ++k) {
-      const double x = al * static_cast<double>(cb.c[k]);
+    for (int k = 0; k < N; ++k) {
+      const double x = al * static_cast<double>(pos[k]);
       const double r = static_cast<double>(static_cast<_Float16>(static_cast<float>(x)));
       const double e = fabs(r - x) / x;
       worst = e > worst ? e : worst;
@@ -57,33 +64,41 @@ static void centroid_fp16(Codebook& cb) {
       best_a = al;
     }
   }
-  for (int k = 0; k < 4; ++k) {
-    const double x = best_a * static_cast<double>(cb.c[4 + k]);
+  for (int k = 0; k < N; ++k) {
+    const double x = best_a * static_cast<double>(pos[k]);
     const _Float16 hv = static_cast<_Float16>(static_cast<float>(x));
     const _Float16 lv = static_cast<_Float16>(static_cast<float>(x - static_cast<double>(hv)));
-    cb.h16[k] = __builtin_bit_cast(uint16_t, hv);
-    cb.l16[k] = __builtin_bit_cast(uint16_t, lv);
+    h16[k] = __builtin_bit_cast(uint16_t, hv);
+    l16[k] = __builtin_bit_cast(uint16_t, lv);
   }
-  cb.inv_alpha = static_cast<float>(1.0 / best_a);
+  return static_cast<float>(1.0 / best_a);
+}
+
+// Symmetric float32 codebook of 2N levels for N(0, 1/128) from the positive half.
+template <int N>
+static void fill_codebook(float* c, float* t) {
+  double lv[N], bd[N - 1];
+  lloyd_max_positive_half<N>(lv, bd);
+  const double s = 1.0 / sqrt(128.0);       // N(0, 1/d), d = 128
+  for (int k = 0; k < N; ++k) {
+    c[N + k] = static_cast<float>(lv[k] * s);
+    c[N - 1 - k] = -c[N + k];
+  }
+  t[N - 1] = 0.0f;
+  for (int k = 0; k < N - 1; ++k) {
+    t[N + k] = static_cast<float>(bd[k] * s);
+    t[N - 2 - k] = -t[N + k];
+  }
 }
 
 static const Codebook& codebook() {
   static Codebook cb;
   static std::once_flag once;
   std::call_once(once, [] {
-    double lv[4], bd[3];
-    lloyd_max_positive_half(lv, bd);
-    const double s = 1.0 / sqrt(128.0);       // N(0, 1/d), d = 128
-    for (int k = 0; k < 4; ++k) {
-      cb.c[4 + k] = static_cast<float>(lv[k] * s);
-      cb.c[3 - k] = -cb.c[4 + k];
-    }
-    cb.t[3] = 0.0f;
-    for (int k = 0; k < 3; ++k) {
-      cb.t[4 + k] = static_cast<float>(bd[k] * s);
-      cb.t[2 - k] = -cb.t[4 + k];
-    }
-    centroid_fp16(cb);
+    fill_codebook<4>(cb.c, cb.t);
+    cb.inv_alpha = centroid_fp16<4>(cb.c + 4, cb.h16, cb.l16);
+    fill_codebook<8>(cb.c4, cb.t4);
+    cb.inv_alpha_k = centroid_fp16<8>(cb.c4 + 8, cb.h16k, cb.l16k);
   });
   return cb;
 }
@@ -97,6 +112,7 @@ static iq_status check_view(const iq_cache_view* v) {
   if (!v->k_codes || !v->v_codes || !v->k_norms || !v->v_norms || !v->rot) return IQ_ERR_INVALID_ARG;
   if (v->rotation != IQ_ROT_WHT_SO4 && v->rotation != IQ_ROT_ISO && v->rotation != IQ_ROT_PLANAR)
     return IQ_ERR_INVALID_ARG;
+  if (v->k_bits != 3 && v->k_bits != 4) return IQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(v->k_codes) | reinterpret_cast<uintptr_t>(v->v_codes) |
        reinterpret_cast<uintptr_t>(v->k_norms) | reinterpret_cast<uintptr_t>(v->v_norms)) & 15u)
     return IQ_ERR_INVALID_ARG;
@@ -126,6 +142,14 @@ iq_status iq_codebook(float centroids[8], float thresholds[7]) {
   const Codebook& cb = codebook();
   for (int k = 0; k < 8; ++k) centroids[k] = cb.c[k];
   for (int k = 0; k < 7; ++k) thresholds[k] = cb.t[k];
+  return IQ_OK;
+}
+
+iq_status iq_codebook_levels(int32_t levels, float* centroids, float* thresholds) {
+  if (!centroids || !thresholds || (levels != 8 && levels != 16)) return IQ_ERR_INVALID_ARG;
+  const Codebook& cb = codebook();
+  for (int k = 0; k < levels; ++k) centroids[k] = levels == 8 ? cb.c[k] : cb.c4[k];
+  for (int k = 0; k < levels - 1; ++k) thresholds[k] = levels == 8 ? cb.t[k] : cb.t4[k];
   return IQ_OK;
 }
 
@@ -161,7 +185,7 @@ iq_status iq_rotate_quantize_append(const iq_cache_view* view, const void* k, co
   if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) return IQ_ERR_INVALID_ARG;
   if (!slots && (first_slot < 0 || static_cast<int64_t>(first_slot) + n_tokens > view->capacity))
     return IQ_ERR_CAPACITY;
-  AppendArgs a{view->rotation, k, v, slots, view->rot, view->k_codes, view->v_codes, view->k_norms, view->v_norms,
+  AppendArgs a{view->rotation, view->k_bits, k, v, slots, view->rot, view->k_codes, view->v_codes, view->k_norms, view->v_norms,
                n_tokens, first_slot, view->num_kv_heads, view->capacity, codebook()};
   return hip_status(launch_append(a, in_dtype == IQ_F16, static_cast<hipStream_t>(stream)));
 }
@@ -175,7 +199,7 @@ iq_status iq_dequantize(const iq_cache_view* view, int32_t first_slot, int32_t n
   if (first_slot < 0 || static_cast<int64_t>(first_slot) + n_tokens > view->capacity) return IQ_ERR_CAPACITY;
   if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15u) return IQ_ERR_INVALID_ARG;
   if (n_tokens == 0 || (!k_out && !v_out)) return IQ_OK;
-  DequantArgs a{view->rotation, view->k_codes, view->v_codes, view->k_norms, view->v_norms, view->rot, k_out, v_out,
+  DequantArgs a{view->rotation, view->k_bits, view->k_codes, view->v_codes, view->k_norms, view->v_norms, view->rot, k_out, v_out,
                 first_slot, n_tokens, view->num_kv_heads, view->capacity, codebook()};
   return hip_status(launch_dequant(a, out_dtype == IQ_F16, static_cast<hipStream_t>(stream)));
 }
@@ -210,6 +234,7 @@ iq_status iq_decode_attention(const iq_cache_view* view, const float* q, int32_t
   a.v_norms = view->v_norms;
   a.rot = view->rot;
   a.rot_kind = view->rotation;
+  a.k_bits = view->k_bits;
   a.q = q;
   a.seq_start = seq_start;
   a.seq_len = seq_len;
@@ -340,6 +365,7 @@ iq_status iq_decode_attention_deferred(const iq_cache_view* view, const int32_t*
   suf.v_norms = view->v_norms;
   suf.rot = view->rot;
   suf.rot_kind = view->rotation;
+  suf.k_bits = view->k_bits;
   suf.q = q;
   suf.seq_start = seq_start;
   suf.seq_len = seq_len;

@@ -40,9 +40,9 @@ namespace iq {
 
 // work-groups go round-robin to the XCDs in launch order; with the split
 // index slowest (grid z), the live splits (short sequences have few) spread evenly
-template <int G>
+template <int G, int KB>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a) {
-  __shared__ PackedSmem<G> sm;
+  __shared__ PackedSmem<G, KB> sm;
   const int split = blockIdx.z;
 #include "iq_decode_packed_body.inc"
 }
@@ -196,16 +196,23 @@ size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodeP
   return static_cast<size_t>(n_seqs) * num_q_heads * p.n_splits * kRec * sizeof(float);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+template <int KB>
+static hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.num_kv_heads, a.n_seqs, a.n_splits);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kDecThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(kDecThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(kDecThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL(decode_split_kernel<16>, grid, dim3(kDecThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<1, KB>), grid, dim3(kDecThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<2, KB>), grid, dim3(kDecThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<4, KB>), grid, dim3(kDecThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<8, KB>), grid, dim3(kDecThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_split_kernel<16, KB>), grid, dim3(kDecThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const hipError_t le = a.k_bits == 4 ? launch_split<4>(a, st) : launch_split<3>(a, st);
+  if (le != hipSuccess) return le;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, {}};

@@ -386,32 +386,41 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_f16_split_kernel(F16Dec
 // essay section "延迟量化"): the prompt's K/V stay fp16, generated tokens are
 // packed. One launch holds both parts' splits, the prefix's first (grid z <
 // pre.n_splits); their records meet in one merge.
-template <int G>
+template <int G, int KB>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_deferred_split_kernel(F16DecodeArgs pre, DecodeArgs suf) {
   __shared__ union {
     F16Smem<G> f;
-    PackedSmem<G> p;
+    PackedSmem<G, KB> p;
   } sm;
   const int z = blockIdx.z;
   if (z < pre.n_splits) {
     f16_split<G>(pre, sm.f, z);
   } else {
-    packed_split<G>(suf, sm.p, z - pre.n_splits);
+    packed_split<G, KB>(suf, sm.p, z - pre.n_splits);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t st) {
+template <int KB>
+static hipError_t launch_deferred_split(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t st) {
   dim3 grid(suf.num_kv_heads, suf.n_seqs, pre.n_splits + suf.n_splits);
   switch (suf.group) {
-    case 1: hipLaunchKernelGGL(decode_deferred_split_kernel<1>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
-    case 2: hipLaunchKernelGGL(decode_deferred_split_kernel<2>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
-    case 4: hipLaunchKernelGGL(decode_deferred_split_kernel<4>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
-    case 8: hipLaunchKernelGGL(decode_deferred_split_kernel<8>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
-    case 16: hipLaunchKernelGGL(decode_deferred_split_kernel<16>, grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 1: hipLaunchKernelGGL((decode_deferred_split_kernel<1, KB>), grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 2: hipLaunchKernelGGL((decode_deferred_split_kernel<2, KB>), grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 4: hipLaunchKernelGGL((decode_deferred_split_kernel<4, KB>), grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 8: hipLaunchKernelGGL((decode_deferred_split_kernel<8, KB>), grid, dim3(kDecThreads), 0, st, pre, suf); break;
+    case 16:
+      hipLaunchKernelGGL((decode_deferred_split_kernel<16, KB>), grid, dim3(kDecThreads), 0, st, pre, suf);
+      break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t st) {
+  const hipError_t le = suf.k_bits == 4 ? launch_deferred_split<4>(pre, suf, st) : launch_deferred_split<3>(pre, suf, st);
+  if (le != hipSuccess) return le;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs m{suf.rot_kind, suf.rot, suf.out, suf.ws, suf.n_seqs, suf.num_q_heads, suf.group, suf.rec_splits, 2, {}};

@@ -22,6 +22,24 @@ __device__ __forceinline__ uint2 pair_entry(const uint32_t (&w)[N], const char* 
   return *reinterpret_cast<const uint2*>(lut + addr);
 }
 
+// 4-bit K: table entry of the code pair in byte BIT / 8 of w (256 entries of
+// 16 copies, 128 bytes apart); the byte never straddles a dword.
+template <int BIT, int N>
+__device__ __forceinline__ uint2 pair_entry4(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
+  constexpr int word = BIT >> 5, field = BIT & 31;
+  uint32_t addr;
+  asm("v_bfe_u32 %0, %1, %2, 8\n\tv_lshl_add_u32 %0, %0, 7, %3" : "=&v"(addr) : "v"(w[word]), "i"(field), "v"(lane_off));
+  return *reinterpret_cast<const uint2*>(lut + addr);
+}
+
+template <int BIT, int N>
+__device__ __forceinline__ half8 code_operand4(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
+  H8 r;
+  r.u2[0] = pair_entry4<BIT>(w, lut, lane_off);
+  r.u2[1] = pair_entry4<BIT + 8>(w, lut, lane_off);
+  return r.h;
+}
+
 // Code operand for the 4 codes at bits BIT .. BIT+11 of w (two pairs).
 template <int BIT, int N>
 __device__ __forceinline__ half8 code_operand(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
@@ -31,22 +49,31 @@ __device__ __forceinline__ half8 code_operand(const uint32_t (&w)[N], const char
   return r.h;
 }
 
-// Packed codes and norms of one 32-slot block for this lane.
+// Packed codes and norms of one 32-slot block for this lane (KB = K bits).
+template <int KB>
 struct BlockData {
-  uint32_t kw0[3], kw1[3], vw[6];
+  uint32_t kw0[KB], kw1[KB], vw[6];
   float4 nk0, nk1, nv0, nv1;
 };
 
 // K tile T row r <-> token 8 (r/4) + 4T + r%4 of the block; this lane loads
 // row n of both tiles (dims 32q .. 32q+31), V tile q (dims 8n .. 8n+7) and
 // the norms of tokens 8q .. 8q+7 (its rows in the score output).
+template <int KB>
 __device__ __forceinline__ void load_block(const DecodeArgs& a, size_t slot_base, int slot0, int n, int q,
-                                           BlockData& d) {
+                                           BlockData<KB>& d) {
+  constexpr int kRow = k_row_bytes(KB);   // 48 or 64
   const int tok_a0 = 8 * (n >> 2) + (n & 3);
-  const uint32_t* k0 = reinterpret_cast<const uint32_t*>(a.k_codes + (slot_base + slot0 + tok_a0) * kRowBytes + 12 * q);
-  const uint32_t* k1 = k0 + kRowBytes;   // token + 4: 4 rows of 48 bytes = 48 dwords
-  d.kw0[0] = k0[0]; d.kw0[1] = k0[1]; d.kw0[2] = k0[2];
-  d.kw1[0] = k1[0]; d.kw1[1] = k1[1]; d.kw1[2] = k1[2];
+  const uint32_t* k0 = reinterpret_cast<const uint32_t*>(a.k_codes + (slot_base + slot0 + tok_a0) * kRow + 4 * KB * q);
+  const uint32_t* k1 = k0 + kRow;   // token + 4: 4 rows = kRow dwords
+  if constexpr (KB == 4) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(k0), x1 = *reinterpret_cast<const uint4*>(k1);
+    d.kw0[0] = x0.x; d.kw0[1] = x0.y; d.kw0[2] = x0.z; d.kw0[3] = x0.w;
+    d.kw1[0] = x1.x; d.kw1[1] = x1.y; d.kw1[2] = x1.z; d.kw1[3] = x1.w;
+  } else {
+    d.kw0[0] = k0[0]; d.kw0[1] = k0[1]; d.kw0[2] = k0[2];
+    d.kw1[0] = k1[0]; d.kw1[1] = k1[1]; d.kw1[2] = k1[2];
+  }
   const uint2* vp = reinterpret_cast<const uint2*>(a.v_codes + ((slot_base + slot0) / kTile + q) * kTileBytes + 24 * n);
   const uint2 v0 = vp[0], v1 = vp[1], v2 = vp[2];
   d.vw[0] = v0.x; d.vw[1] = v0.y; d.vw[2] = v1.x; d.vw[3] = v1.y; d.vw[4] = v2.x; d.vw[5] = v2.y;
@@ -63,19 +90,22 @@ struct Consts {
   bool lo_lane;
   uint32_t lane_off;
   int rel_lo, rel_hi;
-  const char* lut;
+  const char* lut;    // 3-bit code pairs (V, and K when 3-bit)
+  const char* klut;   // 4-bit K code pairs
 };
 
-template <int G>
-__device__ __forceinline__ void process_block(const BlockData& cur, int slot0, int q, const Consts<G>& c,
+template <int G, int KB>
+__device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot0, int q, const Consts<G>& c,
                                               WaveState& st) {
   constexpr bool kSplitN = (G <= 8);
   // ---- scores: D_T[i] = row 4q + i of tile T = token 8q + 4T + i, column n ----
   floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #define IQ_SCORE(KAPPA)                                                        \
   {                                                                            \
-    const half8 ka = code_operand<12 * KAPPA>(cur.kw0, c.lut, c.lane_off);     \
-    const half8 kb = code_operand<12 * KAPPA>(cur.kw1, c.lut, c.lane_off);     \
+    const half8 ka = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw0, c.klut, c.lane_off) \
+                             : code_operand<12 * KAPPA>(cur.kw0, c.lut, c.lane_off);  \
+    const half8 kb = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw1, c.klut, c.lane_off) \
+                             : code_operand<12 * KAPPA>(cur.kw1, c.lut, c.lane_off);  \
     H8 qv;                                                                     \
     qv.u4 = c.qop[64 * KAPPA];                                                 \
     d0 = mfma16(ka, qv.h, d0);                                                 \
@@ -172,25 +202,29 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int slot0, i
 }
 
 // LDS of one packed split work-group.
-template <int G>
+template <int G, int KB>
 struct PackedSmem {
   static constexpr bool kSplitN = (G <= 8);        // hi/lo halves share one MFMA (columns / rows g and g+8)
   static constexpr int kRows = kSplitN ? 2 * G : G;   // accumulator rows kept per wave (hi and lo halves)
   uint2 lut[kLutEntries * kLutCopies];
+  // the wave accumulators after the loop; during it (4-bit K) the K code-pair table
+  union {
+    float wo[kWaves][kRows][kDim];
+    uint2 klut[KB == 4 ? 256 * kLutCopies : 2];
+  } big;
   // query operand of k-step kk for lane 16 q + n: dims 32 q + 4 kk + e (e = 0..3) of
   // head n & 7, each value twice (one fp16 pair); hi halves in columns n < 8, lo
   // halves in n >= 8 (G = 16: hi in qop, lo in qop_lo, column n = head n)
   uint4 qop[8][64];
   uint4 qop_lo[kSplitN ? 1 : 8][64];
-  float wo[kWaves][kRows][kDim];
   float qmax[G];
   float wm[kWaves][G], wl[kWaves][G];
 };
 
 // One split of the packed decode: work-group (h = KV head, s = sequence,
 // split). Records go to split index a.rec_offset + split of a.rec_splits.
-template <int G>
-__device__ __forceinline__ void packed_split(const DecodeArgs& a, PackedSmem<G>& sm, int split) {
+template <int G, int KB>
+__device__ __forceinline__ void packed_split(const DecodeArgs& a, PackedSmem<G, KB>& sm, int split) {
 #include "iq_decode_packed_body.inc"
 
 }

@@ -25,7 +25,16 @@ struct Codebook {
   uint16_t h16[4];   // fp16 bit patterns of alpha * c[4..7] (the positive half) ...
   uint16_t l16[4];   // ... and of the remainders alpha * c - h16
   float inv_alpha;   // 1 / alpha: c[k] = (h16 + l16) * inv_alpha to ~2^-22
+  // the 16-level codebook of 4-bit K rows, same layout
+  float c4[16];
+  float t4[15];      // t4[7] == 0
+  uint16_t h16k[8];
+  uint16_t l16k[8];
+  float inv_alpha_k;
 };
+
+// K row bytes for 3- or 4-bit codes: 128 dims x bits / 8.
+__host__ __device__ constexpr int k_row_bytes(int bits) { return 16 * bits; }
 
 constexpr int kTile = 8;                   // tokens per V tile
 constexpr int kTileBytes = kTile * kRowBytes;   // 384
@@ -342,6 +351,46 @@ __device__ __forceinline__ uint32_t code_of(float y, float t4, float t5, float t
   // the definition gives 0, so NaN is handled explicitly.
   if (y != y) return 0u;
   return 3u - ((a >= t4) + (a >= t5) + (a >= t6));
+}
+
+// 16-level code = #{k : y > thr_k} with the symmetric thresholds of the 4-bit
+// codebook (thr_{14-k} = -thr_k, thr_7 = 0); t8..t14 are fl32(t4[8..14] n).
+__device__ __forceinline__ uint32_t code16_of(float y, const float (&tp)[7]) {
+  const float a = fabsf(y);
+  uint32_t above = 0, at_or_above = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    above += a > tp[k];
+    at_or_above += a >= tp[k];
+  }
+  if (y > 0.0f) return 8u + above;
+  if (y != y) return 0u;   // NaN: the definition gives code 0
+  return 7u - at_or_above;
+}
+
+// Centroid of a 16-level code by selects: c4[v] = c4[8 + (v - 8)] for v >= 8,
+// -c4[8 + (7 - v)] otherwise.
+__device__ __forceinline__ float centroid16(uint32_t v, const Codebook& cb) {
+  const bool neg = v < 8u;
+  const uint32_t m = neg ? 7u - v : v - 8u;
+  const float a0 = (m & 1u) ? cb.c4[9] : cb.c4[8], a1 = (m & 1u) ? cb.c4[11] : cb.c4[10];
+  const float a2 = (m & 1u) ? cb.c4[13] : cb.c4[12], a3 = (m & 1u) ? cb.c4[15] : cb.c4[14];
+  const float b0 = (m & 2u) ? a1 : a0, b1 = (m & 2u) ? a3 : a2;
+  const float mag = (m & 4u) ? b1 : b0;
+  return neg ? -mag : mag;
+}
+
+// fp16 bit pattern of the hi (kLo = false) or lo part of alpha_k * c4[v].
+template <bool kLo>
+__device__ __forceinline__ uint32_t centroid16_f16(uint32_t v, const Codebook& cb) {
+  const uint16_t* t = kLo ? cb.l16k : cb.h16k;
+  const bool neg = v < 8u;
+  const uint32_t m = neg ? 7u - v : v - 8u;
+  const uint32_t a0 = (m & 1u) ? t[1] : t[0], a1 = (m & 1u) ? t[3] : t[2];
+  const uint32_t a2 = (m & 1u) ? t[5] : t[4], a3 = (m & 1u) ? t[7] : t[6];
+  const uint32_t b0 = (m & 2u) ? a1 : a0, b1 = (m & 2u) ? a3 : a2;
+  const uint32_t mag = (m & 4u) ? b1 : b0;
+  return neg ? (mag ^ 0x8000u) : mag;
 }
 
 // Pack 32 codes (3 bits each) into 3 dwords, code i at bits [3i, 3i+3).

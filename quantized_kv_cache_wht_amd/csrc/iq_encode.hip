@@ -87,6 +87,24 @@ __device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], 
   return n;
 }
 
+// Norm, 16-level codes and the lane's 4 packed dwords (code i at bits 4i) of a
+// rotated vector: the 4-bit K rows.
+__device__ __forceinline__ float quantize_pack_lane16(const float (&y)[kPerLane], const Codebook& cb,
+                                                      uint32_t (&w)[4]) {
+  const float n = quad_norm(y);
+  float tp[7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(cb.t4[8 + k], n);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v |= code16_of(y[8 * d + i], tp) << (4 * i);
+    w[d] = v;
+  }
+  return n;
+}
+
 // ---------------------------------------------------------------------------
 // Append: x (K or V of new tokens) -> codes + norms in the cache.
 // grid = (windows, num_kv_heads, 2 [K, V]). Without a slot list a window is
@@ -131,7 +149,7 @@ __device__ __forceinline__ void tile_keep_bits(uint32_t mask, uint32_t (&keep)[3
   }
 }
 
-template <typename T>
+template <typename T, bool kK4>   // kK4: the cache's K rows are 4-bit
 __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   __shared__ __align__(16) float sm[kBlocks * 16];
   __shared__ __align__(16) uint32_t rows[kVecPerBlock][12];
@@ -194,6 +212,17 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     }
     if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
+    if (kK4 && !is_v) {
+      uint32_t w4[4];
+      const float n4 = quantize_pack_lane16(x, a.cb, w4);
+      const int slot = ok ? (scatter ? a.slots[tok] : a.first_slot + tok) : -1;
+      if (slot >= 0 && slot < a.capacity) {
+        const size_t row = static_cast<size_t>(h) * a.capacity + slot;
+        if (part == 0) norms[row] = n4;
+        *reinterpret_cast<uint4*>(codes + row * k_row_bytes(4) + part * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+      continue;
+    }
     uint32_t w[3];
     const float n = quantize_pack_lane(x, a.cb, w);
     const int slot = ok ? (scatter ? a.slots[tok] : a.first_slot + tok) : -1;
@@ -325,6 +354,19 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
   if (a.rot_kind == kRotWhtSo4) wht128_row(x, p);
   so4_apply_row<false>(x, m);
   const float n = row_norm(x);
+  if (!is_v && a.k_bits == 4) {
+    // 4-bit K: this lane's 8 codes are the row's dword p
+    float tp[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(a.cb.t4[8 + k], n);
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= code16_of(x[i], tp) << (4 * i);
+    if (!in_cap) return;
+    if (p == 0) a.k_norms[row] = n;
+    reinterpret_cast<uint32_t*>(a.k_codes + row * k_row_bytes(4))[p] = w;
+    return;
+  }
   const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
   uint32_t c[8];
 #pragma unroll
@@ -440,10 +482,14 @@ __global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
     const bool ok = tok < a.n_tokens;
     const size_t row = static_cast<size_t>(h) * a.capacity + a.first_slot + (ok ? tok : 0);
     uint32_t w[3] = {0u, 0u, 0u};
+    uint4 w4 = make_uint4(0u, 0u, 0u, 0u);
+    const bool k4 = !is_v && a.k_bits == 4;
     float n = 0.f;
     if (ok) {
       n = norms[row];
-      if (!is_v) {
+      if (k4) {
+        w4 = *reinterpret_cast<const uint4*>(codes + row * k_row_bytes(4) + part * 16);
+      } else if (!is_v) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + row * kRowBytes + part * 12);
         w[0] = src[0];
         w[1] = src[1];
@@ -465,8 +511,14 @@ __global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
       }
     }
     float x[kPerLane];
+    if (k4) {
+      const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) x[i] = centroid(code_at(w, i), a.cb);
+      for (int i = 0; i < kPerLane; ++i) x[i] = centroid16((wd[i >> 3] >> (4 * (i & 7))) & 15u, a.cb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) x[i] = centroid(code_at(w, i), a.cb);
+    }
     so4_apply_lane<true>(x, sm, part);
     if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
 #pragma unroll
@@ -495,10 +547,18 @@ hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s) {
     return hipGetLastError();
   }
   dim3 grid(enc_grid_x(a.n_tokens, 2LL * a.num_kv_heads), a.num_kv_heads, 2);
-  if (f16)
-    hipLaunchKernelGGL(append_kernel<_Float16>, grid, dim3(kEncThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(kEncThreads), 0, s, a);
+  const bool k4 = a.k_bits == 4;
+  if (f16) {
+    if (k4)
+      hipLaunchKernelGGL((append_kernel<_Float16, true>), grid, dim3(kEncThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<_Float16, false>), grid, dim3(kEncThreads), 0, s, a);
+  } else {
+    if (k4)
+      hipLaunchKernelGGL((append_kernel<float, true>), grid, dim3(kEncThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<float, false>), grid, dim3(kEncThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace iq {
 
 struct AppendArgs {
   int32_t rot_kind;      // iq_rotation
+  int32_t k_bits;        // 3 or 4
   const void* k;
   const void* v;
   const int32_t* slots;
@@ -44,6 +45,7 @@ struct QuantArgs {
 
 struct DequantArgs {
   int32_t rot_kind;      // iq_rotation
+  int32_t k_bits;        // 3 or 4
   const uint8_t* k_codes;
   const uint8_t* v_codes;
   const float* k_norms;
@@ -80,6 +82,7 @@ struct DecodeArgs {
   int32_t n_splits;           // splits per (seq, kv head) at max_seq_len
   int32_t rec_offset;         // record index of split 0 ...
   int32_t rec_splits;         // ... among this many records per (seq, query head)
+  int32_t k_bits;             // 3 or 4
   float qscale;               // softmax scale * log2(e)
   Codebook cb;
 };

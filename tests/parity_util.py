@@ -30,13 +30,14 @@ def _assert_attention_close(got, ref, what=""):
     assert max_abs <= 2e-3 and rel <= 1e-3, (what, max_abs, rel)
 
 
-def _boundary_mismatch_ok(codes_gpu, codes_ref, y_ref, n_ref):
+def _boundary_mismatch_ok(codes_gpu, codes_ref, y_ref, n_ref, thresholds=None):
     """Mismatched codes must sit within 1e-6 of a boundary (in y/n units) and be < 1e-5 of all."""
     diff = codes_gpu != codes_ref
     nd = int(diff.sum())
     if nd:
         u = y_ref[diff].astype(np.float64) / np.broadcast_to(n_ref[..., None], y_ref.shape)[diff].astype(np.float64)
-        gap = np.min(np.abs(u[:, None] - T32.astype(np.float64)[None, :]), axis=1)
+        thr = T32 if thresholds is None else thresholds
+        gap = np.min(np.abs(u[:, None] - thr.astype(np.float64)[None, :]), axis=1)
         assert np.all(gap <= 1e-6), gap.max()
         assert np.all(np.abs(codes_gpu[diff].astype(int) - codes_ref[diff].astype(int)) == 1)
     assert nd < 1e-5 * codes_ref.size, (nd, codes_ref.size)

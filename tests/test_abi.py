@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     h = ctypes.CDLL(iq.library_path())
     for n in names:
         assert hasattr(h, n), n
@@ -35,14 +35,25 @@ def test_codebook_matches_oracle_bit_for_bit():
     assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
 
 
+def test_codebook16_matches_oracle_bit_for_bit():
+    c, t = iq.iq_codebook(16)
+    oc, ot, _ = iqref.codebook(levels=16)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
+    L = iq.lib()
+    buf = np.zeros(16, np.float32)
+    assert L.iq_codebook_levels(12, buf.ctypes.data, buf.ctypes.data) == -1
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert iq.status_string(s)
     assert iq.status_string(-99) == "unknown status"
 
 
-def _view(head_dim=128, hkv=2, cap=128, ptr=0x10000, rotation=0):
-    return iq.CacheView(head_dim, hkv, cap, ptr, ptr + 0x1000, ptr + 0x2000, ptr + 0x3000, ptr + 0x4000, rotation)
+def _view(head_dim=128, hkv=2, cap=128, ptr=0x10000, rotation=0, k_bits=3):
+    return iq.CacheView(head_dim, hkv, cap, ptr, ptr + 0x1000, ptr + 0x2000, ptr + 0x3000, ptr + 0x4000, rotation,
+                        k_bits)
 
 
 def test_append_validation():
@@ -63,6 +74,8 @@ def test_append_validation():
     assert L.iq_rotate_quantize_append(ctypes.byref(bad), p, p, 1, 4, 0, None, None) == -1
     assert L.iq_rotate_quantize_append(ctypes.byref(_view(rotation=3)), p, p, 1, 4, 0, None, None) == -1
     assert L.iq_rotate_quantize_append(ctypes.byref(_view(rotation=2)), p, p, 1, 0, 0, None, None) == 0
+    assert L.iq_rotate_quantize_append(ctypes.byref(_view(k_bits=5)), p, p, 1, 4, 0, None, None) == -1
+    assert L.iq_rotate_quantize_append(ctypes.byref(_view(k_bits=4)), p, p, 1, 0, 0, None, None) == 0
 
 
 def test_decode_validation():

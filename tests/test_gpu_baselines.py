@@ -88,10 +88,10 @@ def test_unfused_path_matches_fused_and_oracle():
 
 
 # ------------------------------------------------- deferred quantization ----
-@pytest.mark.parametrize("kind", ["wht_so4", "planar"])
+@pytest.mark.parametrize("kind,k_bits", [("wht_so4", 3), ("planar", 3), ("wht_so4", 4)])
 @pytest.mark.parametrize("pre,suf", [([700, 0, 33], [40, 1, 0]), ([0, 0], [300, 12]), ([2100], [0]),
                                      ([3000, 5], [257, 64])])
-def test_deferred_decode_matches_oracle(kind, pre, suf):
+def test_deferred_decode_matches_oracle(kind, k_bits, pre, suf):
     hq, hkv = 32, 4
     pre, suf = np.array(pre, np.int32), np.array(suf, np.int32)
     n_seqs = len(pre)
@@ -105,9 +105,10 @@ def test_deferred_decode_matches_oracle(kind, pre, suf):
     v16 = iqinputs.kv(seed, 1, "v", cap16, hkv, "student_t6", "f16")
     k = iqinputs.kv(seed, 2, "k", cap, hkv, "student_t6", "f16")
     v = iqinputs.kv(seed, 2, "v", cap, hkv, "student_t6", "f16")
-    kr, kn = R.encode_tokens(k, rot, T32)
+    c_k, t_k, _ = R.codebook(levels=16 if k_bits == 4 else 8)
+    kr, kn = R.encode_tokens(k, rot, t_k)
     vt, vn = R.encode_tokens_v(v, rot, T32)
-    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot))
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=k_bits)
     cache.k_codes.copy_(_t(kr))
     cache.v_codes.copy_(_t(vt))
     cache.k_norms.copy_(_t(kn))
@@ -115,7 +116,8 @@ def test_deferred_decode_matches_oracle(kind, pre, suf):
     q = iqinputs.queries(seed, 3, n_seqs, hq)
     out = _np(iq.iq_decode_attention_deferred(cache, _t(sst), _t(suf), int(suf.max()), _t(k16), _t(v16), _t(pst),
                                               _t(pre), int(pre.max()), _t(q)))
-    ref = R.decode_attention_deferred(q, k16, v16, pst, pre, kr, kn, vt, vn, rot, sst, suf, SCALE, C32)
-    _assert_attention_close(out, ref, f"deferred {kind} prefix={list(pre)} suffix={list(suf)}")
+    ref = R.decode_attention_deferred(q, k16, v16, pst, pre, kr, kn, vt, vn, rot, sst, suf, SCALE, C32,
+                                      k_centroids32=c_k)
+    _assert_attention_close(out, ref, f"deferred {kind} k_bits={k_bits} prefix={list(pre)} suffix={list(suf)}")
     for s in np.nonzero((pre + suf) == 0)[0]:
         assert np.all(out[s] == 0)

@@ -325,3 +325,82 @@ def test_dequantize_variants_match_oracle(kind):
         ref = R.dequantize_codes(codes[h], norms[h], rot[h], C32)
         assert np.max(np.abs(k_out[:, h] - ref) / norms[h, :, None]) < 2e-6
         assert np.max(np.abs(v_out[:, h] - ref) / norms[h, :, None]) < 2e-6
+
+
+# -------------------------------------------------- 4-bit K, 3-bit V ----
+C16, T16, _ = R.codebook(levels=16)
+
+
+def _encode_ref_thr(x, rot, thr):
+    hkv = x.shape[1]
+    out_c, out_n, out_y = [], [], []
+    for h in range(hkv):
+        y32 = R.rotate(x[:, h].astype(np.float64), rot[h]).astype(np.float32)
+        c, n = R.quantize(y32, thr)
+        out_c.append(c), out_n.append(n), out_y.append(y32)
+    return np.stack(out_c), np.stack(out_n), np.stack(out_y)
+
+
+@pytest.mark.parametrize("kind", ["wht_so4", "iso"])
+@pytest.mark.parametrize("n_tok,first", [(700, 13), (1, 500), (40, 21)])   # bulk and short appends
+def test_append_k4_matches_oracle(kind, n_tok, first):
+    hkv = 4
+    rot = iqinputs.rotation_params_kind(31, 0, hkv, kind)
+    k = iqinputs.kv(31, 0, "k", n_tok, hkv, "student_t6", "f16")
+    v = iqinputs.kv(31, 0, "v", n_tok, hkv, "student_t6", "f16")
+    cache = iq.PackedKVCache.allocate(hkv, first + n_tok, _t(rot), k_bits=4)
+    assert cache.k_codes.shape[2] == 64
+    iq.iq_rotate_quantize_append(cache, _t(k), _t(v), first_slot=first)
+    codes_ref, n_ref, y_ref = _encode_ref_thr(k, rot, T16)
+    got = R.unpack(_np(cache.k_codes))
+    assert got.max() <= 15
+    _boundary_mismatch_ok(got[:, first:first + n_tok], codes_ref, y_ref, n_ref, T16)
+    assert not got[:, :first].any() and not got[:, first + n_tok:].any()
+    norms = _np(cache.k_norms)[:, first:first + n_tok]
+    assert np.max(np.abs(norms - n_ref) / n_ref) < 2e-6
+    vref, vn_ref, vy = _encode_ref_thr(v, rot, T32)
+    _boundary_mismatch_ok(R.unpack_tiles(_np(cache.v_codes))[:, first:first + n_tok], vref, vy, vn_ref)
+
+
+def test_dequantize_k4_matches_oracle():
+    hkv, n = 2, 256
+    rot = iqinputs.rotation_params(29, 0, hkv)
+    x = iqinputs.kv(29, 0, "k", n, hkv, "fixed_x8", "f32")
+    k16, kn = R.encode_codes(x, rot, T16)
+    v8, vn = R.encode_codes(x, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, n, _t(rot), k_bits=4)
+    cache.k_codes.copy_(_t(R.pack(k16, 4)))
+    cache.v_codes.copy_(_t(R.pack_tiles(v8)))
+    cache.k_norms.copy_(_t(kn))
+    cache.v_norms.copy_(_t(vn))
+    k_out, v_out = iq.iq_dequantize(cache, 0, n)
+    k_out, v_out = _np(k_out).astype(np.float64), _np(v_out).astype(np.float64)
+    for h in range(hkv):
+        assert np.max(np.abs(k_out[:, h] - R.dequantize_codes(k16[h], kn[h], rot[h], C16)) / kn[h, :, None]) < 2e-6
+        assert np.max(np.abs(v_out[:, h] - R.dequantize_codes(v8[h], vn[h], rot[h], C32)) / vn[h, :, None]) < 2e-6
+
+
+@pytest.mark.parametrize("kind", ["wht_so4", "planar"])
+@pytest.mark.parametrize("hq,hkv,lens", [(32, 4, [2100]), (8, 2, [0, 700, 1300]), (16, 1, [513, 3]),
+                                         (32, 8, [13, 4096]), (4, 4, [300])])
+def test_decode_k4_matches_oracle(kind, hq, hkv, lens):
+    lens = np.array(lens, np.int32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    total = int(lens.sum()) + 3
+    cap = -(-total // 32) * 32
+    rot = iqinputs.rotation_params_kind(hq + 5 * hkv, 0, hkv, kind)
+    k = np.zeros((cap, hkv, 128), np.float16)
+    v = np.zeros_like(k)
+    k[:total] = iqinputs.kv(hq, 3, "k", total, hkv, "student_t6", "f16")
+    v[:total] = iqinputs.kv(hq, 3, "v", total, hkv, "student_t6", "f16")
+    kr, kn = R.encode_tokens(k, rot, T16)
+    vt, vn = R.encode_tokens_v(v, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=4)
+    cache.k_codes.copy_(_t(kr))
+    cache.v_codes.copy_(_t(vt))
+    cache.k_norms.copy_(_t(kn))
+    cache.v_norms.copy_(_t(vn))
+    q = iqinputs.queries(hq, 4, len(lens), hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), int(lens.max())))
+    ref = R.decode_attention(q, kr, kn, vt, vn, rot, starts, lens, SCALE, C32, k_centroids32=C16)
+    _assert_attention_close(out, ref, f"4-bit K {kind} hq={hq} hkv={hkv} lens={list(lens)}")
