@@ -123,6 +123,7 @@ def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, 
 
     n = 4 * n_layers
     variants = rotation_variants(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
+    k4 = k4_decode(iq, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
     r = {"layers_cycled": n_layers,
          "fused_packed_decode_us": round(fused_us, 3),
          "fused_packed_bytes_per_launch": hkv * T * 2 * ROW_BYTES,
@@ -130,7 +131,8 @@ def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, 
          "fp16_kv_bytes_per_launch": hkv * T * 2 * 256,
          "dequantize_to_fp16_us": round(time_per_call(torch, dequantize, n, stream), 3),
          "unfused_decode_us": round(time_per_call(torch, unfused, n, stream), 3),
-         "rotation_variants": variants}
+         "rotation_variants": variants,
+         "k4_v3": k4}
     del k16, v16, dk, dv
     return r
 
@@ -163,6 +165,25 @@ def rotation_variants(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synt
         res[kind] = {"decode_us": round(time_per_call(torch, dec, 2 * n_layers, stream), 3),
                      "append_1_token_us": round(time_per_call(torch, app, 2 * n_layers, stream), 3)}
     return res
+
+
+def k4_decode(iq, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, n_layers=24):
+    """Decode with 4-bit K and 3-bit V (120 B per token and KV head) over n_layers caches."""
+    import torch
+    import iqinputs
+    cs = []
+    for l in range(n_layers):
+        rot = torch.from_numpy(iqinputs.rotation_params(9, l, hkv)).to(qs[0].device)
+        c = iq.PackedKVCache.allocate(hkv, T, rot, device=rot.device, k_bits=4)
+        iq.iq_rotate_quantize_append(c, synth_kv(T, 80_000 + l), synth_kv(T, 90_000 + l), first_slot=0,
+                                     stream=stream)
+        cs.append(c)
+
+    def dec(i):
+        l = i % n_layers
+        iq.iq_decode_attention(cs[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
+    return {"decode_us": round(time_per_call(torch, dec, 2 * n_layers, stream), 3),
+            "bytes_per_launch": hkv * T * (64 + 4 + 48 + 4)}
 
 
 def cpu_baseline(w, budget_s: float):
