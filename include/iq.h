@@ -207,6 +207,24 @@ IQ_API iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t t
                                   int32_t max_seq_len, float scale, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* One decode step: append one new token per sequence and attend to the cache
+ * including it, in the two launches of iq_decode_attention (the new token is
+ * encoded and scored by the merge kernel). Equivalent to
+ * iq_rotate_quantize_append of token s at slot seq_start[s] + seq_len[s]
+ * followed by iq_decode_attention over seq_len[s] + 1 slots (the codes and
+ * norms written are the same):
+ *   k_new, v_new  device [n_seqs][num_kv_heads][128] of in_dtype, 16-byte aligned.
+ *   seq_len       device int32 [n_seqs]: tokens already in the cache (<=
+ *                 max_seq_len); the new token's slot must be < capacity.
+ *   other arguments as for iq_decode_attention (same workspace size).
+ * Sequences must not share the new token's slot. A sequence whose rows or new
+ * slot fall outside the cache gets NaN outputs and nothing is written for it. */
+IQ_API iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_new, const void* v_new,
+                                     iq_dtype in_dtype, const float* q, int32_t num_q_heads,
+                                     const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                                     int32_t max_seq_len, float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace iq_decode_attention_deferred needs (0 if invalid). */
 IQ_API size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t max_prefix_len, int32_t max_seq_len);

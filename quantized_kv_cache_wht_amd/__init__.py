@@ -95,6 +95,11 @@ _SIGNATURES = {
                                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                                     ctypes.c_size_t, ctypes.c_void_p]),
+    "iq_append_decode_attention": (ctypes.c_int, [ctypes.POINTER(CacheView), ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p]),
     "iq_decode_attention_f16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -383,4 +388,30 @@ def iq_decode_attention_deferred(cache: PackedKVCache, seq_start: torch.Tensor, 
                                               _dev(out, torch.float32, "out"),
                                               _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                               _stream(stream)))
+    return out
+
+
+def iq_append_decode_attention(cache: PackedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                               seq_start: torch.Tensor, seq_len: torch.Tensor, max_seq_len: int,
+                               scale: float | None = None, out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step: token s of k_new/v_new [n_seqs][Hkv][128] goes to slot seq_start[s] + seq_len[s]
+    (seq_len = tokens already cached) and the attention covers seq_len[s] + 1 slots."""
+    n_seqs, hq, _ = q.shape
+    dt = _in_dtype(k_new)
+    if v_new.dtype != k_new.dtype or v_new.shape != k_new.shape or k_new.shape[0] != n_seqs:
+        raise ValueError("k_new and v_new must be matching [n_seqs][Hkv][128] tensors")
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        workspace = decode_workspace(n_seqs, hq, cache.num_kv_heads, max_seq_len, q.device)
+    view = cache.view()
+    _check("iq_append_decode_attention",
+           lib().iq_append_decode_attention(ctypes.byref(view), _dev(k_new, k_new.dtype, "k_new"),
+                                            _dev(v_new, v_new.dtype, "v_new"), dt, _dev(q, torch.float32, "q"), hq,
+                                            _dev(seq_start, torch.int32, "seq_start"),
+                                            _dev(seq_len, torch.int32, "seq_len"), n_seqs, max_seq_len, scale,
+                                            _dev(out, torch.float32, "out"),
+                                            _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                            _stream(stream)))
     return out

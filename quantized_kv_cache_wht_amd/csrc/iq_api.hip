@@ -298,6 +298,72 @@ iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t token_st
   return hip_status(launch_decode_f16(a, static_cast<hipStream_t>(stream)));
 }
 
+iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_new, const void* v_new,
+                                     iq_dtype in_dtype, const float* q, int32_t num_q_heads, const int32_t* seq_start,
+                                     const int32_t* seq_len, int32_t n_seqs, int32_t max_seq_len, float scale,
+                                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  iq_status st = check_view(view);
+  if (st != IQ_OK) return st;
+  if (in_dtype != IQ_F32 && in_dtype != IQ_F16) return IQ_ERR_INVALID_ARG;
+  if (n_seqs < 0 || max_seq_len < 0 || num_q_heads < 1) return IQ_ERR_INVALID_ARG;
+  if (num_q_heads % view->num_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / view->num_kv_heads;
+  if (!group_supported(group)) return IQ_ERR_UNSUPPORTED;
+  if (n_seqs == 0) return IQ_OK;
+  if (!k_new || !v_new || !q || !seq_start || !seq_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15u)
+    return IQ_ERR_INVALID_ARG;
+  if (n_seqs > 65535 || view->num_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  const DecodePlan plan = decode_plan(n_seqs, view->num_kv_heads, max_seq_len);
+  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.k_codes = view->k_codes;
+  a.v_codes = view->v_codes;
+  a.k_norms = view->k_norms;
+  a.v_norms = view->v_norms;
+  a.rot = view->rot;
+  a.rot_kind = view->rotation;
+  a.k_bits = view->k_bits;
+  a.q = q;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.n_seqs = n_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = view->num_kv_heads;
+  a.group = group;
+  a.capacity = view->capacity;
+  a.max_seq_len = max_seq_len;
+  a.blocks_per_split = plan.blocks_per_split;
+  a.n_splits = plan.n_splits;
+  a.rec_offset = 0;
+  a.rec_splits = plan.n_splits;
+  a.qscale = scale * 1.4426950408889634f;
+  a.cb = codebook();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_decode_splits(a, hs);
+  if (e != hipSuccess) return IQ_ERR_HIP;
+  MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, {}};
+  m.seg[0] = MergeSegment{a.seq_start, a.seq_len, a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits, 0};
+  MergeAppend n{};
+  n.k_new = k_new;
+  n.v_new = v_new;
+  n.new_f16 = in_dtype == IQ_F16 ? 1 : 0;
+  n.k_bits = view->k_bits;
+  n.num_kv_heads = view->num_kv_heads;
+  n.cache_capacity = view->capacity;
+  n.k_codes = view->k_codes;
+  n.v_codes = view->v_codes;
+  n.k_norms = view->k_norms;
+  n.v_norms = view->v_norms;
+  n.q = q;
+  n.qscale = a.qscale;
+  n.cb = a.cb;
+  return hip_status(launch_merge_append(m, n, hs));
+}
+
 size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t max_prefix_len, int32_t max_seq_len) {
   if (n_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_prefix_len < 0 || max_seq_len < 0) return 0;

@@ -50,6 +50,11 @@ __device__ __forceinline__ float dpp_f32(float x) {
 }
 
 template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, false));
+}
+
+template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
   const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), kCtrl, 0xF, 0xF, false);
@@ -87,8 +92,13 @@ __device__ __forceinline__ void wht128_quad(float (&x)[kPerLane], int part) {
 }
 
 // ------------------------------------------------------------- SO(4) ----
+// The block matrices are built without multiply-add contraction, so that
+// every kernel that builds them (each in its own inlining context) gets the
+// same bits and the encode is identical wherever it runs.
+
 // Hamilton product of quaternions (w, x, y, z).
 __device__ __forceinline__ void qmul(const float a[4], const float b[4], float r[4]) {
+#pragma clang fp contract(off)
   r[0] = a[0] * b[0] - a[1] * b[1] - a[2] * b[2] - a[3] * b[3];
   r[1] = a[0] * b[1] + a[1] * b[0] + a[2] * b[3] - a[3] * b[2];
   r[2] = a[0] * b[2] - a[1] * b[3] + a[2] * b[0] + a[3] * b[1];
@@ -98,6 +108,7 @@ __device__ __forceinline__ void qmul(const float a[4], const float b[4], float r
 // Row-major 4x4 matrix of v -> qL (x) v (x) conj(qR), times `scale`, from the
 // 8 stored parameters of one block (quaternions renormalised here).
 __device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m[16]) {
+#pragma clang fp contract(off)
   float ql[4], qr[4];
   float nl = 0.f, nr = 0.f;
 #pragma unroll
@@ -142,6 +153,7 @@ __device__ __forceinline__ const float* rot_of_head(const float* rot, int kind, 
 
 // Row-major matrix of v -> q (x) v from 4 stored parameters (q renormalised).
 __device__ __forceinline__ void iso_matrix(const float* p4, float m[16]) {
+#pragma clang fp contract(off)
   float q[4];
   float nq = 0.f;
 #pragma unroll
@@ -165,6 +177,7 @@ __device__ __forceinline__ void iso_matrix(const float* p4, float m[16]) {
 
 // Row-major matrix of two Givens rotations (c0, s0), (c1, s1) (each pair renormalised).
 __device__ __forceinline__ void givens_matrix(const float* p4, float m[16]) {
+#pragma clang fp contract(off)
   const float n0 = 1.0f / sqrtf(p4[0] * p4[0] + p4[1] * p4[1]);
   const float n1 = 1.0f / sqrtf(p4[2] * p4[2] + p4[3] * p4[3]);
   const float c0 = p4[0] * n0, s0 = p4[1] * n0, c1 = p4[2] * n1, s1 = p4[3] * n1;

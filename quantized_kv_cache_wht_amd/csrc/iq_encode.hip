@@ -317,10 +317,6 @@ __device__ __forceinline__ void load8<_Float16>(const _Float16* __restrict__ src
   for (int j = 0; j < 8; ++j) x[j] = static_cast<float>(v[j]);
 }
 
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, false));
-}
 
 template <typename T>
 __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {

@@ -143,6 +143,25 @@ struct MergeArgs {
   MergeSegment seg[2];
 };
 
+// The decode step's new token, encoded and attended to by the merge kernel
+// (iq_append_decode_attention): token s goes to cache slot seq_start[s] +
+// seq_len[s] of segment 0 and joins that sequence's attention.
+struct MergeAppend {
+  const void* k_new;     // [n_seqs][Hkv][128], fp16 or fp32
+  const void* v_new;
+  int32_t new_f16;
+  int32_t k_bits;
+  int32_t num_kv_heads;
+  int32_t cache_capacity;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_norms;
+  float* v_norms;
+  const float* q;
+  float qscale;
+  Codebook cb;
+};
+
 hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s);
 hipError_t launch_rotate(const RotateArgs& a, bool inverse, hipStream_t s);
 hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
@@ -160,5 +179,8 @@ hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t s);
 // fp16 prefix and packed suffix in one split launch, then the merge
 hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_merge_append(const MergeArgs& a, const MergeAppend& n, hipStream_t s);
+// split kernels only (the packed decode's first launch)
+hipError_t launch_decode_splits(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace iq

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     h = ctypes.CDLL(iq.library_path())
     for n in names:
         assert hasattr(h, n), n
@@ -115,6 +115,22 @@ def test_decode_f16_validation():
     assert call(k=None) == -1
     assert call(n=0) == 0
     assert call(hkv=0) == -1
+
+
+def test_append_decode_validation():
+    L = iq.lib()
+    v = _view(hkv=2)
+    p = ctypes.c_void_p(0x70000)
+    need = L.iq_decode_workspace_bytes(1, 8, 2, 100)
+
+    def call(dt=1, hq=8, ws=need, n=1, kn=p):
+        return L.iq_append_decode_attention(ctypes.byref(v), kn, p, dt, p, hq, p, p, n, 100, 0.1, p, p, ws, None)
+    assert call(dt=5) == -1
+    assert call(hq=6) == -2
+    assert call(ws=need - 1) == -4
+    assert call(kn=None) == -1
+    assert call(kn=ctypes.c_void_p(0x70004)) == -1
+    assert call(n=0) == 0
 
 
 def test_decode_deferred_validation():

