@@ -5,18 +5,22 @@ context, 48 layers, 32 query heads, 4 KV heads, head dim 128, batch 1, K/V
 fp16 with four fixed outlier channels x8 (synthetic, seeded). Untimed set-up
 fills every layer's packed cache with 32767 tokens through the library's own
 bulk encode. One timed step = for each of the 48 layers: encode and append
-one new token (K and V) and run decode attention over the full 32768-token
-packed cache. The 96 launches of a step are captured once as a HIP graph and
-the graph is replayed per step (--eager launches them one by one); every
-replay's outputs are compared with an eager step's, bit for bit.
+one new token (K and V) at slot 32767 and run decode attention over all 32768
+packed tokens, as one iq_append_decode_attention call (a split-K launch whose
+extra work-groups encode the new token beside the splits, then the merge). The 96 launches of a step are
+captured once as a HIP graph and replayed per step (--eager launches them one
+by one); every warm-up replay and the last timed one are compared bit for bit
+with an eager step.
 
-Printed JSON line: value = packed K/V bytes read by the decode per step /
-step time (GB/s); roofline = the decode launch (split + merge kernels; HIP
-events on the launch stream around runs of back-to-back launches) against the
-8 TB/s HBM peak, with the HBM traffic per launch from the committed counter
-summary when it matches the decode sources;
-cpu_baseline = the CPU oracle's decode on a bounded sample of the same
-workload. The quantize-append rate is measured on the set-up's bulk encode.
+Printed JSON line: value = packed K/V bytes of the attended tokens per step /
+step time (GB/s); roofline = the step's launch pair (split + merge kernels;
+HIP events on the launch stream around runs of back-to-back launches) against
+the 8 TB/s HBM peak, with the HBM traffic per launch from the committed
+counter summary when it matches the decode sources; comparisons = decode
+alone, append + decode as two calls, the FP16-KV and unfused paths, the
+rotation variants and 4-bit K; cpu_baseline = the CPU oracle's decode on a
+bounded sample of the same workload. The quantize-append rate is measured on
+the set-up's bulk encode.
 """
 from __future__ import annotations
 
@@ -56,7 +60,7 @@ def decode_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_wht_amd", "csrc")
     for name in ("iq_decode.hip", "iq_decode_common.h", "iq_decode_packed.h", "iq_decode_packed_body.inc",
-                 "iq_device.h", "iq_launch.h"):
+                 "iq_decode_new_token.h", "iq_device.h", "iq_launch.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -97,7 +101,8 @@ def time_per_call(torch, fn, n_calls, stream):
     return e0.elapsed_time(e1) * 1e3 / n_calls
 
 
-def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, fused_us, n_layers=8):
+def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, fused_us, new_k, new_v,
+                n_layers=8):
     """The pages' comparisons on this workload's decode, over n_layers layers' caches in turn:
     the same decode over an fp16 K/V cache (FP16-KV baseline, K/V of the same shape and value
     model), and the unfused path (iq_dequantize of the packed cache to fp16, then that decode)."""
@@ -122,11 +127,23 @@ def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, 
                                    workspace=ws, stream=stream)
 
     n = 4 * n_layers
+
+    def decode_only(i):
+        l = i % n_layers
+        iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
+
+    def append_then_decode(i):
+        l = i % n_layers
+        iq.iq_rotate_quantize_append(caches[l], new_k[l], new_v[l], first_slot=T - 1, stream=stream)
+        decode_only(i)
+
     variants = rotation_variants(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
     k4 = k4_decode(iq, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
     r = {"layers_cycled": n_layers,
-         "fused_packed_decode_us": round(fused_us, 3),
-         "fused_packed_bytes_per_launch": hkv * T * 2 * ROW_BYTES,
+         "fused_step_us": round(fused_us, 3),
+         "decode_only_us": round(time_per_call(torch, decode_only, n, stream), 3),
+         "append_then_decode_us": round(time_per_call(torch, append_then_decode, n, stream), 3),
+         "packed_bytes_per_launch": hkv * T * 2 * ROW_BYTES,
          "fp16_kv_decode_us": round(time_per_call(torch, fp16_decode, n, stream), 3),
          "fp16_kv_bytes_per_launch": hkv * T * 2 * 256,
          "dequantize_to_fp16_us": round(time_per_call(torch, dequantize, n, stream), 3),
@@ -273,14 +290,19 @@ def main():
     new_k = [synth_kv(1, 10_000 + l) for l in range(L)]
     new_v = [synth_kv(1, 20_000 + l) for l in range(L)]
     seq_start = torch.zeros(1, dtype=torch.int32, device=dev)
-    seq_len = torch.full((1,), T, dtype=torch.int32, device=dev)
+    seq_len = torch.full((1,), T, dtype=torch.int32, device=dev)          # after the step's append
+    cached = torch.full((1,), T - 1, dtype=torch.int32, device=dev)       # before it
     ws = iq.decode_workspace(1, hq, hkv, T, device=dev)
     outs = [torch.empty((1, hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
 
+    def step_layer(l, st):
+        # append the new token at slot T - 1 and attend to all T tokens (split + merge launches)
+        iq.iq_append_decode_attention(caches[l], new_k[l], new_v[l], qs[l], seq_start, cached, T - 1, out=outs[l],
+                                      workspace=ws, stream=st)
+
     def step(st):
         for l in range(L):
-            iq.iq_rotate_quantize_append(caches[l], new_k[l], new_v[l], first_slot=T - 1, stream=st)
-            iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=st)
+            step_layer(l, st)
 
     # eager reference of one step
     step(stream)
@@ -319,8 +341,9 @@ def main():
     bytes_per_step = L * bytes_per_launch
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # decode launches (split + merge kernels) timed with HIP events on their
-    # stream: each pair of events brackets one launch per layer, back to back,
+    # decode-step launches (split kernel with the new token's work-groups, then
+    # the merge) timed with HIP events on their stream: each pair of events
+    # brackets one launch pair per layer, back to back,
     # and a spin kernel queued first keeps the GPU busy while the host enqueues
     # them, so the events time the GPU, not the host's calls.
     reps = max(2, args.steps // 4)
@@ -329,14 +352,14 @@ def main():
     evs[0].record(stream)
     for r in range(reps):
         for l in range(L):
-            iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
+            step_layer(l, stream)
         evs[r + 1].record(stream)
     torch.cuda.synchronize()
     dec_us = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 / L for r in range(reps)])
     achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     comp = None if args.no_compare else comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv,
-                                                     T, hkv, float(dec_us.mean()))
+                                                     T, hkv, float(dec_us.mean()), new_k, new_v)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

@@ -1,7 +1,9 @@
 """Per-launch HBM traffic of the decode from two rocprofv3 counter runs of bench.py.
 
 Reads the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run (both of
-`bench.py --eager --copy-calibration-mib N`), scales each counter by what it
+`bench.py --eager --no-compare --copy-calibration-mib N`), takes the decode
+step's two kernels (the split kernel instantiated for the workload's group
+size with the new token's work-groups, and the merge), scales each counter by what it
 reads for the run's own device-to-device copies of N MiB (their true traffic
 is N MiB read and N MiB written), and writes the summary that bench.py reports
 as roofline.traffic when the decode sources still match.
@@ -62,14 +64,15 @@ def main():
     w_copy = sorted(pick(write, "copyBuffer"))[-3:]
     f_scale = copy_kib / statistics.mean(f_copy)
     w_scale = copy_kib / statistics.mean(w_copy)
+    w = iqinputs.WORKLOADS[a.workload]
+    group = w.num_q_heads // w.num_kv_heads
     rows = []
     total = 0.0
-    for label, needle in (("split", "decode_split_kernel"), ("merge", "decode_merge_kernel")):
+    for label, needle in (("split", f"decode_split_kernel<{group}, 3, true>"), ("merge", "decode_merge_kernel<true>")):
         f = statistics.mean(pick(fetch, needle)) * f_scale * 1024
         wv = statistics.mean(pick(write, needle)) * w_scale * 1024
         rows.append((label, f, wv))
         total += f + wv
-    w = iqinputs.WORKLOADS[a.workload]
     alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
     lines = [
         f"# HBM traffic per decode launch: {a.workload}",

@@ -154,8 +154,9 @@ IQ_API iq_status iq_rotate_quantize_append(const iq_cache_view* view, const void
 IQ_API iq_status iq_dequantize(const iq_cache_view* view, int32_t first_slot, int32_t n_tokens,
                         iq_dtype out_dtype, void* k_out, void* v_out, void* stream);
 
-/* Bytes of workspace iq_decode_attention needs for these sizes (0 if the
- * sizes are invalid). */
+/* Bytes of workspace iq_decode_attention, iq_decode_attention_f16 and
+ * iq_append_decode_attention need for these sizes (0 if the sizes are
+ * invalid). */
 IQ_API size_t iq_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_seq_len);
 
@@ -208,8 +209,9 @@ IQ_API iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t t
                                   size_t workspace_bytes, void* stream);
 
 /* One decode step: append one new token per sequence and attend to the cache
- * including it, in the two launches of iq_decode_attention (the new token is
- * encoded and scored by the merge kernel). Equivalent to
+ * including it, in the two launches of iq_decode_attention (extra
+ * work-groups of the first launch encode and score the new token beside the
+ * splits). Equivalent to
  * iq_rotate_quantize_append of token s at slot seq_start[s] + seq_len[s]
  * followed by iq_decode_attention over seq_len[s] + 1 slots (the codes and
  * norms written are the same):

@@ -315,8 +315,9 @@ iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_ne
        reinterpret_cast<uintptr_t>(workspace)) & 15u)
     return IQ_ERR_INVALID_ARG;
   if (n_seqs > 65535 || view->num_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
-  const DecodePlan plan = decode_plan(n_seqs, view->num_kv_heads, max_seq_len);
-  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, decode_plan(n_seqs, view->num_kv_heads, max_seq_len)))
+    return IQ_ERR_WORKSPACE;
+  const DecodePlan plan = decode_plan(n_seqs, view->num_kv_heads, max_seq_len, 1);
   DecodeArgs a{};
   a.k_codes = view->k_codes;
   a.v_codes = view->v_codes;
@@ -339,29 +340,23 @@ iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_ne
   a.blocks_per_split = plan.blocks_per_split;
   a.n_splits = plan.n_splits;
   a.rec_offset = 0;
-  a.rec_splits = plan.n_splits;
+  a.rec_splits = plan.n_splits + 1;   // the splits' records, then the new token's
   a.qscale = scale * 1.4426950408889634f;
   a.cb = codebook();
+  NewToken nt{};
+  nt.k_new = k_new;
+  nt.v_new = v_new;
+  nt.new_f16 = in_dtype == IQ_F16 ? 1 : 0;
+  nt.k_codes = view->k_codes;
+  nt.v_codes = view->v_codes;
+  nt.k_norms = view->k_norms;
+  nt.v_norms = view->v_norms;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode_splits(a, hs);
+  hipError_t e = launch_decode_splits_new(a, nt, hs);
   if (e != hipSuccess) return IQ_ERR_HIP;
-  MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, {}};
+  MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, plan.n_splits, {}};
   m.seg[0] = MergeSegment{a.seq_start, a.seq_len, a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits, 0};
-  MergeAppend n{};
-  n.k_new = k_new;
-  n.v_new = v_new;
-  n.new_f16 = in_dtype == IQ_F16 ? 1 : 0;
-  n.k_bits = view->k_bits;
-  n.num_kv_heads = view->num_kv_heads;
-  n.cache_capacity = view->capacity;
-  n.k_codes = view->k_codes;
-  n.v_codes = view->v_codes;
-  n.k_norms = view->k_norms;
-  n.v_norms = view->v_norms;
-  n.q = q;
-  n.qscale = a.qscale;
-  n.cb = a.cb;
-  return hip_status(launch_merge_append(m, n, hs));
+  return hip_status(launch_merge(m, hs));
 }
 
 size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,

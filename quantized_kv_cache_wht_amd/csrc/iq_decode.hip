@@ -35,15 +35,26 @@
 // p_t nV_t <= 256 and the fp16 operand never overflows while accumulator
 // rescaling is rare.
 #include "iq_decode_packed.h"
+#include "iq_decode_new_token.h"
 
 namespace iq {
 
 // work-groups go round-robin to the XCDs in launch order; with the split
 // index slowest (grid z), the live splits (short sequences have few) spread evenly
-template <int G, int KB>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a) {
+//
+// kNew: grid z has one more slice, dispatched first: z = 0 encodes the decode
+// step's new token (new_token_block) while the splits z - 1 run beside it.
+template <int G, int KB, bool kNew>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a, NewToken nt) {
   __shared__ PackedSmem<G, KB> sm;
-  const int split = blockIdx.z;
+  static_assert(sizeof(PackedSmem<G, KB>) >= sizeof(NewTokenSmem<G>), "new-token LDS must fit");
+  if constexpr (kNew) {
+    if (blockIdx.z == 0) {
+      new_token_block<G, KB>(a, nt, *reinterpret_cast<NewTokenSmem<G>*>(&sm));
+      return;
+    }
+  }
+  const int split = kNew ? blockIdx.z - 1 : blockIdx.z;
 #include "iq_decode_packed_body.inc"
 }
 
@@ -55,48 +66,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
 // a running merge of them, and parks the result in LDS; the 32 rows are then
 // combined with one row per lane of a half-wave. An empty sequence gives 0,
 // an invalid one NaN.
-// 8 dims of a new K or V vector (fp16 or fp32 input).
-__device__ __forceinline__ void load8_any(const void* base, size_t off, bool f16, float (&x)[8]) {
-  if (f16) {
-    const half8 v = *reinterpret_cast<const half8*>(static_cast<const _Float16*>(base) + off);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(v[i]);
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-}
-
-template <bool kRotate, bool kAppend>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a, MergeAppend nw) {
+template <bool kRotate>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
   __shared__ float rm[kMergeRows], rl[kMergeRows];
   __shared__ __align__(16) float ro[kMergeRows][kDim];
   __shared__ __align__(16) float fin[kDim];
-  __shared__ __align__(16) float kcv[kDim], onew[kDim];   // new token: K centroids, rotated V record
-  __shared__ float s_new;
   const int hq = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
   const int h = hq / a.group;
-  // lanes 0..15: the output's inverse rotation; with a new token, rows of 16
-  // lanes 0..15 / 16..31 / 32..47 also rotate its K, its V and the query
-  float rp[16], xn[8];
-  const int nrow = tid >> 4, np = tid & 15;
-  if (kRotate && tid < (kAppend ? 48 : 16)) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, np, rp);
-  if (kAppend && tid < 48) {
-    if (nrow < 2) {
-      load8_any(nrow == 0 ? nw.k_new : nw.v_new, (static_cast<size_t>(s) * nw.num_kv_heads + h) * kDim + 8 * np,
-                nw.new_f16 != 0, xn);
-    } else {
-      const float4* qp = reinterpret_cast<const float4*>(nw.q + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + 8 * np);
-      const float4 q0 = qp[0], q1 = qp[1];
-      xn[0] = q0.x; xn[1] = q0.y; xn[2] = q0.z; xn[3] = q0.w; xn[4] = q1.x; xn[5] = q1.y; xn[6] = q1.z; xn[7] = q1.w;
-    }
-  }
+  float rp[16];
+  if (kRotate && tid < 16) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid, rp);
   // Record positions: segment 0 at [0, n_splits0), segment 1 (if any) from
-  // split_offset on. The first round of record loads goes out before the
-  // sequence bounds are read (two round trips would otherwise follow each
-  // other); records past a segment's live splits are stale and masked out.
+  // split_offset on, the new token's (if any) at extra_rec. The first round
+  // of record loads goes out before the sequence bounds are read (two round
+  // trips would otherwise follow each other); records past a segment's live
+  // splits are stale and masked out.
   const float* recs = a.ws + (static_cast<size_t>(s) * a.num_q_heads + hq) * a.rec_splits * kRec;
   float mv[kMergeChunk], lv[kMergeChunk];
   float4 ov[kMergeChunk];
@@ -121,101 +105,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
     if (g == 0) live0 = live; else live1 = live;
   }
   const int off1 = a.n_segments > 1 ? a.seg[1].split_offset : a.rec_splits;
-  auto live_at = [&](int p) { return p < live0 || (p >= off1 && p - off1 < live1); };
-  if (kAppend && tid < 48) {
-    float m[32];
-    so4_matrices_row(a.rot_kind, rp, m);
-    // ---- the new token: encode K and V (as iq_rotate_quantize_append does), score it ----
-    const int nslot = a.seg[0].seq_start[s] + a.seg[0].seq_len[s];
-    const bool nvalid = ok && nslot >= 0 && nslot < nw.cache_capacity;
-    if (ok && !nvalid) ok = false;
-    if (a.rot_kind == kRotWhtSo4) wht128_row(xn, np);
-    so4_apply_row<false>(xn, m);
-    const bool writer = nvalid && (hq % a.group) == 0;   // one query head of the group stores the codes
-    const size_t crow = static_cast<size_t>(h) * nw.cache_capacity + (nvalid ? nslot : 0);
-    if (nrow == 0) {
-      const float n = row_norm(xn);
-      float cv[8];
-      if (nw.k_bits == 4) {
-        float tp[7];
-#pragma unroll
-        for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(nw.cb.t4[8 + k], n);
-        uint32_t w = 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t c = code16_of(xn[i], tp);
-          w |= c << (4 * i);
-          cv[i] = centroid16(c, nw.cb);
-        }
-        if (writer) reinterpret_cast<uint32_t*>(nw.k_codes + crow * k_row_bytes(4))[np] = w;
-      } else {
-        const float t4 = __fmul_rn(nw.cb.t[4], n), t5 = __fmul_rn(nw.cb.t[5], n), t6 = __fmul_rn(nw.cb.t[6], n);
-        uint32_t b24 = 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t c = code_of(xn[i], t4, t5, t6);
-          b24 |= c << (3 * i);
-          cv[i] = centroid(c, nw.cb);
-        }
-        const uint32_t b1 = dpp_u32<kQuadXor1>(b24), b2 = dpp_u32<kQuadXor2>(b24), b3 = dpp_u32<kQuadXor3>(b24);
-        if (writer && (np & 3) == 0) {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(nw.k_codes + crow * k_row_bytes(3)) + 3 * (np >> 2);
-          dst[0] = b24 | (b1 << 24);
-          dst[1] = (b1 >> 8) | (b2 << 16);
-          dst[2] = (b2 >> 16) | (b3 << 8);
-        }
-      }
-      if (writer && np == 0) nw.k_norms[crow] = n;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kcv[8 * np + i] = cv[i] * n;
-    } else if (nrow == 1) {
-      const float n = row_norm(xn);
-      const float t4 = __fmul_rn(nw.cb.t[4], n), t5 = __fmul_rn(nw.cb.t[5], n), t6 = __fmul_rn(nw.cb.t[6], n);
-      uint32_t c[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        c[i] = code_of(xn[i], t4, t5, t6);
-        onew[8 * np + i] = centroid(c[i], nw.cb) * n;
-      }
-      if (writer) {
-        if (np == 0) nw.v_norms[crow] = n;
-        // V tile: dim j of slot r at bit 24 j + 3 r; this lane's dims are dwords 6np .. 6np+5
-        uint32_t* tile = reinterpret_cast<uint32_t*>(nw.v_codes + (crow / kTile) * kTileBytes) + 6 * np;
-        const int r3 = 3 * (nslot & (kTile - 1));
-        uint32_t nb[6] = {0u, 0u, 0u, 0u, 0u, 0u}, mk[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t f = c[i] << r3, fm = 7u << r3;
-          const int pos = 24 * i, wd = pos >> 5, off = pos & 31;
-          nb[wd] |= f << off;
-          mk[wd] |= fm << off;
-          if (off > 8) {
-            nb[wd + 1] |= f >> (32 - off);
-            mk[wd + 1] |= fm >> (32 - off);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < 6; ++k) {
-          atomicAnd(tile + k, ~mk[k]);
-          atomicOr(tile + k, nb[k]);
-        }
-      }
-    }
-    // same wave: K's centroids are in LDS before the query rows read them
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (nrow == 2) {
-      float d = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) d = __builtin_fmaf(xn[i], kcv[8 * np + i], d);
-      d += row_xor<8>(d);
-      d += row_xor<4>(d);
-      d += row_xor<2>(d);
-      d += row_xor<1>(d);
-      if (np == 0) s_new = nw.qscale * d;
-    }
-  }
+  auto live_at = [&](int p) { return p < live0 || (p >= off1 && p - off1 < live1) || p == a.extra_rec; };
   float mx = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int p0 = row;; p0 += kMergeRows * kMergeChunk) {
@@ -274,20 +164,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
     const float o2 = half_wave_reduce<false>(w * v.z);
     const float o3 = half_wave_reduce<false>(w * v.w);
     if (r == 0) {
-      if (kAppend) {
-        // the new token as one more record: m = its score, l = 1, o' = its rotated V
-        const float sn = s_new;
-        const float M2 = fmaxf(M, sn);
-        const float wa = M == -INFINITY ? 0.f : fast_exp2(M - M2), wb = fast_exp2(sn - M2);
-        const float4 on = reinterpret_cast<const float4*>(onew)[c];
-        const float L2 = wa * L + wb;
-        const float inv = 1.0f / L2;
-        reinterpret_cast<float4*>(fin)[c] = make_float4((wa * o0 + wb * on.x) * inv, (wa * o1 + wb * on.y) * inv,
-                                                        (wa * o2 + wb * on.z) * inv, (wa * o3 + wb * on.w) * inv);
-      } else {
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        reinterpret_cast<float4*>(fin)[c] = make_float4(o0 * inv, o1 * inv, o2 * inv, o3 * inv);
-      }
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      reinterpret_cast<float4*>(fin)[c] = make_float4(o0 * inv, o1 * inv, o2 * inv, o3 * inv);
     }
   }
   __syncthreads();
@@ -305,12 +183,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   }
 }
 
-DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t extra_per_pair) {
   DecodePlan p{};
   // blocks of a 32-aligned start; a misaligned one adds a block, which the last split takes
   const int64_t blocks = (static_cast<int64_t>(max_seq_len > 0 ? max_seq_len : 1) + kBlk - 1) / kBlk;
   const int64_t pairs = static_cast<int64_t>(n_seqs > 0 ? n_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-  const int64_t want_splits = (kTargetBlocks + pairs - 1) / pairs;
+  // the launch's other work-groups (the new token's) take resident slots too
+  int64_t want_splits = (kTargetBlocks + pairs - 1) / pairs - extra_per_pair;
+  if (want_splits < 1) want_splits = 1;
   int64_t bps = (blocks + want_splits - 1) / want_splits;
   if (bps < kMinBlocksPerSplit) bps = kMinBlocksPerSplit;
   const int64_t cap = n_seqs > 1 ? kMaxBlocksPerSplitMany : kMaxBlocksPerSplitOne;
@@ -327,25 +207,30 @@ DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len
 }
 
 size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodePlan& p) {
-  return static_cast<size_t>(n_seqs) * num_q_heads * p.n_splits * kRec * sizeof(float);
+  return static_cast<size_t>(n_seqs) * num_q_heads * (p.n_splits + 1) * kRec * sizeof(float);
 }
 
-template <int KB>
-static hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.num_kv_heads, a.n_seqs, a.n_splits);
+template <int KB, bool kNew>
+static hipError_t launch_split(const DecodeArgs& a, const NewToken& nt, hipStream_t st) {
+  dim3 grid(a.num_kv_heads, a.n_seqs, a.n_splits + (kNew ? 1 : 0));
   switch (a.group) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<1, KB>), grid, dim3(kDecThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<2, KB>), grid, dim3(kDecThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<4, KB>), grid, dim3(kDecThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((decode_split_kernel<8, KB>), grid, dim3(kDecThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((decode_split_kernel<16, KB>), grid, dim3(kDecThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<1, KB, kNew>), grid, dim3(kDecThreads), 0, st, a, nt); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<2, KB, kNew>), grid, dim3(kDecThreads), 0, st, a, nt); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<4, KB, kNew>), grid, dim3(kDecThreads), 0, st, a, nt); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<8, KB, kNew>), grid, dim3(kDecThreads), 0, st, a, nt); break;
+    case 16: hipLaunchKernelGGL((decode_split_kernel<16, KB, kNew>), grid, dim3(kDecThreads), 0, st, a, nt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_splits(const DecodeArgs& a, hipStream_t st) {
-  return a.k_bits == 4 ? launch_split<4>(a, st) : launch_split<3>(a, st);
+  const NewToken none{};
+  return a.k_bits == 4 ? launch_split<4, false>(a, none, st) : launch_split<3, false>(a, none, st);
+}
+
+hipError_t launch_decode_splits_new(const DecodeArgs& a, const NewToken& nt, hipStream_t st) {
+  return a.k_bits == 4 ? launch_split<4, true>(a, nt, st) : launch_split<3, true>(a, nt, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
@@ -353,24 +238,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (le != hipSuccess) return le;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, {}};
+  MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, -1, {}};
   m.seg[0] = MergeSegment{a.seq_start, a.seq_len, a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits, 0};
   return launch_merge(m, st);
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
-  const MergeAppend none{};
   if (a.rot != nullptr)
-    hipLaunchKernelGGL((decode_merge_kernel<true, false>), dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st,
-                       a, none);
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<false, false>), dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st,
-                       a, none);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge_append(const MergeArgs& a, const MergeAppend& n, hipStream_t st) {
-  hipLaunchKernelGGL((decode_merge_kernel<true, true>), dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a, n);
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -423,7 +423,7 @@ hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& su
   if (le != hipSuccess) return le;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{suf.rot_kind, suf.rot, suf.out, suf.ws, suf.n_seqs, suf.num_q_heads, suf.group, suf.rec_splits, 2, {}};
+  MergeArgs m{suf.rot_kind, suf.rot, suf.out, suf.ws, suf.n_seqs, suf.num_q_heads, suf.group, suf.rec_splits, 2, -1, {}};
   m.seg[0] = MergeSegment{pre.seq_start, pre.seq_len, pre.capacity, pre.max_seq_len, pre.blocks_per_split,
                           pre.n_splits, 0};
   m.seg[1] = MergeSegment{suf.seq_start, suf.seq_len, suf.capacity, suf.max_seq_len, suf.blocks_per_split,
@@ -443,7 +443,7 @@ hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MergeArgs m{kRotWhtSo4, nullptr, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, {}};
+  MergeArgs m{kRotWhtSo4, nullptr, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, -1, {}};
   m.seg[0] = MergeSegment{a.seq_start, a.seq_len, a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits, 0};
   return launch_merge(m, st);
 }

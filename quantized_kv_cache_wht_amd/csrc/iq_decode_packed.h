@@ -119,7 +119,7 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
   IQ_SCORE(0) IQ_SCORE(1) IQ_SCORE(2) IQ_SCORE(3) IQ_SCORE(4) IQ_SCORE(5) IQ_SCORE(6) IQ_SCORE(7)
 #undef IQ_SCORE
   const float nk[8] = {cur.nk0.x, cur.nk0.y, cur.nk0.z, cur.nk0.w, cur.nk1.x, cur.nk1.y, cur.nk1.z, cur.nk1.w};
-  const float nv[8] = {cur.nv0.x, cur.nv0.y, cur.nv0.z, cur.nv0.w, cur.nv1.x, cur.nv1.y, cur.nv1.z, cur.nv1.w};
+  float nv[8] = {cur.nv0.x, cur.nv0.y, cur.nv0.z, cur.nv0.w, cur.nv1.x, cur.nv1.y, cur.nv1.z, cur.nv1.w};
   float t[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -142,7 +142,8 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
       const int rel = slot0 + 8 * q + k;
       const bool valid = rel >= c.rel_lo && rel < c.rel_hi;
       t[k] = valid ? t[k] : -INFINITY;    // 2^-inf = 0 below
-      nvmax = fmaxf(nvmax, valid ? nv[k] : 0.f);
+      nv[k] = valid ? nv[k] : 0.f;        // a slot outside the range may hold anything
+      nvmax = fmaxf(nvmax, nv[k]);
     }
   }
   // ---- online softmax with a lazily raised reference ----

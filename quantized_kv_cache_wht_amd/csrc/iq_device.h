@@ -381,13 +381,28 @@ __device__ __forceinline__ uint32_t code16_of(float y, const float (&tp)[7]) {
   return 7u - at_or_above;
 }
 
+// A wave-uniform codebook entry as a register value. Without it the compiler
+// may turn a select between two entries of a by-value kernel argument into a
+// select of their addresses and a vector load from the argument segment, one
+// round trip to memory per element. (Read every entry unconditionally, then
+// select: the read is not speculated into a conditional one.)
+__device__ __forceinline__ float cb_value(float x) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
+}
+__device__ __forceinline__ uint32_t cb_value(uint16_t x) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+}
+
 // Centroid of a 16-level code by selects: c4[v] = c4[8 + (v - 8)] for v >= 8,
 // -c4[8 + (7 - v)] otherwise.
 __device__ __forceinline__ float centroid16(uint32_t v, const Codebook& cb) {
   const bool neg = v < 8u;
   const uint32_t m = neg ? 7u - v : v - 8u;
-  const float a0 = (m & 1u) ? cb.c4[9] : cb.c4[8], a1 = (m & 1u) ? cb.c4[11] : cb.c4[10];
-  const float a2 = (m & 1u) ? cb.c4[13] : cb.c4[12], a3 = (m & 1u) ? cb.c4[15] : cb.c4[14];
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = cb_value(cb.c4[8 + i]);
+  const float a0 = (m & 1u) ? e[1] : e[0], a1 = (m & 1u) ? e[3] : e[2];
+  const float a2 = (m & 1u) ? e[5] : e[4], a3 = (m & 1u) ? e[7] : e[6];
   const float b0 = (m & 2u) ? a1 : a0, b1 = (m & 2u) ? a3 : a2;
   const float mag = (m & 4u) ? b1 : b0;
   return neg ? -mag : mag;
@@ -399,8 +414,11 @@ __device__ __forceinline__ uint32_t centroid16_f16(uint32_t v, const Codebook& c
   const uint16_t* t = kLo ? cb.l16k : cb.h16k;
   const bool neg = v < 8u;
   const uint32_t m = neg ? 7u - v : v - 8u;
-  const uint32_t a0 = (m & 1u) ? t[1] : t[0], a1 = (m & 1u) ? t[3] : t[2];
-  const uint32_t a2 = (m & 1u) ? t[5] : t[4], a3 = (m & 1u) ? t[7] : t[6];
+  uint32_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = cb_value(t[i]);
+  const uint32_t a0 = (m & 1u) ? e[1] : e[0], a1 = (m & 1u) ? e[3] : e[2];
+  const uint32_t a2 = (m & 1u) ? e[5] : e[4], a3 = (m & 1u) ? e[7] : e[6];
   const uint32_t b0 = (m & 2u) ? a1 : a0, b1 = (m & 2u) ? a3 : a2;
   const uint32_t mag = (m & 4u) ? b1 : b0;
   return neg ? (mag ^ 0x8000u) : mag;
@@ -438,8 +456,9 @@ __device__ __forceinline__ float centroid(uint32_t v, const Codebook& cb) {
   const uint32_t m = v & 3u;
   const bool neg = v < 4u;
   const uint32_t idx = neg ? (3u - m) : m;
-  const float lo = (idx & 1u) ? cb.c[5] : cb.c[4];
-  const float hi = (idx & 1u) ? cb.c[7] : cb.c[6];
+  const float e4 = cb_value(cb.c[4]), e5 = cb_value(cb.c[5]), e6 = cb_value(cb.c[6]), e7 = cb_value(cb.c[7]);
+  const float lo = (idx & 1u) ? e5 : e4;
+  const float hi = (idx & 1u) ? e7 : e6;
   const float mag = (idx & 2u) ? hi : lo;
   return neg ? -mag : mag;
 }
@@ -452,8 +471,9 @@ __device__ __forceinline__ uint32_t centroid_f16(uint32_t v, const Codebook& cb)
   const uint32_t m = v & 3u;
   const bool neg = v < 4u;
   const uint32_t idx = neg ? (3u - m) : m;
-  const uint32_t a = (idx & 1u) ? t[1] : t[0];
-  const uint32_t b = (idx & 1u) ? t[3] : t[2];
+  const uint32_t e0 = cb_value(t[0]), e1 = cb_value(t[1]), e2 = cb_value(t[2]), e3 = cb_value(t[3]);
+  const uint32_t a = (idx & 1u) ? e1 : e0;
+  const uint32_t b = (idx & 1u) ? e3 : e2;
   const uint32_t mag = (idx & 2u) ? b : a;
   return neg ? (mag ^ 0x8000u) : mag;
 }
@@ -466,6 +486,41 @@ __device__ __forceinline__ uint32_t field6(const uint32_t* w) {
     return (w[word] >> off) & 63u;
   } else {
     return __builtin_amdgcn_alignbit(w[word + 1], w[word], off) & 63u;
+  }
+}
+
+// ------------------------------------------ one token, 16-lane form ----
+// K row of a 3-bit token: dim j at bits 3j, so lanes 4k .. 4k+3 (24 bits
+// each) own dwords 3k .. 3k+2. Every lane of the quad must call this; lane
+// 4k's w holds the quad's three dwords.
+__device__ __forceinline__ void k3_row_words(const uint32_t (&c)[8], uint32_t (&w)[3]) {
+  uint32_t b24 = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b24 |= c[i] << (3 * i);
+  const uint32_t b1 = dpp_u32<kQuadXor1>(b24), b2 = dpp_u32<kQuadXor2>(b24), b3 = dpp_u32<kQuadXor3>(b24);
+  w[0] = b24 | (b1 << 24);
+  w[1] = (b1 >> 8) | (b2 << 16);
+  w[2] = (b2 >> 16) | (b3 << 8);
+}
+
+// V tile of the token's slot: dim j of tile slot r at bit 24 j + 3 r, so
+// this lane's dims 8p .. 8p+7 are the tile's dwords 6p .. 6p+5. nb = the
+// code bits, mk = the mask of the slot's bits, per dword.
+__device__ __forceinline__ void v_tile_fields(const uint32_t (&c)[8], int slot, uint32_t (&nb)[6],
+                                              uint32_t (&mk)[6]) {
+  const int r3 = 3 * (slot & (kTile - 1));
+#pragma unroll
+  for (int k = 0; k < 6; ++k) nb[k] = mk[k] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t f = c[i] << r3, fm = 7u << r3;   // 24-bit fields
+    const int pos = 24 * i, wd = pos >> 5, off = pos & 31;   // compile-time after unrolling
+    nb[wd] |= f << off;
+    mk[wd] |= fm << off;
+    if (off > 8) {
+      nb[wd + 1] |= f >> (32 - off);
+      mk[wd + 1] |= fm >> (32 - off);
+    }
   }
 }
 

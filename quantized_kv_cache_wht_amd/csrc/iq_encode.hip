@@ -371,33 +371,18 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
   if (p == 0) (is_v ? a.v_norms : a.k_norms)[row] = n;
 
   if (!is_v) {
-    // row layout: dim j at bits 3j; lanes 4k .. 4k+3 own 96 bits = 3 dwords
-    uint32_t b24 = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b24 |= c[i] << (3 * i);
-    const uint32_t b1 = dpp_u32<kQuadXor1>(b24), b2 = dpp_u32<kQuadXor2>(b24), b3 = dpp_u32<kQuadXor3>(b24);
+    uint32_t w[3];
+    k3_row_words(c, w);
     if ((p & 3) == 0) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + row * kRowBytes) + 3 * (p >> 2);
-      dst[0] = b24 | (b1 << 24);
-      dst[1] = (b1 >> 8) | (b2 << 16);
-      dst[2] = (b2 >> 16) | (b3 << 8);
+      dst[0] = w[0];
+      dst[1] = w[1];
+      dst[2] = w[2];
     }
     return;
   }
-  // tile layout: dim j of slot r at bit 24 j + 3 r, i.e. a 24-bit field per dim
-  const int r3 = 3 * (slot & (kTile - 1));
-  uint32_t nb[6] = {0u, 0u, 0u, 0u, 0u, 0u}, mk[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t f = c[i] << r3, fm = 7u << r3;   // 24-bit fields
-    const int pos = 24 * i, wd = pos >> 5, off = pos & 31;   // compile-time after unrolling
-    nb[wd] |= f << off;
-    mk[wd] |= fm << off;
-    if (off > 8) {
-      nb[wd + 1] |= f >> (32 - off);
-      mk[wd + 1] |= fm >> (32 - off);
-    }
-  }
+  uint32_t nb[6], mk[6];
+  v_tile_fields(c, slot, nb, mk);
 #pragma unroll
   for (int k = 0; k < 6; ++k) {
     const uint32_t delta = (old[k] & mk[k]) ^ nb[k];

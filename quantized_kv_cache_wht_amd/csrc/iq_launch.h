@@ -129,7 +129,8 @@ struct MergeSegment {
 // Split-K merge: rot = nullptr for records already in the model's basis (fp16
 // cache), else the rotation whose inverse is applied once. Records of
 // (seq, query head) are rec_splits apart; 1 or 2 segments (deferred decode:
-// the fp16 prefix's splits, then the packed suffix's).
+// the fp16 prefix's splits, then the packed suffix's), plus, if extra_rec >= 0,
+// the record at that index (the decode step's new token), always live.
 struct MergeArgs {
   int32_t rot_kind;      // iq_rotation
   const float* rot;
@@ -140,26 +141,22 @@ struct MergeArgs {
   int32_t group;
   int32_t rec_splits;
   int32_t n_segments;
+  int32_t extra_rec;
   MergeSegment seg[2];
 };
 
-// The decode step's new token, encoded and attended to by the merge kernel
-// (iq_append_decode_attention): token s goes to cache slot seq_start[s] +
-// seq_len[s] of segment 0 and joins that sequence's attention.
-struct MergeAppend {
+// The decode step's new token (iq_append_decode_attention): extra work-groups
+// of the split launch encode token s into cache slot seq_start[s] +
+// seq_len[s] and write its record (score, 1, rotated V) for each query head
+// of the group at split index n_splits.
+struct NewToken {
   const void* k_new;     // [n_seqs][Hkv][128], fp16 or fp32
   const void* v_new;
   int32_t new_f16;
-  int32_t k_bits;
-  int32_t num_kv_heads;
-  int32_t cache_capacity;
-  uint8_t* k_codes;
+  uint8_t* k_codes;      // the cache the splits read, writable
   uint8_t* v_codes;
   float* k_norms;
   float* v_norms;
-  const float* q;
-  float qscale;
-  Codebook cb;
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s);
@@ -167,11 +164,14 @@ hipError_t launch_rotate(const RotateArgs& a, bool inverse, hipStream_t s);
 hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f16, hipStream_t s);
 
-// split-K plan for decode (shared by the workspace query and the launch)
+// split-K plan for decode (shared by the workspace query and the launch);
+// extra_per_pair: work-groups per (seq, KV head) the launch runs beside the
+// splits. Fewer splits never need more workspace, so the plan without extras
+// sizes it.
 struct DecodePlan {
   int32_t blocks_per_split, n_splits;
 };
-DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len);
+DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t extra_per_pair = 0);
 // Workspace: one partial record (m, l, 2 pad, o[128] fp32) per (seq, query head, split).
 size_t decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, const DecodePlan& p);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
@@ -179,8 +179,9 @@ hipError_t launch_decode_f16(const F16DecodeArgs& a, hipStream_t s);
 // fp16 prefix and packed suffix in one split launch, then the merge
 hipError_t launch_decode_deferred(const F16DecodeArgs& pre, const DecodeArgs& suf, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_merge_append(const MergeArgs& a, const MergeAppend& n, hipStream_t s);
-// split kernels only (the packed decode's first launch)
+// split kernels only (the packed decode's first launch); with nt, one more
+// work-group per (KV head, seq) encodes the new token and writes its records
 hipError_t launch_decode_splits(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_splits_new(const DecodeArgs& a, const NewToken& nt, hipStream_t s);
 
 }  // namespace iq

@@ -95,7 +95,8 @@ def test_decode_validation():
     assert L.iq_decode_workspace_bytes(-1, 8, 2, 100) == 0
     # workspace grows with context and shrinks to one split for short contexts
     assert L.iq_decode_workspace_bytes(1, 32, 4, 32768) >= L.iq_decode_workspace_bytes(1, 32, 4, 1024)
-    assert L.iq_decode_workspace_bytes(1, 32, 8, 1) == 32 * 132 * 4   # one record per query head
+    # per query head: one split record, and the decode step's new token's
+    assert L.iq_decode_workspace_bytes(1, 32, 8, 1) == 2 * 32 * 132 * 4
 
 
 def test_decode_f16_validation():
