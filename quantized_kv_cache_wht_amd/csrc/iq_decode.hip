@@ -74,8 +74,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   const int hq = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
   const int h = hq / a.group;
+  // lanes 0..15 apply the inverse rotation; every lane loads its parameters
+  // (a load under a condition would hold up the record loads behind it)
   float rp[16];
-  if (kRotate && tid < 16) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid, rp);
+  if (kRotate) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid & 15, rp);
   // Record positions: segment 0 at [0, n_splits0), segment 1 (if any) from
   // split_offset on, the new token's (if any) at extra_rec. The first round
   // of record loads goes out before the sequence bounds are read (two round

@@ -38,10 +38,18 @@ constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by
 constexpr int kMergeChunk = 4;                           // records per lane per round of loads
 constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
 
+// A value no kernel writes while the reading kernel runs, read through the
+// constant address space: at a wave-uniform address this is a scalar load,
+// which neither waits behind nor holds up the wave's vector loads.
+template <typename T>
+__device__ __forceinline__ T load_invariant(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 template <typename Args>
 __device__ __forceinline__ bool seq_ok(const Args& a, int s, int* start, int* len) {
-  const int st = a.seq_start[s];
-  const int ln = a.seq_len[s];
+  const int st = load_invariant(a.seq_start + s);
+  const int ln = load_invariant(a.seq_len + s);
   *start = st;
   *len = ln;
   return st >= 0 && ln >= 0 && ln <= a.max_seq_len && static_cast<int64_t>(st) + ln <= a.capacity;

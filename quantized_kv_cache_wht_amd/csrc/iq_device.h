@@ -105,6 +105,21 @@ __device__ __forceinline__ void qmul(const float a[4], const float b[4], float r
   r[3] = a[0] * b[3] + a[1] * b[2] - a[2] * b[1] + a[3] * b[0];
 }
 
+// Column c of the left-multiplication matrix of q, i.e. q (x) e_c: a signed
+// permutation of q's components (the Hamilton product with a unit quaternion
+// involves no rounding).
+__device__ __forceinline__ void left_column(const float q[4], int c, float t[4]) {
+  if (c == 0) {
+    t[0] = q[0]; t[1] = q[1]; t[2] = q[2]; t[3] = q[3];
+  } else if (c == 1) {
+    t[0] = -q[1]; t[1] = q[0]; t[2] = q[3]; t[3] = -q[2];
+  } else if (c == 2) {
+    t[0] = -q[2]; t[1] = -q[3]; t[2] = q[0]; t[3] = q[1];
+  } else {
+    t[0] = -q[3]; t[1] = q[2]; t[2] = -q[1]; t[3] = q[0];
+  }
+}
+
 // Row-major 4x4 matrix of v -> qL (x) v (x) conj(qR), times `scale`, from the
 // 8 stored parameters of one block (quaternions renormalised here).
 __device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m[16]) {
@@ -125,10 +140,8 @@ __device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m
   for (int i = 0; i < 4; ++i) ql[i] *= nl;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    float e[4] = {0.f, 0.f, 0.f, 0.f};
-    e[c] = 1.0f;
     float t[4], col[4];
-    qmul(ql, e, t);
+    left_column(ql, c, t);
     qmul(t, qrc, col);
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[r] * scale;
@@ -166,10 +179,8 @@ __device__ __forceinline__ void iso_matrix(const float* p4, float m[16]) {
   for (int i = 0; i < 4; ++i) q[i] *= nq;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    float e[4] = {0.f, 0.f, 0.f, 0.f};
-    e[c] = 1.0f;
     float col[4];
-    qmul(q, e, col);
+    left_column(q, c, col);
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[r];
   }
@@ -326,13 +337,16 @@ __device__ __forceinline__ void so4_apply_row(float (&x)[8], const float (&m)[32
 }
 
 // The stored parameters of the lane's two blocks: 16 floats (four float4
-// loads) for the WHT + SO(4) kind, 8 (two) for the others.
+// loads) for the WHT + SO(4) kind, 8 (two) for the others, whose p16[8..15]
+// repeat p16[0..7] and go unused. All four loads are unconditional: a load
+// under a condition makes the compiler wait for it where the paths join.
 __device__ __forceinline__ void load_row_params(const float* rot_head, int kind, int p, float (&p16)[16]) {
   const int per = 2 * rot_params_per_block(kind);
   const float4* r = reinterpret_cast<const float4*>(rot_head + per * p);
+  const int hi = kind == kRotWhtSo4 ? 2 : 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float4 t = (i < 2 || kind == kRotWhtSo4) ? r[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 t = r[i < 2 ? i : hi + i - 2];
     p16[4 * i] = t.x; p16[4 * i + 1] = t.y; p16[4 * i + 2] = t.z; p16[4 * i + 3] = t.w;
   }
 }

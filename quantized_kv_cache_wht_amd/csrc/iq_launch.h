@@ -60,18 +60,10 @@ struct DequantArgs {
   Codebook cb;
 };
 
+// The 32-bit fields come first: one wide scalar load at the kernel's start
+// then covers every size a work-group's first addresses need.
 struct DecodeArgs {
   int32_t rot_kind;      // iq_rotation
-  const uint8_t* k_codes;
-  const uint8_t* v_codes;
-  const float* k_norms;
-  const float* v_norms;
-  const float* rot;
-  const float* q;
-  const int32_t* seq_start;
-  const int32_t* seq_len;
-  float* out;
-  float* ws;             // split partials [n_seqs][Hq][n_splits][132]
   int32_t n_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -84,6 +76,16 @@ struct DecodeArgs {
   int32_t rec_splits;         // ... among this many records per (seq, query head)
   int32_t k_bits;             // 3 or 4
   float qscale;               // softmax scale * log2(e)
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_norms;
+  const float* v_norms;
+  const float* rot;
+  const float* q;
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  float* out;
+  float* ws;             // split partials [n_seqs][Hq][n_splits][132]
   Codebook cb;
 };
 
