@@ -71,13 +71,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   __shared__ float rm[kMergeRows], rl[kMergeRows];
   __shared__ __align__(16) float ro[kMergeRows][kDim];
   __shared__ __align__(16) float fin[kDim];
+  __shared__ __align__(16) float mats[kBlocks * 16];   // the head's block matrices (kRotate)
   const int hq = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
   const int h = hq / a.group;
-  // lanes 0..15 apply the inverse rotation; every lane loads its parameters
-  // (a load under a condition would hold up the record loads behind it)
-  float rp[16];
-  if (kRotate) load_row_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, tid & 15, rp);
+  // threads 0..127 build the head's block matrices (one column each) for the
+  // inverse rotation; every thread loads parameters (a load under a
+  // condition would hold up the record loads behind it)
+  float bp[8];
+  if (kRotate) load_block_params(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, (tid >> 2) & (kBlocks - 1), bp);
   // Record positions: segment 0 at [0, n_splits0), segment 1 (if any) from
   // split_offset on, the new token's (if any) at extra_rec. The first round
   // of record loads goes out before the sequence bounds are read (two round
@@ -108,6 +110,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   }
   const int off1 = a.n_segments > 1 ? a.seg[1].split_offset : a.rec_splits;
   auto live_at = [&](int p) { return p < live0 || (p >= off1 && p - off1 < live1) || p == a.extra_rec; };
+  // the block matrices while the records are in flight (their parameters were requested first)
+  if (kRotate) build_head_matrices(a.rot_kind, bp, mats);
   float mx = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int p0 = row;; p0 += kMergeRows * kMergeChunk) {
@@ -150,8 +154,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
     rl[row] = l;
   }
   reinterpret_cast<float4*>(ro[row])[d4] = o;
-  float m[32];
-  if (kRotate && tid < 16) so4_matrices_row(a.rot_kind, rp, m);
   __syncthreads();
   {
     // half-wave: lane = row (0..31), dims 4 c .. 4 c + 3 with c = tid / 32
@@ -176,6 +178,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = fin[8 * tid + i];
     if (kRotate) {
+      float m[32];
+      const float4* mp = reinterpret_cast<const float4*>(mats + 32 * tid);   // blocks 2 tid, 2 tid + 1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 v = mp[i];
+        m[4 * i] = v.x; m[4 * i + 1] = v.y; m[4 * i + 2] = v.z; m[4 * i + 3] = v.w;
+      }
       so4_apply_row<true>(x, m);
       if (a.rot_kind == kRotWhtSo4) wht128_row(x, tid);
     }

@@ -46,13 +46,20 @@ __device__ __forceinline__ T load_invariant(const T* p) {
   return *(const __attribute__((address_space(4))) T*)(p);
 }
 
+// Sequence bounds that are valid for the launch: rows inside the cache and a
+// length within max_seq_len.
+template <typename Args>
+__device__ __forceinline__ bool seq_check(const Args& a, int st, int ln) {
+  return st >= 0 && ln >= 0 && ln <= a.max_seq_len && static_cast<int64_t>(st) + ln <= a.capacity;
+}
+
 template <typename Args>
 __device__ __forceinline__ bool seq_ok(const Args& a, int s, int* start, int* len) {
   const int st = load_invariant(a.seq_start + s);
   const int ln = load_invariant(a.seq_len + s);
   *start = st;
   *len = ln;
-  return st >= 0 && ln >= 0 && ln <= a.max_seq_len && static_cast<int64_t>(st) + ln <= a.capacity;
+  return seq_check(a, st, ln);
 }
 
 // 32-slot blocks covering [start, start + len) from the 32-aligned base.

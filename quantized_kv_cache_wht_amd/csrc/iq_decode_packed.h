@@ -218,6 +218,7 @@ struct PackedSmem {
   // halves in n >= 8 (G = 16: hi in qop, lo in qop_lo, column n = head n)
   uint4 qop[8][64];
   uint4 qop_lo[kSplitN ? 1 : 8][64];
+  float mats[kBlocks * 16];   // the head's 32 block matrices, row-major
   float qmax[G];
   float wm[kWaves][G], wl[kWaves][G];
 };

@@ -120,9 +120,9 @@ __device__ __forceinline__ void left_column(const float q[4], int c, float t[4])
   }
 }
 
-// Row-major 4x4 matrix of v -> qL (x) v (x) conj(qR), times `scale`, from the
-// 8 stored parameters of one block (quaternions renormalised here).
-__device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m[16]) {
+// Column c of the 4x4 matrix of v -> qL (x) v (x) conj(qR), times `scale`,
+// from the 8 stored parameters of one block (quaternions renormalised here).
+__device__ __forceinline__ void so4_column(const float* p8, int c, float scale, float col[4]) {
 #pragma clang fp contract(off)
   float ql[4], qr[4];
   float nl = 0.f, nr = 0.f;
@@ -138,14 +138,11 @@ __device__ __forceinline__ void so4_matrix(const float* p8, float scale, float m
   const float qrc[4] = {qr[0] * nr, -qr[1] * nr, -qr[2] * nr, -qr[3] * nr};
 #pragma unroll
   for (int i = 0; i < 4; ++i) ql[i] *= nl;
+  float t[4], u[4];
+  left_column(ql, c, t);
+  qmul(t, qrc, u);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float t[4], col[4];
-    left_column(ql, c, t);
-    qmul(t, qrc, col);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[r] * scale;
-  }
+  for (int r = 0; r < 4; ++r) col[r] = u[r] * scale;
 }
 
 // ------------------------------------------------- rotation kinds ----
@@ -164,8 +161,8 @@ __device__ __forceinline__ const float* rot_of_head(const float* rot, int kind, 
   return rot + static_cast<size_t>(h) * kBlocks * rot_params_per_block(kind);
 }
 
-// Row-major matrix of v -> q (x) v from 4 stored parameters (q renormalised).
-__device__ __forceinline__ void iso_matrix(const float* p4, float m[16]) {
+// Column c of the matrix of v -> q (x) v from 4 stored parameters (q renormalised).
+__device__ __forceinline__ void iso_column(const float* p4, int c, float col[4]) {
 #pragma clang fp contract(off)
   float q[4];
   float nq = 0.f;
@@ -177,46 +174,88 @@ __device__ __forceinline__ void iso_matrix(const float* p4, float m[16]) {
   nq = 1.0f / sqrtf(nq);
 #pragma unroll
   for (int i = 0; i < 4; ++i) q[i] *= nq;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float col[4];
-    left_column(q, c, col);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[r];
+  left_column(q, c, col);
+}
+
+// Column c of the matrix of two Givens rotations (c0, s0) on dims 0, 1 and
+// (c1, s1) on dims 2, 3 (each pair renormalised).
+__device__ __forceinline__ void givens_column(const float* p4, int c, float col[4]) {
+#pragma clang fp contract(off)
+  const int k = c >> 1;   // the pair this column belongs to
+  const float a = p4[2 * k], b = p4[2 * k + 1];
+  const float n = 1.0f / sqrtf(a * a + b * b);
+  const float cs = a * n, sn = b * n;
+  const float x = (c & 1) ? -sn : cs, y = (c & 1) ? cs : sn;   // rows 2k, 2k + 1
+  col[0] = k == 0 ? x : 0.f;
+  col[1] = k == 0 ? y : 0.f;
+  col[2] = k == 1 ? x : 0.f;
+  col[3] = k == 1 ? y : 0.f;
+}
+
+// Column c of the block matrix of the given kind (every kernel builds the
+// matrices through this, so all of them use the same values).
+__device__ __forceinline__ void block_column(int kind, const float* p, int c, float col[4]) {
+  if (kind == kRotIso) {
+    iso_column(p, c, col);
+  } else if (kind == kRotPlanar) {
+    givens_column(p, c, col);
+  } else {
+    so4_column(p, c, 0.08838834764831845f, col);   // 1/sqrt(128)
   }
 }
 
-// Row-major matrix of two Givens rotations (c0, s0), (c1, s1) (each pair renormalised).
-__device__ __forceinline__ void givens_matrix(const float* p4, float m[16]) {
-#pragma clang fp contract(off)
-  const float n0 = 1.0f / sqrtf(p4[0] * p4[0] + p4[1] * p4[1]);
-  const float n1 = 1.0f / sqrtf(p4[2] * p4[2] + p4[3] * p4[3]);
-  const float c0 = p4[0] * n0, s0 = p4[1] * n0, c1 = p4[2] * n1, s1 = p4[3] * n1;
-  const float r[16] = {c0, -s0, 0.f, 0.f, s0, c0, 0.f, 0.f, 0.f, 0.f, c1, -s1, 0.f, 0.f, s1, c1};
+// Row-major 4x4 matrix of one block (one branch on the kind, so the four
+// columns share their normalisation).
+__device__ __forceinline__ void block_matrix(int kind, const float* p, float m[16]) {
+  float col[4][4];
+  if (kind == kRotIso) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m[i] = r[i];
+    for (int c = 0; c < 4; ++c) iso_column(p, c, col[c]);
+  } else if (kind == kRotPlanar) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) givens_column(p, c, col[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) so4_column(p, c, 0.08838834764831845f, col[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[c][r];
 }
 
-__device__ __forceinline__ void block_matrix(int kind, const float* p, float m[16]) {
-  if (kind == kRotIso) {
-    iso_matrix(p, m);
-  } else if (kind == kRotPlanar) {
-    givens_matrix(p, m);
-  } else {
-    so4_matrix(p, 0.08838834764831845f, m);   // 1/sqrt(128)
+// The stored parameters of block b of a head: 8 floats for the WHT + SO(4)
+// kind, 4 for the others (p8[4..7] then repeat p8[0..3], unused). Both loads
+// are unconditional (a load under a condition makes the compiler wait for it
+// where the paths join).
+__device__ __forceinline__ void load_block_params(const float* rot_head, int kind, int b, float (&p8)[8]) {
+  const int per = rot_params_per_block(kind);
+  const float4* r = reinterpret_cast<const float4*>(rot_head + per * b);
+  const float4 t0 = r[0], t1 = r[per == 8 ? 1 : 0];
+  p8[0] = t0.x; p8[1] = t0.y; p8[2] = t0.z; p8[3] = t0.w;
+  p8[4] = t1.x; p8[5] = t1.y; p8[6] = t1.z; p8[7] = t1.w;
+}
+
+// The 32 block matrices of one head into LDS (row-major, 16 floats per
+// block), one column per thread: threads 0..127 work, with bp from
+// load_block_params(rot_head, kind, (threadIdx.x >> 2) & 31, bp).
+__device__ __forceinline__ void build_head_matrices(int kind, const float (&bp)[8], float* sm) {
+  const int t = threadIdx.x;
+  if (t < 4 * kBlocks) {
+    const int b = t >> 2, c = t & 3;
+    float col[4];
+    block_column(kind, bp, c, col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm[b * 16 + r * 4 + c] = col[r];
   }
 }
 
 // Fill LDS with the 32 block matrices of one head (row-major). Must be called
-// by all threads of the block; threads 0..31 work.
+// by all threads of the block (at least 128): threads 0..127 build one column each.
 __device__ __forceinline__ void load_head_matrices(const float* __restrict__ rot_head, int kind, float* sm) {
-  const int t = threadIdx.x;
-  if (t < kBlocks) {
-    float m[16];
-    block_matrix(kind, rot_head + t * rot_params_per_block(kind), m);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm[t * 16 + i] = m[i];
-  }
+  float bp[8];
+  load_block_params(rot_head, kind, (threadIdx.x >> 2) & (kBlocks - 1), bp);
+  build_head_matrices(kind, bp, sm);
 }
 
 // y_b = M_b y_b for this lane's 8 blocks (transpose = use M_b^T).
