@@ -78,6 +78,29 @@ def test_moe30b_full_layer_encode_decode_and_needle():
         assert np.max(np.abs(out[0, h * w.group] - v_p)) < 2e-3 + (1 - wts[p]) * np.max(np.abs(v_p)) * 4
 
 
+def test_moe30b_decode_step_bench_launch():
+    """bench.py's timed call: 32767 tokens encoded in bulk, then one iq_append_decode_attention that
+    appends token 32767 and attends to all 32768 (the split plan with the new token's work-groups).
+    Every code and norm of the grown cache, and every output, against the oracle."""
+    w = iqinputs.WORKLOADS["moe30b_gqa_t32768"]
+    print(f"[{w.name}] decode step", flush=True)
+    inp = iqinputs.layer_inputs(w, 1)
+    k, v, q, rot = inp["k"], inp["v"], inp["q"], inp["rot"]
+    T = w.seq_len
+    cache = iq.PackedKVCache.allocate(k.shape[1], T, _t(rot))
+    iq.iq_rotate_quantize_append(cache, _t(k[:T - 1]), _t(v[:T - 1]), first_slot=0)
+    start = np.zeros(1, np.int32)
+    cached = np.full(1, T - 1, np.int32)
+    ws = iq.decode_workspace(1, w.num_q_heads, w.num_kv_heads, T - 1)
+    out = _np(iq.iq_append_decode_attention(cache, _t(k[T - 1:]), _t(v[T - 1:]), _t(q), _t(start), _t(cached),
+                                            T - 1, workspace=ws))
+    heads = range(w.num_kv_heads)
+    rot_s, kr, kn, vt, vn = _oracle_heads(k, v, rot, heads)
+    nd = _check_codes(cache, heads, kr, kn, vt, vn, k, v, rot, T)
+    ref = R.decode_attention(q, kr, kn, vt, vn, rot_s, start, np.full(1, T, np.int32), SCALE, C32)
+    _assert_attention_close(out, ref, f"{w.name} decode step, {nd} boundary codes")
+
+
 def test_dense8b_full_layer():
     """8192 tokens, Hq 32 / Hkv 8, batch 1, Student-t outlier channels: all heads."""
     w = iqinputs.WORKLOADS["dense8b_gqa_t8192"]
