@@ -38,6 +38,25 @@ constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by
 constexpr int kMergeChunk = 4;                           // records per lane per round of loads
 constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
 
+// Max (or sum) of x over lanes i and i ^ 16, then i ^ 32, of a full wave: the
+// gfx950 row swaps hand each lane itself and its partner, in some order, in
+// the two halves of the result, so a commutative op on the halves is the
+// reduction (one instruction per step, no lane-index arithmetic). The halves
+// are copied to scalars before the bit casts: a bit cast of a vector element
+// is compiled as a read of the vector's first element.
+template <bool kMax>
+__device__ __forceinline__ float rows_reduce(float x) {
+  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const uint32_t a0 = r16[0], a1 = r16[1];
+  x = op(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const uint32_t c = __builtin_bit_cast(uint32_t, x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  const uint32_t c0 = r32[0], c1 = r32[1];
+  return op(__builtin_bit_cast(float, c0), __builtin_bit_cast(float, c1));
+}
+
 // A value no kernel writes while the reading kernel runs, read through the
 // constant address space: at a wave-uniform address this is a scalar load,
 // which neither waits behind nor holds up the wave's vector loads.

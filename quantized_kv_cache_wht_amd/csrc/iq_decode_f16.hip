@@ -135,8 +135,7 @@ __device__ __forceinline__ void f16_softmax_pv(floatx4 d0, floatx4 d1, const _Fl
   }
   // ---- online softmax, reference raised lazily (weights stay <= 2^8: fp16-safe) ----
   float u = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-  u = fmaxf(u, __shfl_xor(u, 16, 64));
-  u = fmaxf(u, __shfl_xor(u, 32, 64));
+  u = rows_reduce<true>(u);
   const bool bump = u > st.m + kLazy;
   if (__any(bump)) {
     const float m_new = bump ? u : st.m;
@@ -303,8 +302,7 @@ __device__ __forceinline__ void f16_split(const F16DecodeArgs& a, F16Smem<G>& sm
 
   // ---- per-wave totals ----
   float l_run = st.l;
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = rows_reduce<false>(l_run);
   if (q == 0 && n < G) {
     wm[wave][n] = st.m;
     wl[wave][n] = l_run;

@@ -150,8 +150,7 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
   const float tmax = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
   const int ex = __builtin_amdgcn_frexp_expf(nvmax);
   float u = tmax + (ex > 0 ? static_cast<float>(ex) : 0.f);
-  u = fmaxf(u, __shfl_xor(u, 16, 64));
-  u = fmaxf(u, __shfl_xor(u, 32, 64));
+  u = rows_reduce<true>(u);
   const bool bump = u > st.m + kLazy;   // same for every lane of one head
   if (__any(bump)) {
     const float m_new = bump ? u : st.m;
