@@ -204,8 +204,7 @@ DecodePlan decode_plan(int32_t n_seqs, int32_t num_kv_heads, int32_t max_seq_len
   if (want_splits < 1) want_splits = 1;
   int64_t bps = (blocks + want_splits - 1) / want_splits;
   if (bps < kMinBlocksPerSplit) bps = kMinBlocksPerSplit;
-  const int64_t cap = n_seqs > 1 ? kMaxBlocksPerSplitMany : kMaxBlocksPerSplitOne;
-  if (bps > cap) bps = cap;
+  if (bps > kMaxBlocksPerSplit) bps = kMaxBlocksPerSplit;
   int64_t ns = (blocks + bps - 1) / bps;
   if (ns > kMaxSplits) {
     bps = (blocks + kMaxSplits - 1) / kMaxSplits;
