@@ -203,6 +203,102 @@ def k4_decode(iq, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, n_
             "bytes_per_launch": hkv * T * (64 + 4 + 48 + 4)}
 
 
+def other_workloads(iq, stream):
+    """The other measured configurations, timed like the main one (HIP events around back-to-back
+    calls). Their caches hold random codes and norms (the decode's work does not depend on the
+    values; parity at these shapes is tested separately); the bulk encode runs on seeded N(0,1) fp16
+    K/V. Also a device-to-device copy, the streaming peak measured on this GPU."""
+    import numpy as np
+    import torch
+    import iqinputs
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260818)
+
+    def timing_cache(hkv, cap):
+        rot = torch.from_numpy(iqinputs.rotation_params(11, 0, hkv)).to(dev)
+        c = iq.PackedKVCache.allocate(hkv, cap, rot, device=dev)
+        c.k_codes.random_(0, 256, generator=gen)
+        c.v_codes.random_(0, 256, generator=gen)
+        c.k_norms.uniform_(5.0, 15.0, generator=gen)
+        c.v_norms.uniform_(5.0, 15.0, generator=gen)
+        return c
+
+    res = {}
+    # 8B dense shape: Hq 32, Hkv 8, 8191 cached tokens, 32 layers, one decode step per layer
+    w = iqinputs.WORKLOADS["dense8b_gqa_t8192"]
+    T, hkv, hq, L = w.seq_len, w.num_kv_heads, w.num_q_heads, w.n_layers
+    cs = [timing_cache(hkv, T) for _ in range(L)]
+    q = torch.randn((1, hq, 128), generator=gen, device=dev)
+    kn = torch.randn((1, hkv, 128), generator=gen, device=dev).half()
+    vn = torch.randn((1, hkv, 128), generator=gen, device=dev).half()
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    cached = torch.full((1,), T - 1, dtype=torch.int32, device=dev)
+    ws = iq.decode_workspace(1, hq, hkv, T, device=dev)
+    out = torch.empty((1, hq, 128), device=dev)
+
+    def step8b(i):
+        iq.iq_append_decode_attention(cs[i % L], kn, vn, q, st, cached, T - 1, out=out, workspace=ws, stream=stream)
+    us = time_per_call(torch, step8b, 2 * L, stream)
+    nbytes = hkv * T * 2 * ROW_BYTES
+    res[w.name] = {"step_per_layer_us": round(us, 3), "ms_per_step": round(us * L / 1e3, 4),
+                   "GBps": round(nbytes / us / 1e3, 1),
+                   "note": "the 32 layers' packed caches (218 MB) fit the 256 MB last-level cache"}
+    del cs
+
+    # batched: 32 sequences with seeded lengths in [1024, 32768], Hkv 8, one layer (over 400 MB)
+    w = iqinputs.WORKLOADS["ragged32_gqa"]
+    lens = np.asarray(iqinputs.seq_lengths(w), np.int32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    total, hkv, hq = int(lens.sum()), w.num_kv_heads, w.num_q_heads
+    cap = -(-total // 32) * 32
+    c = timing_cache(hkv, cap)
+    qb = torch.randn((len(lens), hq, 128), generator=gen, device=dev)
+    stb, lnb = torch.from_numpy(starts).to(dev), torch.from_numpy(lens).to(dev)
+    ml = int(lens.max())
+    wsb = iq.decode_workspace(len(lens), hq, hkv, ml, device=dev)
+    outb = torch.empty_like(qb)
+    us = time_per_call(torch, lambda i: iq.iq_decode_attention(c, qb, stb, lnb, ml, out=outb, workspace=wsb,
+                                                                stream=stream), 10, stream)
+    nbytes = hkv * total * 2 * ROW_BYTES
+    res[w.name] = {"decode_us": round(us, 1), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                   "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del c, wsb
+
+    # long context: bulk encode of 131072 tokens (prefill-style), then decode over three layers' caches
+    w = iqinputs.WORKLOADS["long_t131072"]
+    T, hkv, hq = w.seq_len, w.num_kv_heads, w.num_q_heads
+    k = torch.randn((T, hkv, 128), generator=gen, device=dev).half()
+    v = torch.randn((T, hkv, 128), generator=gen, device=dev).half()
+    rot = torch.from_numpy(iqinputs.rotation_params(12, 0, hkv)).to(dev)
+    cs = [iq.PackedKVCache.allocate(hkv, T, rot, device=dev) for _ in range(3)]
+    us_enc = time_per_call(torch, lambda i: iq.iq_rotate_quantize_append(cs[i % 3], k, v, first_slot=0,
+                                                                         stream=stream), 6, stream)
+    del k, v
+    ql = torch.randn((1, hq, 128), generator=gen, device=dev)
+    stl = torch.zeros(1, dtype=torch.int32, device=dev)
+    lnl = torch.full((1,), T, dtype=torch.int32, device=dev)
+    wsl = iq.decode_workspace(1, hq, hkv, T, device=dev)
+    outl = torch.empty_like(ql)
+    us_dec = time_per_call(torch, lambda i: iq.iq_decode_attention(cs[i % 3], ql, stl, lnl, T, out=outl,
+                                                                   workspace=wsl, stream=stream), 12, stream)
+    enc_bytes = T * hkv * 2 * (256 + ROW_BYTES)
+    dec_bytes = hkv * T * 2 * ROW_BYTES
+    res[w.name] = {"bulk_encode_us": round(us_enc, 1), "bulk_encode_token_layers_per_s": round(T / (us_enc * 1e-6)),
+                   "bulk_encode_GBps": round(enc_bytes / us_enc / 1e3, 1), "decode_us": round(us_dec, 2),
+                   "decode_GBps": round(dec_bytes / us_dec / 1e3, 1)}
+    del cs
+
+    # streaming peak on this GPU: device-to-device copy of 1 GiB (read + write bytes)
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    us = time_per_call(torch, lambda i: b.copy_(a), 5, stream)
+    res["copy_1GiB"] = {"us": round(us, 1), "GBps": round(2 * (1 << 30) / us / 1e3, 1)}
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the oracle's decode (float64, numpy) on (layer 0, KV head h) samples."""
     import numpy as np
@@ -360,6 +456,7 @@ def main():
     traffic = measured_traffic(w.name)
     comp = None if args.no_compare else comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv,
                                                      T, hkv, float(dec_us.mean()), new_k, new_v)
+    others = None if args.no_compare else other_workloads(iq, stream)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -397,6 +494,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
         "comparisons": comp,
+        "other_workloads": others,
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
