@@ -88,14 +88,14 @@ __device__ __forceinline__ void new_token_block(const DecodeArgs& a, const NewTo
       for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(a.cb.t4[8 + k], n);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        c[i] = code16_of(x[i], tp);
+        c[i] = norm_nonfinite(n) ? code_nonfinite(x[i], n, 7u) : code16_of(x[i], tp);
         kw[0] |= c[i] << (4 * i);
         sm.kc[8 * p + i] = centroid16(c[i], a.cb);
       }
     } else {
       const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = code_of(x[i], t4, t5, t6);
+      for (int i = 0; i < 8; ++i) c[i] = norm_nonfinite(n) ? code_nonfinite(x[i], n, 3u) : code_of(x[i], t4, t5, t6);
       if (wave == 0) {
         k3_row_words(c, kw);
 #pragma unroll

@@ -407,32 +407,40 @@ __device__ __forceinline__ float quad_norm(const float (&y)[kPerLane]) {
 
 // code = #{k : y > thr_k}. The thresholds are symmetric (thr_{6-k} = -thr_k,
 // thr_3 = 0), so with a = |y|: y > 0 gives 4 + #{k>=4 : a > thr_k}, and
-// y <= 0 gives 3 - #{k>=4 : a >= thr_k}.
+// y <= 0 gives 3 - #{k>=4 : a >= thr_k}. For a finite norm the thresholds are
+// >= 0 and non-negative floats order as their bit patterns, so a >= t is
+// bits(a) + 1 > bits(t): one integer comparison per threshold serves both
+// signs. Valid for a finite norm (then y is finite too); code_nonfinite
+// covers the rest.
 __device__ __forceinline__ uint32_t code_of(float y, float t4, float t5, float t6) {
-  const float a = fabsf(y);
-  if (y > 0.0f) {
-    return 4u + (a > t4) + (a > t5) + (a > t6);
-  }
-  // y <= 0 or NaN. For NaN every comparison is false, giving code 3 - 0 = 3;
-  // the definition gives 0, so NaN is handled explicitly.
-  if (y != y) return 0u;
-  return 3u - ((a >= t4) + (a >= t5) + (a >= t6));
+  const bool pos = y > 0.0f;
+  const uint32_t u = (__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u);
+  const uint32_t m = (u > __float_as_uint(t4)) + (u > __float_as_uint(t5)) + (u > __float_as_uint(t6));
+  return pos ? 4u + m : 3u - m;
 }
 
 // 16-level code = #{k : y > thr_k} with the symmetric thresholds of the 4-bit
 // codebook (thr_{14-k} = -thr_k, thr_7 = 0); t8..t14 are fl32(t4[8..14] n).
+// Same reading as code_of, for a finite norm.
 __device__ __forceinline__ uint32_t code16_of(float y, const float (&tp)[7]) {
-  const float a = fabsf(y);
-  uint32_t above = 0, at_or_above = 0;
+  const bool pos = y > 0.0f;
+  const uint32_t u = (__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u);
+  uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < 7; ++k) {
-    above += a > tp[k];
-    at_or_above += a >= tp[k];
-  }
-  if (y > 0.0f) return 8u + above;
-  if (y != y) return 0u;   // NaN: the definition gives code 0
-  return 7u - at_or_above;
+  for (int k = 0; k < 7; ++k) m += u > __float_as_uint(tp[k]);
+  return pos ? 8u + m : 7u - m;
 }
+
+// The code of y when the vector's norm n is not finite. Then the middle
+// threshold fl(0 * n) is NaN and the others are NaN (n NaN) or -inf below it
+// and +inf above it (n = +inf), so the definition counts the `below`
+// thresholds (3 or 7) when n = +inf and y > -inf, and gives 0 otherwise.
+__device__ __forceinline__ uint32_t code_nonfinite(float y, float n, uint32_t below) {
+  return (n == __builtin_huge_valf() && y > -__builtin_huge_valf()) ? below : 0u;
+}
+
+// True when a norm is NaN or infinite (the codes then come from code_nonfinite).
+__device__ __forceinline__ bool norm_nonfinite(float n) { return !(n <= 3.402823466e38f); }
 
 // A wave-uniform codebook entry as a register value. Without it the compiler
 // may turn a select between two entries of a by-value kernel argument into a

@@ -83,6 +83,10 @@ __device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], 
   uint32_t c[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) c[i] = code_of(y[i], t4, t5, t6);
+  if (norm_nonfinite(n)) {
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) c[i] = code_nonfinite(y[i], n, 3u);
+  }
   pack32(c, w);
   return n;
 }
@@ -95,11 +99,12 @@ __device__ __forceinline__ float quantize_pack_lane16(const float (&y)[kPerLane]
   float tp[7];
 #pragma unroll
   for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(cb.t4[8 + k], n);
+  const bool nf = norm_nonfinite(n);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     uint32_t v = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v |= code16_of(y[8 * d + i], tp) << (4 * i);
+    for (int i = 0; i < 8; ++i) v |= (nf ? code_nonfinite(y[8 * d + i], n, 7u) : code16_of(y[8 * d + i], tp)) << (4 * i);
     w[d] = v;
   }
   return n;
@@ -355,9 +360,10 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
     float tp[7];
 #pragma unroll
     for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(a.cb.t4[8 + k], n);
+    const bool nf = norm_nonfinite(n);
     uint32_t w = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= code16_of(x[i], tp) << (4 * i);
+    for (int i = 0; i < 8; ++i) w |= (nf ? code_nonfinite(x[i], n, 7u) : code16_of(x[i], tp)) << (4 * i);
     if (!in_cap) return;
     if (p == 0) a.k_norms[row] = n;
     reinterpret_cast<uint32_t*>(a.k_codes + row * k_row_bytes(4))[p] = w;
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
   const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
   uint32_t c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = code_of(x[i], t4, t5, t6);
+  for (int i = 0; i < 8; ++i) c[i] = norm_nonfinite(n) ? code_nonfinite(x[i], n, 3u) : code_of(x[i], t4, t5, t6);
   if (!in_cap) return;
   if (p == 0) (is_v ? a.v_norms : a.k_norms)[row] = n;
 

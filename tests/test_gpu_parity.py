@@ -43,11 +43,19 @@ def test_quantize_pack_bit_exact_on_same_rotated_input():
     x = iqinputs.kv(5, 0, "k", 6000, 1, "fixed_x8", "f32")[:, 0].astype(np.float64)
     x *= g.uniform(1e-3, 1e3, (6000, 1))
     y = R.rotate(x, rot).astype(np.float32)
-    extra = np.zeros((5, 128), np.float32)
+    extra = np.zeros((9, 128), np.float32)
     extra[1, 7] = 2.5                                     # single nonzero: zeros land on the tie at 0
     extra[2] = np.nan
     extra[3] = np.float32(1e-20) * np.ones(128, np.float32)
     extra[4, :] = -1.0
+    # non-finite norms: one NaN dim; a norm past the fp32 range; single +inf and -inf dims
+    extra[5, :] = 1.0
+    extra[5, 9] = np.nan
+    extra[6, :] = 1e38
+    extra[7, :] = -0.5
+    extra[7, 3] = np.inf
+    extra[8, :] = 0.25
+    extra[8, 100] = -np.inf
     # exact ties at the positive and negative boundaries (norm fixed to 1)
     ties = []
     for k in range(7):
@@ -339,6 +347,30 @@ def _encode_ref_thr(x, rot, thr):
         c, n = R.quantize(y32, thr)
         out_c.append(c), out_n.append(n), out_y.append(y32)
     return np.stack(out_c), np.stack(out_n), np.stack(out_y)
+
+
+@pytest.mark.parametrize("k_bits", [3, 4])
+@pytest.mark.parametrize("n_tok", [70, 5])     # bulk kernel, short-append kernel
+def test_append_nonfinite_inputs_give_code_zero(k_bits, n_tok):
+    """A NaN anywhere in a new K or V vector makes its norm NaN, so every one of its codes is 0 (the
+    definition compares with NaN thresholds); its neighbours are encoded as usual."""
+    hkv = 2
+    rot = iqinputs.rotation_params(41, 0, hkv)
+    x = iqinputs.kv(41, 0, "k", n_tok, hkv, "fixed_x8", "f32")
+    x[1, 0, 17] = np.nan
+    x[3, 1, :] = np.nan
+    cache = iq.PackedKVCache.allocate(hkv, 96, _t(rot), k_bits=k_bits)
+    iq.iq_rotate_quantize_append(cache, _t(x), _t(x), first_slot=8)
+    thr = T16 if k_bits == 4 else T32
+    codes_ref, n_ref, y_ref = _encode_ref_thr(x, rot, thr)
+    got = R.unpack(_np(cache.k_codes))[:, 8:8 + n_tok]
+    gv = R.unpack_tiles(_np(cache.v_codes))[:, 8:8 + n_tok]
+    for g in (got, gv):
+        assert not g[0, 1].any() and not g[1, 3].any()
+    assert np.isnan(_np(cache.k_norms)[0, 9]) and np.isnan(_np(cache.v_norms)[1, 11])
+    finite = np.isfinite(n_ref)
+    _boundary_mismatch_ok(np.where(finite[..., None], got, 0), np.where(finite[..., None], codes_ref, 0),
+                          np.nan_to_num(y_ref), np.where(finite, n_ref, 1.0), thr)
 
 
 @pytest.mark.parametrize("kind", ["wht_so4", "iso"])

@@ -381,6 +381,27 @@ def check_quantize(codebook):
     assert np.isnan(nn[0]) and not cn.any()
 
 
+def test_quantize_nonfinite_norms_follow_the_definition(codebook):
+    """code = #{k : y > fl32(t_k n)}: a NaN norm makes every threshold NaN (all codes 0); an infinite
+    norm makes the middle threshold 0 * inf = NaN and the others -inf (below) or +inf (above), so a
+    code counts the thresholds below the middle (3 of 7; 7 of 15 with 16 levels) when y > -inf."""
+    _, t32, _ = codebook
+    _, t16, _ = R.codebook(levels=16)
+    one_nan = np.ones((1, 128), np.float32)
+    one_nan[0, 9] = np.nan
+    c, n = R.quantize(one_nan, t32)
+    assert np.isnan(n[0]) and not c.any()
+    big = np.full((1, 128), 1e38, np.float32)                 # fp64 norm 1.1e39: +inf in fp32
+    c, n = R.quantize(big, t32)
+    assert n[0] == np.inf and np.all(c == 3)
+    c, _ = R.quantize(big, t16)
+    assert np.all(c == 7)
+    mixed = np.ones((1, 128), np.float32)
+    mixed[0, 0], mixed[0, 1] = np.inf, -np.inf
+    c, n = R.quantize(mixed, t32)
+    assert n[0] == np.inf and c[0, 0] == 3 and c[0, 1] == 0 and np.all(c[0, 2:] == 3)
+
+
 def test_quantize_is_nearest_centroid(codebook):
     check_quantize(codebook)
 
