@@ -94,8 +94,11 @@ __device__ __forceinline__ void new_token_block(const DecodeArgs& a, const NewTo
       }
     } else {
       const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
+      codes_of8(x, t4, t5, t6, c);
+      if (norm_nonfinite(n)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = norm_nonfinite(n) ? code_nonfinite(x[i], n, 3u) : code_of(x[i], t4, t5, t6);
+        for (int i = 0; i < 8; ++i) c[i] = code_nonfinite(x[i], n, 3u);
+      }
       if (wave == 0) {
         k3_row_words(c, kw);
 #pragma unroll

@@ -371,8 +371,11 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
   }
   const float t4 = __fmul_rn(a.cb.t[4], n), t5 = __fmul_rn(a.cb.t[5], n), t6 = __fmul_rn(a.cb.t[6], n);
   uint32_t c[8];
+  codes_of8(x, t4, t5, t6, c);
+  if (norm_nonfinite(n)) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = norm_nonfinite(n) ? code_nonfinite(x[i], n, 3u) : code_of(x[i], t4, t5, t6);
+    for (int i = 0; i < 8; ++i) c[i] = code_nonfinite(x[i], n, 3u);
+  }
   if (!in_cap) return;
   if (p == 0) (is_v ? a.v_norms : a.k_norms)[row] = n;
 
