@@ -23,8 +23,8 @@
 //     weights times V norms (hi rows g, lo rows g + 8), B = code centroids.
 // Code pairs become operand dwords through a 64-entry table in LDS (entry p =
 // {hi(c_a) | lo(c_a) << 16, hi(c_b) | lo(c_b) << 16} for the codes a, b of
-// pair p), replicated 16 times so the lanes of a 16-lane group hit distinct
-// banks; one 8-byte read fills two operand registers.
+// pair p), replicated 32 times so the lanes of a half-wave hit distinct banks;
+// one 8-byte read fills two operand registers.
 //
 // Layout of the cache (see include/iq.h): K rows of 48 bytes per token; V in
 // tiles of 8 slots, dim-major, so the codes one PV operand needs (one dim,

@@ -7,7 +7,12 @@
 namespace iq {
 
 constexpr int kLutEntries = 64;      // all pairs of 3-bit codes
-constexpr int kLutCopies = 16;       // one per lane of a 16-lane group
+// Copies of the 3-bit table, one per lane of a half-wave: an LDS read of 8
+// bytes serves 32 lanes per cycle, so with 16 copies lanes i and i + 16 would
+// meet in one bank whenever their entries' parity agrees (measured as ~2
+// conflict cycles per LDS instruction in the decode loop).
+constexpr int kLutCopies = 32;
+constexpr int kKLutCopies = 16;      // the 4-bit K table's (256 entries): one per lane of a row
 
 // Table entry of the code pair at bit BIT of w: {hi|lo of code a, hi|lo of code b}.
 template <int BIT, int N>
@@ -15,10 +20,10 @@ __device__ __forceinline__ uint2 pair_entry(const uint32_t (&w)[N], const char* 
   constexpr int word = BIT >> 5, off = BIT & 31;
   const uint32_t src = (off <= 26) ? w[word] : __builtin_amdgcn_alignbit(w[word + 1], w[word], off);
   constexpr int field = (off <= 26) ? off : 0;
-  // byte address = field * 128 + lane_off, as one bit-field extract and one
+  // byte address = field * 256 + lane_off, as one bit-field extract and one
   // shift-add (the compiler's own lowering of this takes three instructions)
   uint32_t addr;
-  asm("v_bfe_u32 %0, %1, %2, 6\n\tv_lshl_add_u32 %0, %0, 7, %3" : "=&v"(addr) : "v"(src), "i"(field), "v"(lane_off));
+  asm("v_bfe_u32 %0, %1, %2, 6\n\tv_lshl_add_u32 %0, %0, 8, %3" : "=&v"(addr) : "v"(src), "i"(field), "v"(lane_off));
   return *reinterpret_cast<const uint2*>(lut + addr);
 }
 
@@ -88,7 +93,8 @@ struct Consts {
   const uint4* qop_lo;   // G = 16: the lo halves, same layout
   float fscale;
   bool lo_lane;
-  uint32_t lane_off;
+  uint32_t lane_off;    // this lane's copy of the 3-bit table: (lane & 31) * 8
+  uint32_t klane_off;   // and of the 4-bit K table: (lane & 15) * 8
   int rel_lo, rel_hi;
   const char* lut;    // 3-bit code pairs (V, and K when 3-bit)
   const char* klut;   // 4-bit K code pairs
@@ -102,9 +108,9 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
   floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #define IQ_SCORE(KAPPA)                                                        \
   {                                                                            \
-    const half8 ka = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw0, c.klut, c.lane_off) \
+    const half8 ka = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw0, c.klut, c.klane_off) \
                              : code_operand<12 * KAPPA>(cur.kw0, c.lut, c.lane_off);  \
-    const half8 kb = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw1, c.klut, c.lane_off) \
+    const half8 kb = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw1, c.klut, c.klane_off) \
                              : code_operand<12 * KAPPA>(cur.kw1, c.lut, c.lane_off);  \
     H8 qv;                                                                     \
     qv.u4 = c.qop[64 * KAPPA];                                                 \
@@ -210,7 +216,7 @@ struct PackedSmem {
   // the wave accumulators after the loop; during it (4-bit K) the K code-pair table
   union {
     float wo[kWaves][kRows][kDim];
-    uint2 klut[KB == 4 ? 256 * kLutCopies : 2];
+    uint2 klut[KB == 4 ? 256 * kKLutCopies : 2];
   } big;
   // query operand of k-step kk for lane 16 q + n: dims 32 q + 4 kk + e (e = 0..3) of
   // head n & 7, each value twice (one fp16 pair); hi halves in columns n < 8, lo
