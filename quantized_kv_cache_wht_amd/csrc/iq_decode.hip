@@ -23,8 +23,9 @@
 //     weights times V norms (hi rows g, lo rows g + 8), B = code centroids.
 // Code pairs become operand dwords through a 64-entry table in LDS (entry p =
 // {hi(c_a) | lo(c_a) << 16, hi(c_b) | lo(c_b) << 16} for the codes a, b of
-// pair p), replicated 32 times so the lanes of a half-wave hit distinct banks;
-// one 8-byte read fills two operand registers.
+// pair p), replicated 16 times (one copy per lane of a 16-lane group); one
+// 8-byte read fills two operand registers. Each wave streams its blocks
+// through two LDS stages of its own with global->LDS loads (iq_decode_packed.h).
 //
 // Layout of the cache (see include/iq.h): K rows of 48 bytes per token; V in
 // tiles of 8 slots, dim-major, so the codes one PV operand needs (one dim,
@@ -47,6 +48,7 @@ namespace iq {
 template <int G, int KB, bool kNew>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs a, NewToken nt) {
   __shared__ PackedSmem<G, KB> sm;
+  __shared__ StageMem<G, KB> stg;
   static_assert(sizeof(PackedSmem<G, KB>) >= sizeof(NewTokenSmem<G>), "new-token LDS must fit");
   if constexpr (kNew) {
     if (blockIdx.z == 0) {

@@ -87,6 +87,17 @@ __device__ __forceinline__ int n_blocks(int start, int len) {
   return len > 0 ? ((start - (start & ~(kBlk - 1)) + len + kBlk - 1) / kBlk) : 0;
 }
 
+// Work-group barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads. (__syncthreads' fence also waits for
+// every global->LDS load in flight, which would drain the block prefetch.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS byte address of a __shared__ object (for inline asm operands).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_address(const T* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)(p)));
+}
+
 __device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

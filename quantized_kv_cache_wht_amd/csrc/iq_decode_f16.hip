@@ -388,13 +388,16 @@ template <int G, int KB>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_deferred_split_kernel(F16DecodeArgs pre, DecodeArgs suf) {
   __shared__ union {
     F16Smem<G> f;
-    PackedSmem<G, KB> p;
+    struct {
+      PackedSmem<G, KB> p;
+      StageMem<G, KB> stg;
+    } k;
   } sm;
   const int z = blockIdx.z;
   if (z < pre.n_splits) {
     f16_split<G>(pre, sm.f, z);
   } else {
-    packed_split<G, KB>(suf, sm.p, z - pre.n_splits);
+    packed_split<G, KB>(suf, sm.k.p, sm.k.stg, z - pre.n_splits);
   }
 }
 

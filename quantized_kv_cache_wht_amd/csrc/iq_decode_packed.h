@@ -7,12 +7,15 @@
 namespace iq {
 
 constexpr int kLutEntries = 64;      // all pairs of 3-bit codes
-// Copies of the 3-bit table, one per lane of a half-wave: an LDS read of 8
-// bytes serves 32 lanes per cycle, so with 16 copies lanes i and i + 16 would
-// meet in one bank whenever their entries' parity agrees (measured as ~2
-// conflict cycles per LDS instruction in the decode loop).
-constexpr int kLutCopies = 32;
-constexpr int kKLutCopies = 16;      // the 4-bit K table's (256 entries): one per lane of a row
+// Copies of the 3-bit table, one per lane of a 16-lane group. (An LDS read of
+// 8 bytes serves 32 lanes per cycle, so lanes i and i + 16 meet in one bank
+// when their entries' parity agrees; 32 copies remove those conflicts but
+// measured no faster, and their extra 8 KB would cost a third work-group per
+// CU.)
+constexpr int kLutCopies = 16;
+// the 4-bit K table's (256 entries): one per lane of half a row, so that with
+// the staged blocks two work-groups still fit in a CU's LDS
+constexpr int kKLutCopies = 8;
 
 // Table entry of the code pair at bit BIT of w: {hi|lo of code a, hi|lo of code b}.
 template <int BIT, int N>
@@ -20,20 +23,28 @@ __device__ __forceinline__ uint2 pair_entry(const uint32_t (&w)[N], const char* 
   constexpr int word = BIT >> 5, off = BIT & 31;
   const uint32_t src = (off <= 26) ? w[word] : __builtin_amdgcn_alignbit(w[word + 1], w[word], off);
   constexpr int field = (off <= 26) ? off : 0;
-  // byte address = field * 256 + lane_off, as one bit-field extract and one
-  // shift-add (the compiler's own lowering of this takes three instructions)
+  // byte address = field * 8 kLutCopies + lane_off, as one bit-field extract
+  // and one shift-add (the compiler's own lowering of this takes three)
+  constexpr int shift = kLutCopies == 16 ? 7 : 8;
+  static_assert(kLutCopies == 16 || kLutCopies == 32, "entry stride is a shift");
   uint32_t addr;
-  asm("v_bfe_u32 %0, %1, %2, 6\n\tv_lshl_add_u32 %0, %0, 8, %3" : "=&v"(addr) : "v"(src), "i"(field), "v"(lane_off));
+  asm("v_bfe_u32 %0, %1, %2, 6\n\tv_lshl_add_u32 %0, %0, %4, %3"
+      : "=&v"(addr)
+      : "v"(src), "i"(field), "v"(lane_off), "i"(shift));
   return *reinterpret_cast<const uint2*>(lut + addr);
 }
 
 // 4-bit K: table entry of the code pair in byte BIT / 8 of w (256 entries of
-// 16 copies, 128 bytes apart); the byte never straddles a dword.
+// kKLutCopies copies, 8 kKLutCopies bytes apart); the byte never straddles a dword.
 template <int BIT, int N>
 __device__ __forceinline__ uint2 pair_entry4(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
   constexpr int word = BIT >> 5, field = BIT & 31;
+  constexpr int shift = kKLutCopies == 8 ? 6 : 7;
+  static_assert(kKLutCopies == 8 || kKLutCopies == 16, "entry stride is a shift");
   uint32_t addr;
-  asm("v_bfe_u32 %0, %1, %2, 8\n\tv_lshl_add_u32 %0, %0, 7, %3" : "=&v"(addr) : "v"(w[word]), "i"(field), "v"(lane_off));
+  asm("v_bfe_u32 %0, %1, %2, 8\n\tv_lshl_add_u32 %0, %0, %4, %3"
+      : "=&v"(addr)
+      : "v"(w[word]), "i"(field), "v"(lane_off), "i"(shift));
   return *reinterpret_cast<const uint2*>(lut + addr);
 }
 
@@ -61,30 +72,135 @@ struct BlockData {
   float4 nk0, nk1, nv0, nv1;
 };
 
-// K tile T row r <-> token 8 (r/4) + 4T + r%4 of the block; this lane loads
-// row n of both tiles (dims 32q .. 32q+31), V tile q (dims 8n .. 8n+7) and
-// the norms of tokens 8q .. 8q+7 (its rows in the score output).
+// One wave's copy of a 32-slot block in LDS: the K rows, the V tiles, then
+// the K and V norms, each as contiguous in the cache (a block starts at a
+// multiple of 32 slots, so every part is 16-byte aligned there and here).
 template <int KB>
-__device__ __forceinline__ void load_block(const DecodeArgs& a, size_t slot_base, int slot0, int n, int q,
-                                           BlockData<KB>& d) {
-  constexpr int kRow = k_row_bytes(KB);   // 48 or 64
-  const int tok_a0 = 8 * (n >> 2) + (n & 3);
-  const uint32_t* k0 = reinterpret_cast<const uint32_t*>(a.k_codes + (slot_base + slot0 + tok_a0) * kRow + 4 * KB * q);
-  const uint32_t* k1 = k0 + kRow;   // token + 4: 4 rows = kRow dwords
-  if constexpr (KB == 4) {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(k0), x1 = *reinterpret_cast<const uint4*>(k1);
-    d.kw0[0] = x0.x; d.kw0[1] = x0.y; d.kw0[2] = x0.z; d.kw0[3] = x0.w;
-    d.kw1[0] = x1.x; d.kw1[1] = x1.y; d.kw1[2] = x1.z; d.kw1[3] = x1.w;
+struct Stage {
+  static constexpr int kK = 0;
+  static constexpr int kV = kBlk * k_row_bytes(KB);                // 1536 or 2048
+  static constexpr int kNK = kV + kBlk / kTile * kTileBytes;       // + 1536
+  static constexpr int kNV = kNK + kBlk * 4;
+  static constexpr int kBytes = kNV + kBlk * 4;
+  static constexpr int kLoads = 6;   // global->LDS load instructions per block
+};
+
+// LDS of a split work-group that its waves fill and read on their own: two
+// stages per wave during the loop, the wave's accumulators after it (a wave
+// writes only its own area, so no barrier separates the two uses).
+template <int G, int KB>
+struct StageMem {
+  static constexpr int kRows = (G <= 8) ? 2 * G : G;   // accumulator rows (hi and lo halves when G <= 8)
+  static constexpr int kStageBytes = Stage<KB>::kBytes;
+  static constexpr int kAreaBytes = 2 * kStageBytes > kRows * kDim * 4 ? 2 * kStageBytes : kRows * kDim * 4;
+  union Area {
+    uint4 stage[2][kStageBytes / 16];
+    float wo[kRows][kDim];
+    uint4 raw[kAreaBytes / 16];
+  };
+  Area w[kWaves];
+};
+
+// One global->LDS load: 16 bytes per lane from base + voff (base wave-uniform)
+// to LDS address lds + 16 * lane. Written as inline asm: the compiler's own
+// form of it is not kept inside divergent branches (it merged the two halves
+// of a conditional pair of these into one load with the wrong LDS base).
+__device__ __forceinline__ void load_lds16(uintptr_t base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// Copies block `slot` (absolute slot of the head's cache row, a multiple of
+// 32; wave-uniform) into the stage at LDS address `lds` (wave-uniform): K and
+// V take two loads each, the K and V norms one each (lanes 0-7, 8-15);
+// voff = 16 * lane. Every load counts once on vmcnt.
+template <int KB>
+__device__ __forceinline__ void issue_block_loads(const DecodeArgs& a, size_t slot, uint32_t lds, uint32_t voff,
+                                                  int lane) {
+  using S = Stage<KB>;
+  const uintptr_t kp = reinterpret_cast<uintptr_t>(a.k_codes) + slot * k_row_bytes(KB);
+  const uintptr_t vp = reinterpret_cast<uintptr_t>(a.v_codes) + slot / kTile * kTileBytes;
+  load_lds16(kp, voff, lds + S::kK);
+  if (KB == 4 || lane < 32) load_lds16(kp + 1024, voff, lds + S::kK + 1024);
+  load_lds16(vp, voff, lds + S::kV);
+  if (lane < 32) load_lds16(vp + 1024, voff, lds + S::kV + 1024);
+  if (lane < 8) load_lds16(reinterpret_cast<uintptr_t>(a.k_norms + slot), voff, lds + S::kNK);
+  else if (lane < 16) load_lds16(reinterpret_cast<uintptr_t>(a.v_norms + slot) - 128, voff, lds + S::kNK);
+}
+
+// This lane's part of a staged block (K tile rows n of both tiles, dims
+// 32q..; V tile q, dims 8n..; the norms of tokens 8q..8q+7), read once the
+// block's loads have landed: kPending is how many global->LDS loads issued
+// after them may still be in flight (vmcnt counts in issue order). The reads
+// are inline asm with their own waits, so the compiler neither delays them
+// behind the younger loads nor reuses their registers early. kOff = the
+// stage's byte offset from stage 0; ka, va, na = this lane's K, V and norm
+// addresses in stage 0.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int KB, int kOff, int kPending>
+__device__ __forceinline__ void read_stage(uint32_t ka, uint32_t va, uint32_t na, BlockData<KB>& d) {
+  f32x4 nk0, nk1, nv0, nv1;   // (float outputs: a bit cast of a vector element reads element 0)
+  u32x2 v0, v1, v2;
+  if constexpr (KB == 3) {
+    // K: 12 bytes at a 4-byte-aligned offset per tile row -> three dword reads
+    uint32_t k[6];
+    asm volatile(
+        "s_waitcnt vmcnt(%[n])\n\t"
+        "ds_read_b32 %[k0], %[ka] offset:%[o0]\n\t"
+        "ds_read_b32 %[k1], %[ka] offset:%[o1]\n\t"
+        "ds_read_b32 %[k2], %[ka] offset:%[o2]\n\t"
+        "ds_read_b32 %[k3], %[ka] offset:%[o3]\n\t"
+        "ds_read_b32 %[k4], %[ka] offset:%[o4]\n\t"
+        "ds_read_b32 %[k5], %[ka] offset:%[o5]\n\t"
+        "ds_read_b64 %[v0], %[va] offset:%[v0o]\n\t"
+        "ds_read_b64 %[v1], %[va] offset:%[v1o]\n\t"
+        "ds_read_b64 %[v2], %[va] offset:%[v2o]\n\t"
+        "ds_read_b128 %[nk0], %[na] offset:%[n0]\n\t"
+        "ds_read_b128 %[nk1], %[na] offset:%[n1]\n\t"
+        "ds_read_b128 %[nv0], %[na] offset:%[n2]\n\t"
+        "ds_read_b128 %[nv1], %[na] offset:%[n3]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [k2] "=&v"(k[2]), [k3] "=&v"(k[3]), [k4] "=&v"(k[4]),
+          [k5] "=&v"(k[5]), [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [nk0] "=&v"(nk0), [nk1] "=&v"(nk1),
+          [nv0] "=&v"(nv0), [nv1] "=&v"(nv1)
+        : [ka] "v"(ka), [va] "v"(va), [na] "v"(na), [n] "n"(kPending), [o0] "n"(kOff), [o1] "n"(kOff + 4),
+          [o2] "n"(kOff + 8), [o3] "n"(kOff + 4 * 48), [o4] "n"(kOff + 4 * 48 + 4), [o5] "n"(kOff + 4 * 48 + 8),
+          [v0o] "n"(kOff), [v1o] "n"(kOff + 8), [v2o] "n"(kOff + 16), [n0] "n"(kOff),
+          [n1] "n"(kOff + 16), [n2] "n"(kOff + 128), [n3] "n"(kOff + 144)
+        : "memory");
+    d.kw0[0] = k[0]; d.kw0[1] = k[1]; d.kw0[2] = k[2];
+    d.kw1[0] = k[3]; d.kw1[1] = k[4]; d.kw1[2] = k[5];
   } else {
-    d.kw0[0] = k0[0]; d.kw0[1] = k0[1]; d.kw0[2] = k0[2];
-    d.kw1[0] = k1[0]; d.kw1[1] = k1[1]; d.kw1[2] = k1[2];
+    u32x4 k0, k1;
+    asm volatile(
+        "s_waitcnt vmcnt(%[n])\n\t"
+        "ds_read_b128 %[k0], %[ka] offset:%[o0]\n\t"
+        "ds_read_b128 %[k1], %[ka] offset:%[o1]\n\t"
+        "ds_read_b64 %[v0], %[va] offset:%[v0o]\n\t"
+        "ds_read_b64 %[v1], %[va] offset:%[v1o]\n\t"
+        "ds_read_b64 %[v2], %[va] offset:%[v2o]\n\t"
+        "ds_read_b128 %[nk0], %[na] offset:%[n0]\n\t"
+        "ds_read_b128 %[nk1], %[na] offset:%[n1]\n\t"
+        "ds_read_b128 %[nv0], %[na] offset:%[n2]\n\t"
+        "ds_read_b128 %[nv1], %[na] offset:%[n3]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [k0] "=&v"(k0), [k1] "=&v"(k1), [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [nk0] "=&v"(nk0), [nk1] "=&v"(nk1),
+          [nv0] "=&v"(nv0), [nv1] "=&v"(nv1)
+        : [ka] "v"(ka), [va] "v"(va), [na] "v"(na), [n] "n"(kPending), [o0] "n"(kOff), [o1] "n"(kOff + 4 * 64),
+          [v0o] "n"(kOff), [v1o] "n"(kOff + 8), [v2o] "n"(kOff + 16), [n0] "n"(kOff),
+          [n1] "n"(kOff + 16), [n2] "n"(kOff + 128), [n3] "n"(kOff + 144)
+        : "memory");
+    d.kw0[0] = k0[0]; d.kw0[1] = k0[1]; d.kw0[2] = k0[2]; d.kw0[3] = k0[3];
+    d.kw1[0] = k1[0]; d.kw1[1] = k1[1]; d.kw1[2] = k1[2]; d.kw1[3] = k1[3];
   }
-  const uint2* vp = reinterpret_cast<const uint2*>(a.v_codes + ((slot_base + slot0) / kTile + q) * kTileBytes + 24 * n);
-  const uint2 v0 = vp[0], v1 = vp[1], v2 = vp[2];
-  d.vw[0] = v0.x; d.vw[1] = v0.y; d.vw[2] = v1.x; d.vw[3] = v1.y; d.vw[4] = v2.x; d.vw[5] = v2.y;
-  const float4* nkp = reinterpret_cast<const float4*>(a.k_norms + slot_base + slot0 + 8 * q);
-  const float4* nvp = reinterpret_cast<const float4*>(a.v_norms + slot_base + slot0 + 8 * q);
-  d.nk0 = nkp[0]; d.nk1 = nkp[1]; d.nv0 = nvp[0]; d.nv1 = nvp[1];
+  d.vw[0] = v0[0]; d.vw[1] = v0[1]; d.vw[2] = v1[0]; d.vw[3] = v1[1]; d.vw[4] = v2[0]; d.vw[5] = v2[1];
+  d.nk0 = make_float4(nk0[0], nk0[1], nk0[2], nk0[3]);
+  d.nk1 = make_float4(nk1[0], nk1[1], nk1[2], nk1[3]);
+  d.nv0 = make_float4(nv0[0], nv0[1], nv0[2], nv0[3]);
+  d.nv1 = make_float4(nv1[0], nv1[1], nv1[2], nv1[3]);
 }
 
 template <int G>
@@ -93,8 +209,8 @@ struct Consts {
   const uint4* qop_lo;   // G = 16: the lo halves, same layout
   float fscale;
   bool lo_lane;
-  uint32_t lane_off;    // this lane's copy of the 3-bit table: (lane & 31) * 8
-  uint32_t klane_off;   // and of the 4-bit K table: (lane & 15) * 8
+  uint32_t lane_off;    // this lane's copy of the 3-bit table: (lane % kLutCopies) * 8
+  uint32_t klane_off;   // and of the 4-bit K table: (lane % kKLutCopies) * 8
   int rel_lo, rel_hi;
   const char* lut;    // 3-bit code pairs (V, and K when 3-bit)
   const char* klut;   // 4-bit K code pairs
@@ -208,21 +324,18 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
 }
 
 // LDS of one packed split work-group.
+// (the staged blocks and, after the loop, the wave accumulators are in a
+// StageMem beside it)
 template <int G, int KB>
 struct PackedSmem {
   static constexpr bool kSplitN = (G <= 8);        // hi/lo halves share one MFMA (columns / rows g and g+8)
-  static constexpr int kRows = kSplitN ? 2 * G : G;   // accumulator rows kept per wave (hi and lo halves)
   uint2 lut[kLutEntries * kLutCopies];
-  // the wave accumulators after the loop; during it (4-bit K) the K code-pair table
-  union {
-    float wo[kWaves][kRows][kDim];
-    uint2 klut[KB == 4 ? 256 * kKLutCopies : 2];
-  } big;
+  uint2 klut[KB == 4 ? 256 * kKLutCopies : 2];
   // query operand of k-step kk for lane 16 q + n: dims 32 q + 4 kk + e (e = 0..3) of
   // head n & 7, each value twice (one fp16 pair); hi halves in columns n < 8, lo
   // halves in n >= 8 (G = 16: hi in qop, lo in qop_lo, column n = head n)
   uint4 qop[8][64];
-  uint4 qop_lo[kSplitN ? 1 : 8][64];
+  uint4 qop_lo[kSplitN ? 1 : 8][kSplitN ? 1 : 64];   // (unused when kSplitN)
   float mats[kBlocks * 16];   // the head's 32 block matrices, row-major
   float qmax[G];
   float wm[kWaves][G], wl[kWaves][G];
@@ -231,7 +344,8 @@ struct PackedSmem {
 // One split of the packed decode: work-group (h = KV head, s = sequence,
 // split). Records go to split index a.rec_offset + split of a.rec_splits.
 template <int G, int KB>
-__device__ __forceinline__ void packed_split(const DecodeArgs& a, PackedSmem<G, KB>& sm, int split) {
+__device__ __forceinline__ void packed_split(const DecodeArgs& a, PackedSmem<G, KB>& sm, StageMem<G, KB>& stg,
+                                             int split) {
 #include "iq_decode_packed_body.inc"
 
 }
