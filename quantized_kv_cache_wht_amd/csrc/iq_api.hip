@@ -315,9 +315,14 @@ iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_ne
        reinterpret_cast<uintptr_t>(workspace)) & 15u)
     return IQ_ERR_INVALID_ARG;
   if (n_seqs > 65535 || view->num_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
-  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, decode_plan(n_seqs, view->num_kv_heads, max_seq_len)))
-    return IQ_ERR_WORKSPACE;
-  const DecodePlan plan = decode_plan(n_seqs, view->num_kv_heads, max_seq_len, 1);
+  const DecodePlan plain = decode_plan(n_seqs, view->num_kv_heads, max_seq_len);
+  if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, plain)) return IQ_ERR_WORKSPACE;
+  // The new token's work-groups join the split launch: if they and the plain
+  // plan's splits do not all fit on the GPU at once, the plan leaves them room
+  // (a second round of work-groups would cost a whole split's time).
+  const int64_t wgs = static_cast<int64_t>(plain.n_splits + 1) * n_seqs * view->num_kv_heads;
+  const DecodePlan plan =
+      wgs <= split_new_resident_wgs(group, view->k_bits) ? plain : decode_plan(n_seqs, view->num_kv_heads, max_seq_len, 1);
   DecodeArgs a{};
   a.k_codes = view->k_codes;
   a.v_codes = view->v_codes;

@@ -35,6 +35,8 @@
 // of nV), raised lazily (only when a block exceeds it by more than 2^8), so
 // p_t nV_t <= 256 and the fp16 operand never overflows while accumulator
 // rescaling is rare.
+#include <atomic>
+
 #include "iq_decode_packed.h"
 #include "iq_decode_new_token.h"
 
@@ -234,6 +236,39 @@ static hipError_t launch_split(const DecodeArgs& a, const NewToken& nt, hipStrea
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int KB>
+static const void* split_new_kernel(int group) {
+  switch (group) {
+    case 1: return reinterpret_cast<const void*>(&decode_split_kernel<1, KB, true>);
+    case 2: return reinterpret_cast<const void*>(&decode_split_kernel<2, KB, true>);
+    case 4: return reinterpret_cast<const void*>(&decode_split_kernel<4, KB, true>);
+    case 8: return reinterpret_cast<const void*>(&decode_split_kernel<8, KB, true>);
+    case 16: return reinterpret_cast<const void*>(&decode_split_kernel<16, KB, true>);
+    default: return nullptr;
+  }
+}
+
+int64_t split_new_resident_wgs(int group, int k_bits) {
+  // per device (up to 64), group (1, 2, 4, 8, 16) and K width; 0 = not yet asked
+  constexpr int kDevices = 64;
+  static std::atomic<int64_t> cache[kDevices][5][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
+  const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : group == 16 ? 4 : -1;
+  if (gi < 0) return 0;
+  std::atomic<int64_t>& slot = cache[dev][gi][k_bits == 4 ? 1 : 0];
+  int64_t v = slot.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  const void* f = k_bits == 4 ? split_new_kernel<4>(group) : split_new_kernel<3>(group);
+  int per_cu = 0, cus = 0;
+  if (f == nullptr || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kDecThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = static_cast<int64_t>(per_cu) * cus;
+  if (v > 0) slot.store(v, std::memory_order_relaxed);
+  return v;
 }
 
 hipError_t launch_decode_splits(const DecodeArgs& a, hipStream_t st) {

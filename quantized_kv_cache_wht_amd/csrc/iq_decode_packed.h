@@ -104,11 +104,20 @@ struct StageMem {
 // One global->LDS load: 16 bytes per lane from base + voff (base wave-uniform)
 // to LDS address lds + 16 * lane. Written as inline asm: the compiler's own
 // form of it is not kept inside divergent branches (it merged the two halves
-// of a conditional pair of these into one load with the wrong LDS base).
+// of a conditional pair of these into one load with the wrong LDS base). M0,
+// which holds the LDS address, is saved and restored around the load (the
+// compiler does not let inline asm clobber it).
 __device__ __forceinline__ void load_lds16(uintptr_t base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               ::"v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
 }
 
 // Copies block `slot` (absolute slot of the head's cache row, a multiple of

@@ -185,5 +185,9 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 // work-group per (KV head, seq) encodes the new token and writes its records
 hipError_t launch_decode_splits(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_splits_new(const DecodeArgs& a, const NewToken& nt, hipStream_t s);
+// Work-groups of the append-decode split kernel for (group, K bits) that the
+// current device holds at once (occupancy x CUs, asked once per device); 0 if
+// the runtime cannot say.
+int64_t split_new_resident_wgs(int group, int k_bits);
 
 }  // namespace iq
