@@ -36,7 +36,10 @@ constexpr int kMaxSplits = 2048;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeLanes = kDim / 4;                    // lanes per record, 4 dims each
 constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by side
-constexpr int kMergeChunk = 4;                           // records per lane per round of loads
+// records per lane per round of loads (a fifth, so that 129 records take one
+// round, measured no faster: a merge work-group is bound by how fast its CU
+// pulls the ~68 KB of records, not by the rounds)
+constexpr int kMergeChunk = 4;
 constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
 
 // Max (or sum) of x over lanes i and i ^ 16, then i ^ 32, of a full wave: the

@@ -214,8 +214,8 @@ __device__ __forceinline__ void read_stage(uint32_t ka, uint32_t va, uint32_t na
 
 template <int G>
 struct Consts {
-  const uint4* qop;      // this lane's query operand of k-step kk at qop[64 kk] (LDS)
-  const uint4* qop_lo;   // G = 16: the lo halves, same layout
+  uint4 q[8];            // this lane's query operand of k-step kk (registers: read every block)
+  const uint4* qop_lo;   // G = 16: the lo halves, at qop_lo[64 kk] (LDS)
   float fscale;
   bool lo_lane;
   uint32_t lane_off;    // this lane's copy of the 3-bit table: (lane % kLutCopies) * 8
@@ -238,7 +238,7 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
     const half8 kb = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw1, c.klut, c.klane_off) \
                              : code_operand<12 * KAPPA>(cur.kw1, c.lut, c.lane_off);  \
     H8 qv;                                                                     \
-    qv.u4 = c.qop[64 * KAPPA];                                                 \
+    qv.u4 = c.q[KAPPA];                                                        \
     d0 = mfma16(ka, qv.h, d0);                                                 \
     d1 = mfma16(kb, qv.h, d1);                                                 \
     if (!kSplitN) {                                                            \
