@@ -299,6 +299,15 @@ __device__ __forceinline__ void f16_split(const F16DecodeArgs& a, F16Smem<G>& sm
     f16_softmax_pv<G>(d0, d1, vt, b * kBlk, lane, c, st);
     b += kWaves;
   }
+  // Every accumulator element is read once (see the packed kernel's body:
+  // with G < 4 some are never stored, and their registers must not be reused
+  // while the MFMA writing them is in flight).
+  {
+    float sink = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) sink += (st.acc[d][0] + st.acc[d][1]) + (st.acc[d][2] + st.acc[d][3]);
+    asm volatile("" ::"v"(sink));
+  }
 
   // ---- per-wave totals ----
   float l_run = st.l;

@@ -225,12 +225,19 @@ struct Consts {
   const char* klut;   // 4-bit K code pairs
 };
 
+// One 32-slot block of the loop, in three parts (running the next block's
+// scores beside this block's PV product was built and measured slower: 167
+// VGPRs, no gain from the interleaving):
+//   block_scores:  D_T[i] = row 4q + i of tile T = token 8q + 4T + i, column n
+//   block_softmax: the scores in log2 units, the running reference, the
+//                  weights p = 2^(s - m) nV as fp16 operands
+//   block_pv:      acc[D] += P x (V centroids of dims 8n + D)
 template <int G, int KB>
-__device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot0, int q, const Consts<G>& c,
-                                              WaveState& st) {
+__device__ __forceinline__ void block_scores(const BlockData<KB>& cur, const Consts<G>& c, floatx4& d0,
+                                             floatx4& d1) {
   constexpr bool kSplitN = (G <= 8);
-  // ---- scores: D_T[i] = row 4q + i of tile T = token 8q + 4T + i, column n ----
-  floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+  d0 = floatx4{0.f, 0.f, 0.f, 0.f};
+  d1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #define IQ_SCORE(KAPPA)                                                        \
   {                                                                            \
     const half8 ka = KB == 4 ? code_operand4<16 * KAPPA>(cur.kw0, c.klut, c.klane_off) \
@@ -249,6 +256,19 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
   }
   IQ_SCORE(0) IQ_SCORE(1) IQ_SCORE(2) IQ_SCORE(3) IQ_SCORE(4) IQ_SCORE(5) IQ_SCORE(6) IQ_SCORE(7)
 #undef IQ_SCORE
+}
+
+// P operands of one block: rows 2i, 2i + 1 of token group T hold token i's
+// weight (hi for G <= 8 in rows g, lo in rows g + 8; G = 16: hi in pa, lo in pa_lo)
+struct BlockWeights {
+  H8 pa[2], pa_lo[2];
+};
+
+template <int G, int KB>
+__device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& d1, const BlockData<KB>& cur,
+                                              int slot0, int q, const Consts<G>& c, WaveState& st,
+                                              BlockWeights& w) {
+  constexpr bool kSplitN = (G <= 8);
   const float nk[8] = {cur.nk0.x, cur.nk0.y, cur.nk0.z, cur.nk0.w, cur.nk1.x, cur.nk1.y, cur.nk1.z, cur.nk1.w};
   float nv[8] = {cur.nv0.x, cur.nv0.y, cur.nv0.z, cur.nv0.w, cur.nv1.x, cur.nv1.y, cur.nv1.z, cur.nv1.w};
   float t[8];
@@ -299,7 +319,6 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
   }
   const float mref = (st.m == -INFINITY) ? 0.f : st.m;
   // weights: token group T = tokens 8q + 4T + i; A slots (2i, 2i+1) both hold token i's weight
-  H8 pa[2], pa_lo[2];
   float esum = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -309,27 +328,43 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
     // hi = p truncated to 11 significant bits (exact in fp16), lo = the rest
     const float hp = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) & 0xffffe000u);
     if (kSplitN) {
-      pa[k >> 2].u[k & 3] = dup16(c.lo_lane ? p - hp : hp);
+      w.pa[k >> 2].u[k & 3] = dup16(c.lo_lane ? p - hp : hp);
     } else {
-      pa[k >> 2].u[k & 3] = dup16(hp);
-      pa_lo[k >> 2].u[k & 3] = dup16(p - hp);
+      w.pa[k >> 2].u[k & 3] = dup16(hp);
+      w.pa_lo[k >> 2].u[k & 3] = dup16(p - hp);
     }
   }
   st.l += esum;
-  // ---- PV: B = centroids of dim 8n + D for the 4 tokens 4T..4T+3 of V tile q ----
+}
+
+// PV: B = centroids of dim 8n + D for the 4 tokens 4T..4T+3 of V tile q
+template <int G>
+__device__ __forceinline__ void block_pv(const uint32_t (&vw)[6], const BlockWeights& w, const Consts<G>& c,
+                                         WaveState& st) {
+  constexpr bool kSplitN = (G <= 8);
 #define IQ_PV(D)                                                                     \
   {                                                                                  \
-    const half8 v0 = code_operand<24 * D>(cur.vw, c.lut, c.lane_off);                \
-    const half8 v1 = code_operand<24 * D + 12>(cur.vw, c.lut, c.lane_off);           \
-    st.acc[D] = mfma16(pa[0].h, v0, st.acc[D]);                                      \
-    st.acc[D] = mfma16(pa[1].h, v1, st.acc[D]);                                      \
+    const half8 v0 = code_operand<24 * D>(vw, c.lut, c.lane_off);                    \
+    const half8 v1 = code_operand<24 * D + 12>(vw, c.lut, c.lane_off);               \
+    st.acc[D] = mfma16(w.pa[0].h, v0, st.acc[D]);                                    \
+    st.acc[D] = mfma16(w.pa[1].h, v1, st.acc[D]);                                    \
     if (!kSplitN) {                                                                  \
-      st.acc[D] = mfma16(pa_lo[0].h, v0, st.acc[D]);                                 \
-      st.acc[D] = mfma16(pa_lo[1].h, v1, st.acc[D]);                                 \
+      st.acc[D] = mfma16(w.pa_lo[0].h, v0, st.acc[D]);                               \
+      st.acc[D] = mfma16(w.pa_lo[1].h, v1, st.acc[D]);                               \
     }                                                                                \
   }
   IQ_PV(0) IQ_PV(1) IQ_PV(2) IQ_PV(3) IQ_PV(4) IQ_PV(5) IQ_PV(6) IQ_PV(7)
 #undef IQ_PV
+}
+
+template <int G, int KB>
+__device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot0, int q, const Consts<G>& c,
+                                              WaveState& st) {
+  floatx4 d0, d1;
+  BlockWeights w;
+  block_scores<G, KB>(cur, c, d0, d1);
+  block_softmax<G, KB>(d0, d1, cur, slot0, q, c, st, w);
+  block_pv<G>(cur.vw, w, c, st);
 }
 
 // LDS of one packed split work-group.
