@@ -445,6 +445,10 @@ def test_decode_k4_matches_oracle(kind, hq, hkv, lens):
     (16, 1, [513, 3], 4, "wht_so4", True),
     (32, 8, [13, 4096, 31], 4, "iso", True),
     (4, 4, [300, 7], 3, "wht_so4", False),
+    # full occupancy with 4-bit K (two work-groups per CU): the plain plan's 512 splits and the 4
+    # new-token work-groups do not fit at once, so the plan leaves them room (the 3-bit case at this
+    # shape keeps the plain plan: test_gpu_fullsize's decode step)
+    (32, 4, [32767], 4, "wht_so4", True),
 ])
 def test_append_decode_equals_append_then_decode(hq, hkv, lens, k_bits, kind, f16):
     """The fused step writes the same codes and norms as iq_rotate_quantize_append and returns the
