@@ -67,14 +67,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
 // then out = Hn B^T (o' / l), the single inverse rotation (kRotate; the fp16
 // decode's records are already in the model's basis). Lane t first reads
 // dims 4 (t % 32) .. +3 of records t / 32, t / 32 + 32, ... (coalesced), keeps
-// a running merge of them, and parks the result in LDS; the 32 rows are then
-// combined with one row per lane of a half-wave. An empty sequence gives 0,
-// an invalid one NaN.
+// a running merge of them, and parks the result in LDS; wave 0 then combines
+// the 32 rows and rotates, two dims per lane. An empty sequence gives 0, an
+// invalid one NaN.
 template <bool kRotate>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
   __shared__ float rm[kMergeRows], rl[kMergeRows];
   __shared__ __align__(16) float ro[kMergeRows][kDim];
-  __shared__ __align__(16) float fin[kDim];
   __shared__ __align__(16) float mats[kBlocks * 16];   // the head's block matrices (kRotate)
   const int hq = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, row = tid / kMergeLanes, d4 = tid % kMergeLanes;
@@ -159,42 +158,34 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   }
   reinterpret_cast<float4*>(ro[row])[d4] = o;
   __syncthreads();
-  {
-    // half-wave: lane = row (0..31), dims 4 c .. 4 c + 3 with c = tid / 32
-    const int r = tid & (kMergeRows - 1), c = tid / kMergeRows;
+  // The rest runs on wave 0 alone, two dims per lane (t and t + 64): the row
+  // partials' weights (lane r holds row r's; lanes 32..63 repeat them), their
+  // weighted sum read column-wise from LDS, then the inverse rotation in
+  // registers, with no further barrier.
+  if (tid < 64) {
+    const int t = tid;
+    const int r = t & (kMergeRows - 1);
     const float m_r = rm[r];
     const float M = half_wave_reduce<true>(m_r);
     const float w = M == -INFINITY ? 0.f : fast_exp2(m_r - M);
-    const float4 v = reinterpret_cast<const float4*>(ro[r])[c];
     const float L = half_wave_reduce<false>(w * rl[r]);
-    const float o0 = half_wave_reduce<false>(w * v.x);
-    const float o1 = half_wave_reduce<false>(w * v.y);
-    const float o2 = half_wave_reduce<false>(w * v.z);
-    const float o3 = half_wave_reduce<false>(w * v.w);
-    if (r == 0) {
-      const float inv = L > 0.f ? 1.0f / L : 0.f;
-      reinterpret_cast<float4*>(fin)[c] = make_float4(o0 * inv, o1 * inv, o2 * inv, o3 * inv);
-    }
-  }
-  __syncthreads();
-  if (tid < 16) {
-    float x[8];
+    float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = fin[8 * tid + i];
+    for (int k = 0; k < kMergeRows; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+      x0 = __builtin_fmaf(wk, ro[k][t], x0);
+      x1 = __builtin_fmaf(wk, ro[k][t + 64], x1);
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    x0 *= inv;
+    x1 *= inv;
     if (kRotate) {
-      float m[32];
-      const float4* mp = reinterpret_cast<const float4*>(mats + 32 * tid);   // blocks 2 tid, 2 tid + 1
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = mp[i];
-        m[4 * i] = v.x; m[4 * i + 1] = v.y; m[4 * i + 2] = v.z; m[4 * i + 3] = v.w;
-      }
-      so4_apply_row<true>(x, m);
-      if (a.rot_kind == kRotWhtSo4) wht128_row(x, tid);
+      so4_apply_pair<true>(x0, x1, mats, t);
+      if (a.rot_kind == kRotWhtSo4) wht128_pair(x0, x1, t);
     }
-    float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim + 8 * tid);
-    dst[0] = ok ? make_float4(x[0], x[1], x[2], x[3]) : make_float4(NAN, NAN, NAN, NAN);
-    dst[1] = ok ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(NAN, NAN, NAN, NAN);
+    float* dst = a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim;
+    dst[t] = ok ? x0 : NAN;
+    dst[t + 64] = ok ? x1 : NAN;
   }
 }
 

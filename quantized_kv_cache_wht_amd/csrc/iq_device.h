@@ -298,6 +298,72 @@ __device__ __forceinline__ float row_xor(float x) {
   return x;
 }
 
+// Value of lane t ^ M of the wave for M = 16 or 32: the gfx950 row swaps hand
+// each lane itself and that partner, and the partner is the one whose bits
+// differ from the lane's own (either one when they are equal).
+template <int M>
+__device__ __forceinline__ float lane_xor_far(float x) {
+  static_assert(M == 16 || M == 32, "row swap partners");
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  uint32_t r0, r1;
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  return __builtin_bit_cast(float, r0 == b ? r1 : r0);
+}
+
+// A 128-vector held two dims per lane of a full wave: dims t and t + 64 in
+// lane t (x0, x1).
+//   so4_apply_pair: the block-diagonal SO(4) product (kTranspose: B^T) with
+//     the block matrices in mats (row-major 4x4 per block); the four dims of
+//     a block are the lanes of one quad, fetched by quad broadcasts.
+//   wht128_pair: the unnormalised Sylvester Hadamard transform: bit 6 of the
+//     dim in the lane, bits 5 and 4 by row swaps, bits 3..0 within a row.
+template <bool kTranspose>
+__device__ __forceinline__ void so4_apply_pair(float& x0, float& x1, const float* mats, int t) {
+  const int i = t & 3;
+  const float* m0 = mats + 16 * (t >> 2);
+  const float* m1 = m0 + 16 * 16;   // dim t + 64: block t / 4 + 16
+  const float u0[4] = {dpp_f32<0x00>(x0), dpp_f32<0x55>(x0), dpp_f32<0xAA>(x0), dpp_f32<0xFF>(x0)};
+  const float u1[4] = {dpp_f32<0x00>(x1), dpp_f32<0x55>(x1), dpp_f32<0xAA>(x1), dpp_f32<0xFF>(x1)};
+  float a0[4], a1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a0[j] = kTranspose ? m0[j * 4 + i] : m0[i * 4 + j];
+    a1[j] = kTranspose ? m1[j * 4 + i] : m1[i * 4 + j];
+  }
+  x0 = __builtin_fmaf(a0[3], u0[3], __builtin_fmaf(a0[2], u0[2], __builtin_fmaf(a0[1], u0[1], a0[0] * u0[0])));
+  x1 = __builtin_fmaf(a1[3], u1[3], __builtin_fmaf(a1[2], u1[2], __builtin_fmaf(a1[1], u1[1], a1[0] * u1[0])));
+}
+
+__device__ __forceinline__ void wht128_pair(float& x0, float& x1, int t) {
+  {
+    const float a = x0, b = x1;
+    x0 = a + b;
+    x1 = a - b;
+  }
+  // the lane with the bit set keeps (partner - self)
+#define IQ_PAIR_STAGE(M, FETCH)                      \
+  {                                                  \
+    const float sgn = (t & (M)) ? -1.0f : 1.0f;      \
+    x0 = __builtin_fmaf(x0, sgn, FETCH(x0));         \
+    x1 = __builtin_fmaf(x1, sgn, FETCH(x1));         \
+  }
+  IQ_PAIR_STAGE(32, lane_xor_far<32>)
+  IQ_PAIR_STAGE(16, lane_xor_far<16>)
+  IQ_PAIR_STAGE(8, row_xor<8>)
+  IQ_PAIR_STAGE(4, row_xor<4>)
+  IQ_PAIR_STAGE(2, row_xor<2>)
+  IQ_PAIR_STAGE(1, row_xor<1>)
+#undef IQ_PAIR_STAGE
+}
+
 template <int M>
 __device__ __forceinline__ void wht_row_stage(float (&x)[8], int p) {
   const float s = (p & M) ? -1.0f : 1.0f;   // the lane with the bit set keeps (partner - self)
