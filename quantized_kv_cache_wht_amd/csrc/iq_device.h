@@ -239,31 +239,39 @@ __device__ __forceinline__ void load_block_params(const float* rot_head, int kin
 // The 32 block matrices of one head into LDS (row-major, 16 floats per
 // block), one column per thread: threads 0..127 work, with bp from
 // load_block_params(rot_head, kind, (threadIdx.x >> 2) & 31, bp).
+// kQuadOrder: block 8 p + b (the b-th block of quad-form lane part p) goes to
+// slot 4 b + p, so that the four lanes of a vector, reading their b-th blocks
+// together, hit different LDS banks (block-major order puts them 512 bytes
+// apart, all in one bank); otherwise block-major.
+template <bool kQuadOrder = false>
 __device__ __forceinline__ void build_head_matrices(int kind, const float (&bp)[8], float* sm) {
   const int t = threadIdx.x;
   if (t < 4 * kBlocks) {
     const int b = t >> 2, c = t & 3;
+    const int slot = kQuadOrder ? (b & 7) * 4 + (b >> 3) : b;
     float col[4];
     block_column(kind, bp, c, col);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm[b * 16 + r * 4 + c] = col[r];
+    for (int r = 0; r < 4; ++r) sm[slot * 16 + r * 4 + c] = col[r];
   }
 }
 
-// Fill LDS with the 32 block matrices of one head (row-major). Must be called
-// by all threads of the block (at least 128): threads 0..127 build one column each.
+// Fill LDS with the 32 block matrices of one head (row-major each, in the
+// quad-form order that so4_apply_lane reads). Must be called by all threads of
+// the block (at least 128): threads 0..127 build one column each.
 __device__ __forceinline__ void load_head_matrices(const float* __restrict__ rot_head, int kind, float* sm) {
   float bp[8];
   load_block_params(rot_head, kind, (threadIdx.x >> 2) & (kBlocks - 1), bp);
-  build_head_matrices(kind, bp, sm);
+  build_head_matrices<true>(kind, bp, sm);
 }
 
-// y_b = M_b y_b for this lane's 8 blocks (transpose = use M_b^T).
+// y_b = M_b y_b for this lane's 8 blocks (transpose = use M_b^T); the
+// matrices as load_head_matrices lays them out (block 8 part + b at slot 4 b + part).
 template <bool kTranspose>
 __device__ __forceinline__ void so4_apply_lane(float (&x)[kPerLane], const float* sm, int part) {
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    const float4* mp = reinterpret_cast<const float4*>(sm + (part * 8 + b) * 16);
+    const float4* mp = reinterpret_cast<const float4*>(sm + (b * 4 + part) * 16);
     const float4 r0 = mp[0], r1 = mp[1], r2 = mp[2], r3 = mp[3];
     const float m[16] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w,
                          r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};

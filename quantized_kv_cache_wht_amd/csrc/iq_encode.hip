@@ -53,6 +53,44 @@ __device__ __forceinline__ void load_vec<_Float16>(const _Float16* __restrict__ 
   }
 }
 
+// This lane's inputs of one vector as raw words (32 values: 4 uint4 for fp16,
+// 8 for fp32), loaded unconditionally from a valid address, so that the load
+// can be issued a window ahead and waited for only where raw_to_x uses it.
+template <typename T>
+struct RawVec {
+  static constexpr int kWords = kPerLane * sizeof(T) / 16;
+  uint4 w[kWords];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_raw(const T* __restrict__ src, RawVec<T>& r) {
+#pragma unroll
+  for (int i = 0; i < RawVec<T>::kWords; ++i) r.w[i] = reinterpret_cast<const uint4*>(src)[i];
+}
+
+template <typename T>
+__device__ __forceinline__ void raw_to_x(const RawVec<T>& r, bool ok, float (&x)[kPerLane]) {
+  if constexpr (sizeof(T) == 2) {
+    typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int i = 0; i < RawVec<T>::kWords; ++i) {
+      const half8 v = __builtin_bit_cast(half8, r.w[i]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = static_cast<float>(v[k]);
+        x[8 * i + k] = ok ? f : 0.f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RawVec<T>::kWords; ++i) {
+      const uint32_t u[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = ok ? __builtin_bit_cast(float, u[k]) : 0.f;
+    }
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_vec(T* __restrict__ dst, const float (&x)[kPerLane]);
 
@@ -194,10 +232,16 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   };
   float x[kPerLane];
   uint32_t old[3] = {0u, 0u, 0u};
+  // raw inputs of the window being processed; the next window's are requested
+  // before this one is rotated and quantized
+  RawVec<T> raw;
+  auto src_of = [&](int w) {
+    const int tk = token_of(w);
+    const bool in = tk >= 0 && tk < a.n_tokens;
+    return src + (static_cast<size_t>(in ? tk : 0) * a.num_kv_heads + h) * kDim + part * kPerLane;
+  };
   if (win < n_windows) {
-    const int tok = token_of(win);
-    const bool ok = tok >= 0 && tok < a.n_tokens;
-    load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
+    load_raw<T>(src_of(win), raw);
     if (is_v && !scatter) {
       const uint32_t m = tile_mask(win);
       if (m != 0u && m != 0xffu) {
@@ -212,9 +256,8 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   for (; win < n_windows; win += gridDim.x) {
     const int tok = token_of(win);
     const bool ok = tok >= 0 && tok < a.n_tokens;
-    if (win != static_cast<int>(blockIdx.x)) {
-      load_vec<T>(src + (static_cast<size_t>(ok ? tok : 0) * a.num_kv_heads + h) * kDim + part * kPerLane, ok, x);
-    }
+    raw_to_x<T>(raw, ok, x);
+    if (win + static_cast<int>(gridDim.x) < n_windows) load_raw<T>(src_of(win + gridDim.x), raw);
     if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
     if (kK4 && !is_v) {
