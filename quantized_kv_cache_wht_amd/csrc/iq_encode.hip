@@ -233,7 +233,9 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   float x[kPerLane];
   uint32_t old[3] = {0u, 0u, 0u};
   // raw inputs of the window being processed; the next window's are requested
-  // before this one is rotated and quantized
+  // before this one is rotated and quantized (not for 4-bit K, where the
+  // extra registers cost a work-group per CU: measured slower)
+  constexpr bool kPrefetch = !kK4;
   RawVec<T> raw;
   auto src_of = [&](int w) {
     const int tk = token_of(w);
@@ -241,7 +243,12 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     return src + (static_cast<size_t>(in ? tk : 0) * a.num_kv_heads + h) * kDim + part * kPerLane;
   };
   if (win < n_windows) {
-    load_raw<T>(src_of(win), raw);
+    if (kPrefetch) {
+      load_raw<T>(src_of(win), raw);
+    } else {
+      const int tok = token_of(win);
+      load_vec<T>(src_of(win), tok >= 0 && tok < a.n_tokens, x);
+    }
     if (is_v && !scatter) {
       const uint32_t m = tile_mask(win);
       if (m != 0u && m != 0xffu) {
@@ -256,8 +263,12 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   for (; win < n_windows; win += gridDim.x) {
     const int tok = token_of(win);
     const bool ok = tok >= 0 && tok < a.n_tokens;
-    raw_to_x<T>(raw, ok, x);
-    if (win + static_cast<int>(gridDim.x) < n_windows) load_raw<T>(src_of(win + gridDim.x), raw);
+    if (kPrefetch) {
+      raw_to_x<T>(raw, ok, x);
+      if (win + static_cast<int>(gridDim.x) < n_windows) load_raw<T>(src_of(win + gridDim.x), raw);
+    } else if (win != static_cast<int>(blockIdx.x)) {
+      load_vec<T>(src_of(win), ok, x);
+    }
     if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
     so4_apply_lane<false>(x, sm, part);
     if (kK4 && !is_v) {
