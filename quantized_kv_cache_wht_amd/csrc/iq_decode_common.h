@@ -48,9 +48,25 @@ constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference 
 // reduction (one instruction per step, no lane-index arithmetic). The halves
 // are copied to scalars before the bit casts: a bit cast of a vector element
 // is compiled as a read of the vector's first element.
+// Max of floats as the hardware computes it (a quiet NaN operand yields the
+// other one, as fmaxf does). fmaxf itself is compiled with a canonicalising
+// max of each operand not known to be canonical (loads, inline-asm outputs,
+// lane exchanges) in front: two or three instructions per max. No signalling
+// NaN reaches these.
+__device__ __forceinline__ float max_hw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_hw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <bool kMax>
 __device__ __forceinline__ float rows_reduce(float x) {
-  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  auto op = [](float u, float v) { return kMax ? max_hw(u, v) : u + v; };
   const uint32_t b = __builtin_bit_cast(uint32_t, x);
   const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
   const uint32_t a0 = r16[0], a1 = r16[1];

@@ -264,7 +264,11 @@ struct BlockWeights {
   H8 pa[2], pa_lo[2];
 };
 
-template <int G, int KB>
+// kFull: every slot of the block lies in the sequence (the caller's
+// wave-uniform test), so no slot is masked. A separate instantiation rather
+// than a branch inside: a branch that may rewrite the scores and norms costs
+// the common case a copy of each at the join.
+template <int G, int KB, bool kFull>
 __device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& d1, const BlockData<KB>& cur,
                                               int slot0, int q, const Consts<G>& c, WaveState& st,
                                               BlockWeights& w) {
@@ -282,23 +286,18 @@ __device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& 
     if (kSplitN) t[k] += dpp_row_ror8(t[k]);
     t[k] *= nk[k] * c.fscale;             // the score, log2 units
   }
-  float nvmax;
-  const bool full = slot0 >= c.rel_lo && slot0 + kBlk <= c.rel_hi;   // wave-uniform
-  if (full) {
-    nvmax = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])), fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
-  } else {
-    nvmax = 0.f;
+  if constexpr (!kFull) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int rel = slot0 + 8 * q + k;
       const bool valid = rel >= c.rel_lo && rel < c.rel_hi;
       t[k] = valid ? t[k] : -INFINITY;    // 2^-inf = 0 below
       nv[k] = valid ? nv[k] : 0.f;        // a slot outside the range may hold anything
-      nvmax = fmaxf(nvmax, nv[k]);
     }
   }
+  const float nvmax = max_hw(max3_hw(nv[0], nv[1], nv[2]), max3_hw(max3_hw(nv[3], nv[4], nv[5]), nv[6], nv[7]));
   // ---- online softmax with a lazily raised reference ----
-  const float tmax = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+  const float tmax = max_hw(max3_hw(t[0], t[1], t[2]), max3_hw(max3_hw(t[3], t[4], t[5]), t[6], t[7]));
   const int ex = __builtin_amdgcn_frexp_expf(nvmax);
   float u = tmax + (ex > 0 ? static_cast<float>(ex) : 0.f);
   u = rows_reduce<true>(u);
@@ -363,7 +362,10 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
   floatx4 d0, d1;
   BlockWeights w;
   block_scores<G, KB>(cur, c, d0, d1);
-  block_softmax<G, KB>(d0, d1, cur, slot0, q, c, st, w);
+  if (slot0 >= c.rel_lo && slot0 + kBlk <= c.rel_hi)   // wave-uniform
+    block_softmax<G, KB, true>(d0, d1, cur, slot0, q, c, st, w);
+  else
+    block_softmax<G, KB, false>(d0, d1, cur, slot0, q, c, st, w);
   block_pv<G>(cur.vw, w, c, st);
 }
 
