@@ -16,7 +16,9 @@ Printed JSON line: value = packed K/V bytes of the attended tokens per step /
 step time (GB/s); roofline = the step's launch pair (split + merge kernels;
 HIP events on the launch stream around runs of back-to-back launches) against
 the 8 TB/s HBM peak, with the HBM traffic per launch from the committed
-counter summary when it matches the decode sources; comparisons = decode
+counter summary when it matches the decode sources; valu_roof = the same
+launch pair's VALU instructions (same summary) against the chip's VALU issue
+rate; comparisons = decode
 alone, append + decode as two calls, the FP16-KV and unfused paths, the
 rotation variants and 4-bit K; cpu_baseline = the CPU oracle's decode on a
 bounded sample of the same workload. The quantize-append rate is measured on
@@ -36,6 +38,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# VALU issue roof: one wave64 VALU instruction per clock per CU (4 SIMDs x 16
+# lanes; fp32 without packed math), 256 CUs at 2.4 GHz, in G instructions/s
+VALU_PEAK_GINST = 256 * 2.4
 ROW_BYTES = 48 + 4          # packed codes + fp32 norm, one (token, KV head, K or V)
 SPIN_CYCLES_PER_LAUNCH = 200_000   # ~80 us of GPU clock per queued launch: more than the host needs
 
@@ -66,12 +71,12 @@ def decode_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, if it was taken on
-    the current decode sources; else None."""
+def measured_counters(workload: str) -> dict:
+    """The per-launch counter figures of the committed summary (HBM bytes, VALU and
+    MFMA instructions), if it was taken on the current decode sources; else {}."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     with open(path) as f:
         for line in f:
@@ -79,11 +84,19 @@ def measured_traffic(workload: str):
                 k, v = line[2:].strip().split(": ", 1)
                 fields[k.strip("`")] = v.strip().strip("`")
     if fields.get("decode_source_sha256") != decode_source_digest():
-        return None
-    try:
-        return float(fields["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for k in ("hbm_bytes_per_launch", "valu_insts_per_launch", "mfma_insts_per_launch"):
+        try:
+            out[k] = float(fields[k])
+        except (KeyError, ValueError):
+            pass
+    return out
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, or None."""
+    return measured_counters(workload).get("hbm_bytes_per_launch")
 
 
 def time_per_call(torch, fn, n_calls, stream):
@@ -453,7 +466,9 @@ def main():
     torch.cuda.synchronize()
     dec_us = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 / L for r in range(reps)])
     achieved = bytes_per_launch / (dec_us.mean() * 1e-6) / 1e9
-    traffic = measured_traffic(w.name)
+    counters = measured_counters(w.name)
+    traffic = counters.get("hbm_bytes_per_launch")
+    valu = counters.get("valu_insts_per_launch")
     comp = None if args.no_compare else comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv,
                                                      T, hkv, float(dec_us.mean()), new_k, new_v)
     others = None if args.no_compare else other_workloads(iq, stream)
@@ -493,6 +508,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
+        # the same launch pair against the VALU issue roof (instruction count from the
+        # committed counter summary, time from the events above; null when stale)
+        "valu_roof": None if valu is None else {
+            "bound": "alu", "achieved": round(valu / (dec_us.mean() * 1e-6) / 1e9, 2), "peak": VALU_PEAK_GINST,
+            "unit": "Ginst/s", "frac": round(valu / (dec_us.mean() * 1e-6) / 1e9 / VALU_PEAK_GINST, 4),
+            "valu_insts_per_launch": round(valu), "mfma_insts_per_launch": round(counters.get("mfma_insts_per_launch", 0))},
         "comparisons": comp,
         "other_workloads": others,
     }

@@ -6,10 +6,13 @@ step's two kernels (the split kernel instantiated for the workload's group
 size with the new token's work-groups, and the merge), scales each counter by what it
 reads for the run's own device-to-device copies of N MiB (their true traffic
 is N MiB read and N MiB written), and writes the summary that bench.py reports
-as roofline.traffic when the decode sources still match.
+as roofline.traffic when the decode sources still match. With --insts, a third
+run's instruction counters (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_INSTS_LDS,
+SQ_INSTS_SALU, SQ_WAVES: wave-level instructions summed over the chip) go into
+the same summary; bench.py reports the VALU count against the VALU issue roof.
 
     python bench_traffic.py --fetch DIR --write DIR --copy-mib N --workload W \\
-        --command "..." --out profiles/decode_W_traffic.md
+        [--insts DIR] --command "..." --out profiles/decode_W_traffic.md
 """
 from __future__ import annotations
 
@@ -50,6 +53,7 @@ def main():
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--workload", required=True)
+    ap.add_argument("--insts", default=None, help="run dir of the instruction-counter pass")
     ap.add_argument("--command", required=True, help="the two profiling commands, for the record")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
@@ -74,10 +78,18 @@ def main():
         rows.append((label, f, wv))
         total += f + wv
     alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
+    inst_names = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES")
+    insts = {}
+    if a.insts:
+        runs = {c: per_kernel(a.insts, c) for c in inst_names}
+        for label, needle in (("split", f"decode_split_kernel<{group}, 3, true>"),
+                              ("merge", "decode_merge_kernel<true>")):
+            insts[label] = {c: statistics.mean(pick(runs[c], needle)) for c in inst_names}
     lines = [
-        f"# HBM traffic per decode launch: {a.workload}",
+        f"# HBM traffic{' and instructions' if insts else ''} per decode launch: {a.workload}",
         "",
-        f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one rocprofv3 run each:",
+        f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch){' and the instruction counters' if insts else ''}, "
+        f"one rocprofv3 run each:",
         "",
         "```",
         a.command,
@@ -100,6 +112,20 @@ def main():
         f"- hbm_bytes_per_launch: {total:.0f}",
         f"- fetch_scale: {f_scale:.6f}",
         f"- write_scale: {w_scale:.6f}",
+    ]
+    if insts:
+        lines[-4:-4] = [
+            "",
+            "Instructions per dispatch (wave-level, summed over the chip):",
+            "",
+            "| kernel | " + " | ".join(inst_names) + " |",
+            "|---|" + "---|" * len(inst_names),
+        ] + [f"| {label} | " + " | ".join(f"{v[c]:,.0f}" for c in inst_names) + " |" for label, v in insts.items()]
+        lines += [
+            f"- valu_insts_per_launch: {sum(v['SQ_INSTS_VALU'] for v in insts.values()):.0f}",
+            f"- mfma_insts_per_launch: {sum(v['SQ_INSTS_MFMA'] for v in insts.values()):.0f}",
+        ]
+    lines += [
         f"- decode_source_sha256: {decode_source_digest()}",
         "",
     ]
