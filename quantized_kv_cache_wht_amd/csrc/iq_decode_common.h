@@ -122,7 +122,7 @@ __device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, floatx
 }
 
 __device__ __forceinline__ float dpp_row_ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  return dpp_f32<0x128>(x);   // row_ror:8
 }
 
 // 2^x on the transcendental unit (results below 2^-126 flush to 0, which the

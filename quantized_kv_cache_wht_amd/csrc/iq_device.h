@@ -44,21 +44,31 @@ constexpr int kTileBytes = kTile * kRowBytes;   // 384
 constexpr int kQuadXor1 = 0xB1;   // [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;   // [2,3,0,1]
 
+// Lane moves with bound_ctrl set: a lane whose source is out of its row or
+// disabled reads 0. The patterns used here (quad permutations, rotations and
+// mirrors within a row) always have a source in range. A move with an "old"
+// operand of 0 instead would give the same values, but costs a v_mov that
+// initialises each destination first.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_mov_dpp(x, kCtrl, 0xF, 0xF, true);
+}
+
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, dpp_i32<kCtrl>(__builtin_bit_cast(int, x)));
 }
 
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, false));
+  return static_cast<uint32_t>(dpp_i32<kCtrl>(static_cast<int>(x)));
 }
 
 template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), kCtrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, 0xF, 0xF, false);
+  const int lo = dpp_i32<kCtrl>(static_cast<int>(u & 0xffffffffu));
+  const int hi = dpp_i32<kCtrl>(static_cast<int>(u >> 32));
   return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
 }
 
