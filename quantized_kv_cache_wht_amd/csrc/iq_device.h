@@ -497,20 +497,20 @@ __device__ __forceinline__ float quad_norm(const float (&y)[kPerLane]) {
 // signs. Valid for a finite norm (then y is finite too); code_nonfinite
 // covers the rest.
 __device__ __forceinline__ uint32_t code_of(float y, float t4, float t5, float t6) {
-  const uint32_t pos = y > 0.0f;
-  const uint32_t u = (__float_as_uint(y) & 0x7fffffffu) + 1u - pos;
+  const uint32_t npos = !(y > 0.0f);   // also for NaN
+  const uint32_t u = (__float_as_uint(y) & 0x7fffffffu) + npos;
   const uint32_t m = (u > __float_as_uint(t4)) + (u > __float_as_uint(t5)) + (u > __float_as_uint(t6));
-  return m ^ (3u + pos);   // 4 + m or 3 - m, m <= 3
+  return m ^ (4u - npos);   // 4 + m or 3 - m, m <= 3
 }
 
 // code_of for 8 values, stage by stage across the 8 (each comparison's mask
 // is read a few instructions after it is written, not right away).
 __device__ __forceinline__ void codes_of8(const float* y, float t4, float t5, float t6, uint32_t* c) {
-  uint32_t pos[8], u[8], m[8];
+  uint32_t npos[8], u[8], m[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pos[i] = y[i] > 0.0f;
+  for (int i = 0; i < 8; ++i) npos[i] = !(y[i] > 0.0f);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = (__float_as_uint(y[i]) & 0x7fffffffu) + 1u - pos[i];
+  for (int i = 0; i < 8; ++i) u[i] = (__float_as_uint(y[i]) & 0x7fffffffu) + npos[i];
 #pragma unroll
   for (int i = 0; i < 8; ++i) m[i] = u[i] > __float_as_uint(t4);
 #pragma unroll
@@ -518,19 +518,19 @@ __device__ __forceinline__ void codes_of8(const float* y, float t4, float t5, fl
 #pragma unroll
   for (int i = 0; i < 8; ++i) m[i] += u[i] > __float_as_uint(t6);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = m[i] ^ (3u + pos[i]);
+  for (int i = 0; i < 8; ++i) c[i] = m[i] ^ (4u - npos[i]);
 }
 
 // 16-level code = #{k : y > thr_k} with the symmetric thresholds of the 4-bit
 // codebook (thr_{14-k} = -thr_k, thr_7 = 0); t8..t14 are fl32(t4[8..14] n).
 // Same reading as code_of, for a finite norm.
 __device__ __forceinline__ uint32_t code16_of(float y, const float (&tp)[7]) {
-  const uint32_t pos = y > 0.0f;
-  const uint32_t u = (__float_as_uint(y) & 0x7fffffffu) + 1u - pos;
+  const uint32_t npos = !(y > 0.0f);   // also for NaN
+  const uint32_t u = (__float_as_uint(y) & 0x7fffffffu) + npos;
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < 7; ++k) m += u > __float_as_uint(tp[k]);
-  return m ^ (7u + pos);   // 8 + m or 7 - m, m <= 7
+  return m ^ (8u - npos);   // 8 + m or 7 - m, m <= 7
 }
 
 // The code of y when the vector's norm n is not finite. Then the middle

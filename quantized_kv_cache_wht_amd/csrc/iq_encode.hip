@@ -68,25 +68,24 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ src, RawVec<T>& r
   for (int i = 0; i < RawVec<T>::kWords; ++i) r.w[i] = reinterpret_cast<const uint4*>(src)[i];
 }
 
+// (A vector past the call's tokens converts its stand-in row as well: nothing
+// of it is stored.)
 template <typename T>
-__device__ __forceinline__ void raw_to_x(const RawVec<T>& r, bool ok, float (&x)[kPerLane]) {
+__device__ __forceinline__ void raw_to_x(const RawVec<T>& r, float (&x)[kPerLane]) {
   if constexpr (sizeof(T) == 2) {
     typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 #pragma unroll
     for (int i = 0; i < RawVec<T>::kWords; ++i) {
       const half8 v = __builtin_bit_cast(half8, r.w[i]);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = static_cast<float>(v[k]);
-        x[8 * i + k] = ok ? f : 0.f;
-      }
+      for (int k = 0; k < 8; ++k) x[8 * i + k] = static_cast<float>(v[k]);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < RawVec<T>::kWords; ++i) {
       const uint32_t u[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[4 * i + k] = ok ? __builtin_bit_cast(float, u[k]) : 0.f;
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = __builtin_bit_cast(float, u[k]);
     }
   }
 }
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     const int tok = token_of(win);
     const bool ok = tok >= 0 && tok < a.n_tokens;
     if (kPrefetch) {
-      raw_to_x<T>(raw, ok, x);
+      raw_to_x<T>(raw, x);
       if (win + static_cast<int>(gridDim.x) < n_windows) load_raw<T>(src_of(win + gridDim.x), raw);
     } else if (win != static_cast<int>(blockIdx.x)) {
       load_vec<T>(src_of(win), ok, x);
