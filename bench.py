@@ -116,9 +116,11 @@ def time_per_call(torch, fn, n_calls, stream):
 
 def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, fused_us, new_k, new_v,
                 n_layers=8):
-    """The pages' comparisons on this workload's decode, over n_layers layers' caches in turn:
-    the same decode over an fp16 K/V cache (FP16-KV baseline, K/V of the same shape and value
-    model), and the unfused path (iq_dequantize of the packed cache to fp16, then that decode)."""
+    """The pages' comparisons on this workload's decode: the same decode over an fp16 K/V cache
+    (FP16-KV baseline, K/V of the same shape and value model) and the unfused path (iq_dequantize
+    of the packed cache to fp16, then that decode), over n_layers layers' caches in turn (fp16
+    caches of that many layers exceed the last-level cache); the decode alone and the step as two
+    calls over all of the step's packed caches, as the fused step runs."""
     import torch
     k16 = [synth_kv(T, 30_000 + l).transpose(0, 1).contiguous() for l in range(n_layers)]   # [Hkv][T][128]
     v16 = [synth_kv(T, 40_000 + l).transpose(0, 1).contiguous() for l in range(n_layers)]
@@ -140,22 +142,24 @@ def comparisons(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, 
                                    workspace=ws, stream=stream)
 
     n = 4 * n_layers
+    n_packed = len(caches)
 
     def decode_only(i):
-        l = i % n_layers
+        l = i % n_packed
         iq.iq_decode_attention(caches[l], qs[l], seq_start, seq_len, T, out=outs[l], workspace=ws, stream=stream)
 
     def append_then_decode(i):
-        l = i % n_layers
+        l = i % n_packed
         iq.iq_rotate_quantize_append(caches[l], new_k[l], new_v[l], first_slot=T - 1, stream=stream)
         decode_only(i)
 
     variants = rotation_variants(iq, caches, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
     k4 = k4_decode(iq, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv)
     r = {"layers_cycled": n_layers,
+         "packed_layers_cycled": n_packed,
          "fused_step_us": round(fused_us, 3),
-         "decode_only_us": round(time_per_call(torch, decode_only, n, stream), 3),
-         "append_then_decode_us": round(time_per_call(torch, append_then_decode, n, stream), 3),
+         "decode_only_us": round(time_per_call(torch, decode_only, 2 * n_packed, stream), 3),
+         "append_then_decode_us": round(time_per_call(torch, append_then_decode, 2 * n_packed, stream), 3),
          "packed_bytes_per_launch": hkv * T * 2 * ROW_BYTES,
          "fp16_kv_decode_us": round(time_per_call(torch, fp16_decode, n, stream), 3),
          "fp16_kv_bytes_per_launch": hkv * T * 2 * 256,
