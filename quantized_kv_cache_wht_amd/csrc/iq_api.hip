@@ -119,6 +119,15 @@ static iq_status check_view(const iq_cache_view* v) {
   return IQ_OK;
 }
 
+// Device of the stream the work goes to (the current device for the null stream).
+static hipError_t stream_device(hipStream_t s, int* dev) {
+  if (s == nullptr) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(s, &d);
+  if (e == hipSuccess) *dev = static_cast<int>(d);
+  return e;
+}
+
 }  // namespace iq
 
 using namespace iq;
@@ -298,10 +307,12 @@ iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t token_st
   return hip_status(launch_decode_f16(a, static_cast<hipStream_t>(stream)));
 }
 
-iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_new, const void* v_new,
-                                     iq_dtype in_dtype, const float* q, int32_t num_q_heads, const int32_t* seq_start,
-                                     const int32_t* seq_len, int32_t n_seqs, int32_t max_seq_len, float scale,
-                                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
+// The fused decode step into a workspace of `workspace_bytes` bytes. All
+// host-side checks come first.
+static iq_status append_decode(const iq_cache_view* view, const void* k_new, const void* v_new, iq_dtype in_dtype,
+                               const float* q, int32_t num_q_heads, const int32_t* seq_start, const int32_t* seq_len,
+                               int32_t n_seqs, int32_t max_seq_len, float scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   iq_status st = check_view(view);
   if (st != IQ_OK) return st;
   if (in_dtype != IQ_F32 && in_dtype != IQ_F16) return IQ_ERR_INVALID_ARG;
@@ -310,19 +321,24 @@ iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_ne
   const int32_t group = num_q_heads / view->num_kv_heads;
   if (!group_supported(group)) return IQ_ERR_UNSUPPORTED;
   if (n_seqs == 0) return IQ_OK;
-  if (!k_new || !v_new || !q || !seq_start || !seq_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !q || !seq_start || !seq_len || !out || !workspace)
+    return IQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
        reinterpret_cast<uintptr_t>(workspace)) & 15u)
     return IQ_ERR_INVALID_ARG;
   if (n_seqs > 65535 || view->num_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
   const DecodePlan plain = decode_plan(n_seqs, view->num_kv_heads, max_seq_len);
   if (workspace_bytes < decode_workspace_bytes(n_seqs, num_q_heads, plain)) return IQ_ERR_WORKSPACE;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  if (stream_device(hs, &dev) != hipSuccess) return IQ_ERR_HIP;
   // The new token's work-groups join the split launch: if they and the plain
   // plan's splits do not all fit on the GPU at once, the plan leaves them room
   // (a second round of work-groups would cost a whole split's time).
   const int64_t wgs = static_cast<int64_t>(plain.n_splits + 1) * n_seqs * view->num_kv_heads;
-  const DecodePlan plan =
-      wgs <= split_new_resident_wgs(group, view->k_bits) ? plain : decode_plan(n_seqs, view->num_kv_heads, max_seq_len, 1);
+  const DecodePlan plan = wgs <= split_new_resident_wgs(dev, group, view->k_bits)
+                              ? plain
+                              : decode_plan(n_seqs, view->num_kv_heads, max_seq_len, 1);
   DecodeArgs a{};
   a.k_codes = view->k_codes;
   a.v_codes = view->v_codes;
@@ -356,12 +372,19 @@ iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_ne
   nt.v_codes = view->v_codes;
   nt.k_norms = view->k_norms;
   nt.v_norms = view->v_norms;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = launch_decode_splits_new(a, nt, hs);
   if (e != hipSuccess) return IQ_ERR_HIP;
   MergeArgs m{a.rot_kind, a.rot, a.out, a.ws, a.n_seqs, a.num_q_heads, a.group, a.rec_splits, 1, plan.n_splits, {}};
   m.seg[0] = MergeSegment{a.seq_start, a.seq_len, a.capacity, a.max_seq_len, a.blocks_per_split, a.n_splits, 0};
   return hip_status(launch_merge(m, hs));
+}
+
+iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_new, const void* v_new,
+                                     iq_dtype in_dtype, const float* q, int32_t num_q_heads, const int32_t* seq_start,
+                                     const int32_t* seq_len, int32_t n_seqs, int32_t max_seq_len, float scale,
+                                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return append_decode(view, k_new, v_new, in_dtype, q, num_q_heads, seq_start, seq_len, n_seqs, max_seq_len, scale,
+                       out, workspace, workspace_bytes, stream);
 }
 
 size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -31,10 +31,11 @@
 // tiles of 8 slots, dim-major, so the codes one PV operand needs (one dim,
 // consecutive tokens) are adjacent bits.
 //
-// Softmax reference m: an upper bound of s_t + log2(nV_t) (via the exponent
-// of nV), raised lazily (only when a block exceeds it by more than 2^8), so
-// p_t nV_t <= 256 and the fp16 operand never overflows while accumulator
-// rescaling is rare.
+// Softmax reference m: tracks max_t (s_t + log2 nV_t), token by token, and is
+// raised lazily (only when a weight would exceed 2^15, and then to where the
+// largest weight is 2^7), so 2^(s_t - m) nV_t stays within fp16's range with
+// normal halves over ~21 binary orders below the largest, whatever the scale
+// of the V norms, while accumulator rescaling is rare.
 #include <atomic>
 
 #include "iq_decode_packed.h"
@@ -241,22 +242,27 @@ static const void* split_new_kernel(int group) {
   }
 }
 
-int64_t split_new_resident_wgs(int group, int k_bits) {
+int64_t split_new_resident_wgs(int dev, int group, int k_bits) {
   // per device (up to 64), group (1, 2, 4, 8, 16) and K width; 0 = not yet asked
   constexpr int kDevices = 64;
   static std::atomic<int64_t> cache[kDevices][5][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
+  if (dev < 0 || dev >= kDevices) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : group == 16 ? 4 : -1;
   if (gi < 0) return 0;
   std::atomic<int64_t>& slot = cache[dev][gi][k_bits == 4 ? 1 : 0];
   int64_t v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
   const void* f = k_bits == 4 ? split_new_kernel<4>(group) : split_new_kernel<3>(group);
+  if (f == nullptr) return 0;
+  // the occupancy query answers for the current device: make it `dev` for the call
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return 0;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return 0;
   int per_cu = 0, cus = 0;
-  if (f == nullptr || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kDecThreads, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kDecThreads, 0) == hipSuccess &&
+                  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (!ok) return 0;
   v = static_cast<int64_t>(per_cu) * cus;
   if (v > 0) slot.store(v, std::memory_order_relaxed);
   return v;

@@ -40,7 +40,15 @@ constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by
 // round, measured no faster: a merge work-group is bound by how fast its CU
 // pulls the ~68 KB of records, not by the rounds)
 constexpr int kMergeChunk = 4;
-constexpr float kLazy = 8.0f;        // log2 slack before the softmax reference is raised
+// Online-softmax reference m (log2 units). A weight w = 2^(s - m) (times the
+// V norm in the packed decode) enters the PV MFMA as fp16 hi/lo halves. m is
+// raised only when some weight would exceed 2^kWeightMaxLog2, and then to
+// where the largest weight is 2^kWeightRefLog2: the weights stay below the
+// fp16 maximum (65504 > 2^15.09), and those down to 2^-21 of the largest keep
+// normal fp16 halves, so that accumulator rescaling is rare and small weights
+// keep their precision.
+constexpr float kWeightMaxLog2 = 15.0f;
+constexpr float kWeightRefLog2 = 7.0f;
 
 // Max (or sum) of x over lanes i and i ^ 16, then i ^ 32, of a full wave: the
 // gfx950 row swaps hand each lane itself and its partner, in some order, in

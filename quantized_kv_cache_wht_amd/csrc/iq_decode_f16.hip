@@ -133,12 +133,12 @@ __device__ __forceinline__ void f16_softmax_pv(floatx4 d0, floatx4 d1, const _Fl
       t[k] = (rel >= c.rel_lo && rel < c.rel_hi) ? t[k] : -INFINITY;
     }
   }
-  // ---- online softmax, reference raised lazily (weights stay <= 2^8: fp16-safe) ----
+  // ---- online softmax, reference raised lazily (weights stay <= 2^15: fp16-safe) ----
   float u = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
   u = rows_reduce<true>(u);
-  const bool bump = u > st.m + kLazy;
+  const bool bump = u > st.m + kWeightMaxLog2;
   if (__any(bump)) {
-    const float m_new = bump ? u : st.m;
+    const float m_new = bump ? u - kWeightRefLog2 : st.m;
     const float alpha = bump ? fast_exp2(st.m - m_new) : 1.f;
     st.l *= alpha;
     st.m = m_new;
@@ -251,7 +251,7 @@ __device__ __forceinline__ void f16_split(const F16DecodeArgs& a, F16Smem<G>& sm
     H8 hi, lo;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float x0 = xq[i] * inv, x1 = xq[i + 1] * inv;
+      const float x0 = (xq[i] * inv) * 128.0f, x1 = (xq[i + 1] * inv) * 128.0f;   // 2^7 q / max|q|
       const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x0) & 0xffffe000u);
       const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x1) & 0xffffe000u);
       hi.u[i >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(h0, h1));
@@ -275,7 +275,7 @@ __device__ __forceinline__ void f16_split(const F16DecodeArgs& a, F16Smem<G>& sm
 
   F16Consts<G> c;
   const int g = kSplitN ? (n & 7) : n;
-  c.fscale = a.qscale * (g < G ? qmax[g] : 0.f);
+  c.fscale = a.qscale * ((g < G ? qmax[g] : 0.f) * 0x1p-7f);
   c.qop = &qop[0][lane];
   c.qop_lo = &qop_lo[0][lane];
   c.lo_lane = kSplitN && n >= 8;

@@ -16,6 +16,8 @@ constexpr int kLutCopies = 16;
 // the 4-bit K table's (256 entries): one per lane of half a row, so that with
 // the staged blocks two work-groups still fit in a CU's LDS
 constexpr int kKLutCopies = 8;
+// bit pattern of 2^-80: the V norm floor of the softmax reference
+constexpr uint32_t kNormFloorBits = (127u - 80u) << 23;
 
 // Table entry of the code pair at bit BIT of w: {hi|lo of code a, hi|lo of code b}.
 template <int BIT, int N>
@@ -295,15 +297,24 @@ __device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& 
       nv[k] = valid ? nv[k] : 0.f;        // a slot outside the range may hold anything
     }
   }
-  const float nvmax = max_hw(max3_hw(nv[0], nv[1], nv[2]), max3_hw(max3_hw(nv[3], nv[4], nv[5]), nv[6], nv[7]));
   // ---- online softmax with a lazily raised reference ----
-  const float tmax = max_hw(max3_hw(t[0], t[1], t[2]), max3_hw(max3_hw(t[3], t[4], t[5]), t[6], t[7]));
-  const int ex = __builtin_amdgcn_frexp_expf(nvmax);
-  float u = tmax + (ex > 0 ? static_cast<float>(ex) : 0.f);
+  // The reference follows the largest log2 of a weight p nV = 2^(s - m) nV,
+  // i.e. of s + log2 nV, token by token, so that the fp16 halves of the
+  // weights keep their precision whatever the scale of the V norms. lg(x) =
+  // bits(x) / 2^23 - 127 is a lower bound of log2 x within 0.09 (the bit
+  // pattern read as a number); a norm below 2^-80 counts as 2^-80 here, which
+  // keeps 2^(s - m), and so the weights' sum, below 2^96. (Norms are >= 0.)
+  float u8[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t nb = max(__builtin_bit_cast(uint32_t, nv[k]), kNormFloorBits);
+    u8[k] = __builtin_fmaf(static_cast<float>(nb), 0x1p-23f, t[k]);   // s + lg(nV) + 127
+  }
+  float u = max_hw(max3_hw(u8[0], u8[1], u8[2]), max3_hw(max3_hw(u8[3], u8[4], u8[5]), u8[6], u8[7]));
   u = rows_reduce<true>(u);
-  const bool bump = u > st.m + kLazy;   // same for every lane of one head
+  const bool bump = u > st.m + (kWeightMaxLog2 + 127.0f);   // same for every lane of one head
   if (__any(bump)) {
-    const float m_new = bump ? u : st.m;
+    const float m_new = bump ? u - (kWeightRefLog2 + 127.0f) : st.m;
     const float alpha = bump ? fast_exp2(st.m - m_new) : 1.f;   // m = -inf gives 0
     st.l *= alpha;
     st.m = m_new;

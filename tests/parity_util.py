@@ -22,12 +22,14 @@ def _np(t):
     return t.cpu().numpy()
 
 
-def _assert_attention_close(got, ref, what=""):
+def _assert_attention_close(got, ref, what="", v_scale=1.0):
+    """max-abs <= 2e-3 and rel-L2 <= 1e-3. The max-abs bound is stated for V of unit scale; the
+    output is linear in V, so for V scaled by v_scale it is 2e-3 * v_scale (rel-L2 is scale-free)."""
     err = np.abs(got - ref)
     max_abs = float(err.max()) if err.size else 0.0
-    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
     print(f"[{what}] max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
-    assert max_abs <= 2e-3 and rel <= 1e-3, (what, max_abs, rel)
+    assert max_abs <= 2e-3 * v_scale and rel <= 1e-3, (what, max_abs, rel)
 
 
 def _boundary_mismatch_ok(codes_gpu, codes_ref, y_ref, n_ref, thresholds=None):
