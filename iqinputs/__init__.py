@@ -130,6 +130,26 @@ def kv(seed: int, layer: int, which: str, n_tokens: int, num_kv_heads: int,
     return _as_dtype(x, dtype)
 
 
+def kv_seq(seed: int, layer: int, which: str, seq: int, n_tokens: int, num_kv_heads: int,
+           outliers: str, dtype: str) -> np.ndarray:
+    """Synthetic K or V of one sequence of a ragged batch, [n_tokens][num_kv_heads][128], keyed by
+    (seed, tensor, layer, seq): any sequence can be drawn alone. Same value model as ``kv`` (the
+    Student-t channels of a KV head are the layer's, shared by all sequences)."""
+    tid = {"k": _T_K, "v": _T_V}[which]
+    g = rng(seed, tid, layer, 1 + seq)
+    x = g.standard_normal((n_tokens, num_kv_heads, HEAD_DIM))
+    if outliers == "fixed_x8":
+        x[:, :, list(FIXED_OUTLIER_CHANNELS)] *= FIXED_OUTLIER_SCALE
+    elif outliers == "student_t6":
+        gc = rng(seed, _T_CHAN, layer, tid)
+        for h in range(num_kv_heads):
+            ch = gc.choice(HEAD_DIM, N_STUDENT_T_CHANNELS, replace=False)
+            x[:, h, ch] = g.standard_t(3, size=(n_tokens, N_STUDENT_T_CHANNELS))
+    else:
+        raise ValueError(outliers)
+    return _as_dtype(x, dtype)
+
+
 def queries(seed: int, layer: int, n_seqs: int, num_q_heads: int) -> np.ndarray:
     """Decode queries, float32 [n_seqs][num_q_heads][128], i.i.d. N(0,1)."""
     return rng(seed, _T_Q, layer).standard_normal((n_seqs, num_q_heads, HEAD_DIM)).astype(np.float32)

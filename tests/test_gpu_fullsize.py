@@ -166,3 +166,74 @@ def test_ragged32_launch_configuration():
     got = np.concatenate([out[:, h * g:(h + 1) * g] for h in heads], axis=1)
     _assert_attention_close(got[seqs], ref[seqs], f"{w.name} seqs {seqs} heads {heads}")
     assert np.all(np.isfinite(out))
+
+
+def test_ragged32_batch_at_workload_lengths():
+    """The batched workload as bench.py launches it: 32 sequences with the workload's seeded
+    lengths (uniform in [1024, 32768]) back to back in one flat cache, Hq 32 / Hkv 8, max_seq_len =
+    the longest. Every sequence is encoded by the GPU's bulk append; the sampled ones (the shortest,
+    the longest, and those whose last split holds the fewest and the most 32-slot blocks) from their
+    seeded inputs, which the oracle encodes too, the others from device random numbers (their
+    outputs are not checked; they make the launch the real one). Codes of the sampled sequences and
+    the outputs of two KV heads' query heads against the oracle."""
+    w = iqinputs.WORKLOADS["ragged32_gqa"]
+    print(f"[{w.name}] workload lengths", flush=True)
+    lens = iqinputs.seq_lengths(w)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    total, hkv, hq, g = int(lens.sum()), w.num_kv_heads, w.num_q_heads, w.group
+    ml = int(lens.max())
+    # the plan of this batch: splits of 64 blocks (its cap), as many as the longest sequence needs
+    n_splits = iq.iq_decode_workspace_bytes(w.n_seqs, hq, hkv, ml) // (w.n_seqs * hq * 132 * 4) - 1
+    assert n_splits == -(-(-(-ml // 32)) // 64)
+    nblk = (starts % 32 + lens + 31) // 32
+    tail = nblk % 64
+    order = np.argsort(tail)
+    sampled = sorted({int(np.argmin(lens)), int(np.argmax(lens)), int(order[0]), int(order[1]), int(order[-1]),
+                      int(order[-2])})
+    assert len(sampled) >= 5
+    rot = iqinputs.rotation_params(w.seed, 0, hkv)
+    cache = iq.PackedKVCache.allocate(hkv, total, _t(rot))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    inputs = {}
+    for s in range(w.n_seqs):
+        n = int(lens[s])
+        if s in sampled:
+            k = iqinputs.kv_seq(w.seed, 0, "k", s, n, hkv, w.outliers, w.dtype)
+            v = iqinputs.kv_seq(w.seed, 0, "v", s, n, hkv, w.outliers, w.dtype)
+            inputs[s] = (k, v)
+            kt, vt = _t(k), _t(v)
+        else:
+            kt = torch.randn((n, hkv, 128), generator=gen, device="cuda").half()
+            vt = torch.randn((n, hkv, 128), generator=gen, device="cuda").half()
+        iq.iq_rotate_quantize_append(cache, kt, vt, first_slot=int(starts[s]))
+    q = iqinputs.queries(w.seed, 0, w.n_seqs, hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), ml))
+    assert np.all(np.isfinite(out))
+    heads = [1, 6]
+    kc, vc = _np(cache.k_codes)[heads], _np(cache.v_codes)[heads]
+    kn_gpu, vn_gpu = _np(cache.k_norms)[heads], _np(cache.v_norms)[heads]
+    nd = 0
+    for s in sampled:
+        a, n = int(starts[s]), int(lens[s])
+        k, v = inputs[s]
+        pad = -(-n // 8) * 8
+        kp = np.zeros((pad, hkv, 128), k.dtype)
+        vp = np.zeros_like(kp)
+        kp[:n], vp[:n] = k, v
+        rot_s, kr, kn, vt, vn = _oracle_heads(kp, vp, rot, heads)
+        # codes and norms the GPU wrote for this sequence
+        for x, ref_codes, ref_norms, got_codes, got_norms in (
+                (k, R.unpack(kr)[:, :n], kn[:, :n], R.unpack(kc[:, a:a + n]), kn_gpu[:, a:a + n]),
+                (v, R.unpack_tiles(vt)[:, :n], vn[:, :n],
+                 R.unpack_tiles(vc[:, a // 8:(a + n + 7) // 8])[:, a % 8:a % 8 + n], vn_gpu[:, a:a + n])):
+            y = np.stack([R.rotate(x[:, h].astype(np.float64), rot[h]).astype(np.float32) for h in heads])
+            nd += _boundary_mismatch_ok(got_codes, ref_codes, y, ref_norms)
+            assert np.max(np.abs(got_norms - ref_norms) / ref_norms) < 2e-6
+        q_s = np.concatenate([q[s:s + 1, h * g:(h + 1) * g] for h in heads], axis=1)
+        ref = R.decode_attention(q_s, kr, kn, vt, vn, rot_s, np.zeros(1, np.int32), np.full(1, n, np.int32), SCALE,
+                                 C32)
+        got = np.concatenate([out[s:s + 1, h * g:(h + 1) * g] for h in heads], axis=1)
+        _assert_attention_close(got, ref, f"{w.name} seq {s} (len {n}, start {a}, {int(nblk[s])} blocks) "
+                                          f"heads {heads}")
+    print(f"[{w.name}] sampled {sampled}, {nd} boundary codes", flush=True)
