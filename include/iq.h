@@ -17,8 +17,11 @@
  * Conventions shared by every entry point:
  *   - d = head_dim = 128 only (anything else: IQ_ERR_UNSUPPORTED).
  *   - Pointers marked "device" are device memory owned by the caller; the
- *     library never allocates, frees or retains them, and keeps no state
- *     besides a lazily computed host copy of the codebook.
+ *     library never allocates, frees or retains them. Its only state: a
+ *     lazily computed host copy of the codebook, the number of decode-step
+ *     work-groups each device holds at once (asked once per device and
+ *     kept), and the scratch array of iq_append_decode_attention_noalloc in
+ *     each GPU's memory (with its device address, asked once per device).
  *   - All GPU work is enqueued asynchronously on `stream` (a hipStream_t;
  *     NULL = the legacy default stream). A return of IQ_OK means the work was
  *     launched, not that it has finished.
@@ -226,6 +229,28 @@ IQ_API iq_status iq_append_decode_attention(const iq_cache_view* view, const voi
                                      const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
                                      int32_t max_seq_len, float scale, float* out, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* Size of the library's scratch array on each GPU, the most that
+ * iq_append_decode_attention_noalloc can use (16 MiB). */
+#define IQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * iq_append_decode_attention without a workspace argument. The split-K
+ * records go to a scratch array of IQ_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory, one per GPU, from the library's loading until the
+ * process ends; the call allocates nothing. Arguments and results are those
+ * of iq_append_decode_attention (same kernels, same plan, same outputs).
+ *   Errors: IQ_ERR_WORKSPACE when iq_decode_workspace_bytes() for these
+ *   sizes exceeds IQ_NOALLOC_SCRATCH_BYTES (nothing is launched); IQ_ERR_HIP
+ *   when the scratch array's address on the stream's GPU cannot be obtained.
+ *   The array keeps the last call's contents; no call depends on them.
+ *   Calls that overlap on one GPU (other streams, other host threads) share
+ *   the array and race: they must be serialised by the caller. */
+IQ_API iq_status iq_append_decode_attention_noalloc(const iq_cache_view* view, const void* k_new, const void* v_new,
+                                             iq_dtype in_dtype, const float* q, int32_t num_q_heads,
+                                             const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                                             int32_t max_seq_len, float scale, float* out, void* stream);
 
 /* Bytes of workspace iq_decode_attention_deferred needs (0 if invalid). */
 IQ_API size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -100,6 +100,11 @@ _SIGNATURES = {
                                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                                   ctypes.c_void_p]),
+    "iq_append_decode_attention_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_int32,
+                                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                                          ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                                          ctypes.c_void_p]),
     "iq_decode_attention_f16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -414,4 +419,29 @@ def iq_append_decode_attention(cache: PackedKVCache, k_new: torch.Tensor, v_new:
                                             _dev(out, torch.float32, "out"),
                                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                             _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # IQ_NOALLOC_SCRATCH_BYTES
+
+
+def iq_append_decode_attention_noalloc(cache: PackedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                                       q: torch.Tensor, seq_start: torch.Tensor, seq_len: torch.Tensor,
+                                       max_seq_len: int, out: torch.Tensor, scale: float | None = None,
+                                       stream=None) -> torch.Tensor:
+    """iq_append_decode_attention with the library's own scratch array in place of a workspace:
+    allocates nothing (``out`` is the caller's). Calls overlapping on one GPU must be serialised."""
+    n_seqs, hq, _ = q.shape
+    dt = _in_dtype(k_new)
+    if v_new.dtype != k_new.dtype or v_new.shape != k_new.shape or k_new.shape[0] != n_seqs:
+        raise ValueError("k_new and v_new must be matching [n_seqs][Hkv][128] tensors")
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    view = cache.view()
+    _check("iq_append_decode_attention_noalloc",
+           lib().iq_append_decode_attention_noalloc(ctypes.byref(view), _dev(k_new, k_new.dtype, "k_new"),
+                                                    _dev(v_new, v_new.dtype, "v_new"), dt,
+                                                    _dev(q, torch.float32, "q"), hq,
+                                                    _dev(seq_start, torch.int32, "seq_start"),
+                                                    _dev(seq_len, torch.int32, "seq_len"), n_seqs, max_seq_len, scale,
+                                                    _dev(out, torch.float32, "out"), _stream(stream)))
     return out

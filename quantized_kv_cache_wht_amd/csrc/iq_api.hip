@@ -128,6 +128,32 @@ static hipError_t stream_device(hipStream_t s, int* dev) {
   return e;
 }
 
+// Scratch of iq_append_decode_attention_noalloc: the split-K records, in a
+// file-scope device array of IQ_NOALLOC_SCRATCH_BYTES. Every GPU the library
+// runs on holds its own copy, at its own address, until the process ends; in
+// host code `scratch` names a host-side stand-in, so kernels and copies take
+// the address that hipGetSymbolAddress returns with that GPU current, asked
+// once per device and kept here.
+static __device__ __align__(256) float scratch[IQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+static void* scratch_address(int dev) {
+  constexpr int kDevices = 64;
+  static void* addr[kDevices] = {};
+  static std::mutex mu;
+  if (dev < 0 || dev >= kDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] != nullptr) return addr[dev];
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return nullptr;
+  addr[dev] = p;
+  return p;
+}
+
 }  // namespace iq
 
 using namespace iq;
@@ -307,12 +333,13 @@ iq_status iq_decode_attention_f16(const void* k, const void* v, int64_t token_st
   return hip_status(launch_decode_f16(a, static_cast<hipStream_t>(stream)));
 }
 
-// The fused decode step into a workspace of `workspace_bytes` bytes. All
-// host-side checks come first.
+// The fused decode step into a workspace of `workspace_bytes` bytes: the
+// caller's, or (use_scratch) the library's scratch array of this GPU, whose
+// address is asked for only after every host-side check has passed.
 static iq_status append_decode(const iq_cache_view* view, const void* k_new, const void* v_new, iq_dtype in_dtype,
                                const float* q, int32_t num_q_heads, const int32_t* seq_start, const int32_t* seq_len,
                                int32_t n_seqs, int32_t max_seq_len, float scale, float* out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, bool use_scratch, void* stream) {
   iq_status st = check_view(view);
   if (st != IQ_OK) return st;
   if (in_dtype != IQ_F32 && in_dtype != IQ_F16) return IQ_ERR_INVALID_ARG;
@@ -321,7 +348,7 @@ static iq_status append_decode(const iq_cache_view* view, const void* k_new, con
   const int32_t group = num_q_heads / view->num_kv_heads;
   if (!group_supported(group)) return IQ_ERR_UNSUPPORTED;
   if (n_seqs == 0) return IQ_OK;
-  if (!k_new || !v_new || !q || !seq_start || !seq_len || !out || !workspace)
+  if (!k_new || !v_new || !q || !seq_start || !seq_len || !out || (!use_scratch && !workspace))
     return IQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
        reinterpret_cast<uintptr_t>(workspace)) & 15u)
@@ -332,6 +359,7 @@ static iq_status append_decode(const iq_cache_view* view, const void* k_new, con
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   int dev = 0;
   if (stream_device(hs, &dev) != hipSuccess) return IQ_ERR_HIP;
+  if (use_scratch && (workspace = scratch_address(dev)) == nullptr) return IQ_ERR_HIP;
   // The new token's work-groups join the split launch: if they and the plain
   // plan's splits do not all fit on the GPU at once, the plan leaves them room
   // (a second round of work-groups would cost a whole split's time).
@@ -384,7 +412,15 @@ iq_status iq_append_decode_attention(const iq_cache_view* view, const void* k_ne
                                      const int32_t* seq_len, int32_t n_seqs, int32_t max_seq_len, float scale,
                                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
   return append_decode(view, k_new, v_new, in_dtype, q, num_q_heads, seq_start, seq_len, n_seqs, max_seq_len, scale,
-                       out, workspace, workspace_bytes, stream);
+                       out, workspace, workspace_bytes, false, stream);
+}
+
+iq_status iq_append_decode_attention_noalloc(const iq_cache_view* view, const void* k_new, const void* v_new,
+                                             iq_dtype in_dtype, const float* q, int32_t num_q_heads,
+                                             const int32_t* seq_start, const int32_t* seq_len, int32_t n_seqs,
+                                             int32_t max_seq_len, float scale, float* out, void* stream) {
+  return append_decode(view, k_new, v_new, in_dtype, q, num_q_heads, seq_start, seq_len, n_seqs, max_seq_len, scale,
+                       out, nullptr, IQ_NOALLOC_SCRATCH_BYTES, true, stream);
 }
 
 size_t iq_decode_deferred_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     h = ctypes.CDLL(iq.library_path())
     for n in names:
         assert hasattr(h, n), n
@@ -132,6 +132,33 @@ def test_append_decode_validation():
     assert call(kn=None) == -1
     assert call(kn=ctypes.c_void_p(0x70004)) == -1
     assert call(n=0) == 0
+
+
+def test_append_decode_noalloc_validation():
+    """The no-allocation step checks the records' size against the scratch array on the host: a call
+    whose records would not fit is refused before anything reaches a GPU."""
+    L = iq.lib()
+    v = _view(hkv=4)
+    p = ctypes.c_void_p(0x90000)
+
+    def call(hq=32, n=1, ml=100, kn=p):
+        return L.iq_append_decode_attention_noalloc(ctypes.byref(v), kn, p, 1, p, hq, p, p, n, ml, 0.1, p, None)
+    big = L.iq_decode_workspace_bytes(64, 32, 4, 32768)
+    assert big > iq.NOALLOC_SCRATCH_BYTES
+    assert call(n=64, ml=32768) == -4
+    assert L.iq_decode_workspace_bytes(1, 32, 4, 32768) <= iq.NOALLOC_SCRATCH_BYTES
+    assert L.iq_decode_workspace_bytes(32, 32, 8, 32768) <= iq.NOALLOC_SCRATCH_BYTES   # the ragged batch's
+    assert call(hq=12) == -2        # group 3
+    assert call(hq=6) == -1         # Hq % Hkv
+    assert call(kn=None) == -1
+    assert call(n=-1) == -1
+    assert call(n=0) == 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "iq.h")).read()
+    m = re.search(r"#define IQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == iq.NOALLOC_SCRATCH_BYTES
 
 
 def test_decode_deferred_validation():
