@@ -19,7 +19,10 @@ constexpr int kKLutCopies = 8;
 // bit pattern of 2^-80: the V norm floor of the softmax reference
 constexpr uint32_t kNormFloorBits = (127u - 80u) << 23;
 
-// Table entry of the code pair at bit BIT of w: {hi|lo of code a, hi|lo of code b}.
+// Table entry of the code pair (a, b) at bit BIT of w: {hi(a) | hi(b) << 16,
+// lo(a) | lo(b) << 16}, the fp16 halves of alpha c. The score operand takes
+// the whole entry (against a query operand laid out (x_a, x_b, x_a, x_b)); the
+// PV operand only its first dword, the hi halves (pair_hi).
 template <int BIT, int N>
 __device__ __forceinline__ uint2 pair_entry(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
   constexpr int word = BIT >> 5, off = BIT & 31;
@@ -58,12 +61,41 @@ __device__ __forceinline__ half8 code_operand4(const uint32_t (&w)[N], const cha
   return r.h;
 }
 
-// Code operand for the 4 codes at bits BIT .. BIT+11 of w (two pairs).
+// Score operand for the 4 codes at bits BIT .. BIT+11 of w (two pairs):
+// (hi a, hi b, lo a, lo b, hi c, hi d, lo c, lo d).
 template <int BIT, int N>
 __device__ __forceinline__ half8 code_operand(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
   H8 r;
   r.u2[0] = pair_entry<BIT>(w, lut, lane_off);
   r.u2[1] = pair_entry<BIT + 6>(w, lut, lane_off);
+  return r.h;
+}
+
+// The hi halves of the table entry of the code pair at bit BIT of w (its first dword).
+template <int BIT, int N>
+__device__ __forceinline__ uint32_t pair_hi(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
+  constexpr int word = BIT >> 5, off = BIT & 31;
+  const uint32_t src = (off <= 26) ? w[word] : __builtin_amdgcn_alignbit(w[word + 1], w[word], off);
+  constexpr int field = (off <= 26) ? off : 0;
+  constexpr int shift = kLutCopies == 16 ? 7 : 8;
+  uint32_t addr;
+  asm("v_bfe_u32 %0, %1, %2, 6\n\tv_lshl_add_u32 %0, %0, %4, %3"
+      : "=&v"(addr)
+      : "v"(src), "i"(field), "v"(lane_off), "i"(shift));
+  return *reinterpret_cast<const uint32_t*>(lut + addr);
+}
+
+// PV operand: hi(alpha c) of the 8 codes at bits BIT .. BIT+23 of w (the 8
+// tokens of one dim of a V tile), two per table read. The hi half alone is
+// within 2e-5 of alpha c (alpha is chosen for that), and an error of the V
+// centroids enters the output linearly, never through the softmax.
+template <int BIT, int N>
+__device__ __forceinline__ half8 code_operand_hi(const uint32_t (&w)[N], const char* lut, uint32_t lane_off) {
+  H8 r;
+  r.u[0] = pair_hi<BIT>(w, lut, lane_off);
+  r.u[1] = pair_hi<BIT + 6>(w, lut, lane_off);
+  r.u[2] = pair_hi<BIT + 12>(w, lut, lane_off);
+  r.u[3] = pair_hi<BIT + 18>(w, lut, lane_off);
   return r.h;
 }
 
@@ -219,7 +251,7 @@ struct Consts {
   uint4 q[8];            // this lane's query operand of k-step kk (registers: read every block)
   const uint4* qop_lo;   // G = 16: the lo halves, at qop_lo[64 kk] (LDS)
   float fscale;
-  bool lo_lane;
+  uint32_t lo_mask;     // G <= 8: 0xffffe000 where the lane's P row carries the lo halves, else 0
   uint32_t lane_off;    // this lane's copy of the 3-bit table: (lane % kLutCopies) * 8
   uint32_t klane_off;   // and of the 4-bit K table: (lane % kKLutCopies) * 8
   int rel_lo, rel_hi;
@@ -233,7 +265,8 @@ struct Consts {
 //   block_scores:  D_T[i] = row 4q + i of tile T = token 8q + 4T + i, column n
 //   block_softmax: the scores in log2 units, the running reference, the
 //                  weights p = 2^(s - m) nV as fp16 operands
-//   block_pv:      acc[D] += P x (V centroids of dims 8n + D)
+//   block_pv:      acc[D] += P x (V centroids of dims 8n + D), all 32 tokens
+//                  in one MFMA (K = the tokens: lane group q holds 8q .. 8q+7)
 template <int G, int KB>
 __device__ __forceinline__ void block_scores(const BlockData<KB>& cur, const Consts<G>& c, floatx4& d0,
                                              floatx4& d1) {
@@ -260,10 +293,11 @@ __device__ __forceinline__ void block_scores(const BlockData<KB>& cur, const Con
 #undef IQ_SCORE
 }
 
-// P operands of one block: rows 2i, 2i + 1 of token group T hold token i's
-// weight (hi for G <= 8 in rows g, lo in rows g + 8; G = 16: hi in pa, lo in pa_lo)
+// P operand of one block: lane (n, q) holds row n, tokens 8q .. 8q+7 (G <= 8:
+// rows g the hi halves of head g's weights, rows g + 8 the lo halves; G = 16:
+// hi halves in pa, lo halves in pa_lo, row = head)
 struct BlockWeights {
-  H8 pa[2], pa_lo[2];
+  H8 pa, pa_lo;
 };
 
 // kFull: every slot of the block lies in the sequence (the caller's
@@ -328,40 +362,42 @@ __device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& 
     }
   }
   const float mref = (st.m == -INFINITY) ? 0.f : st.m;
-  // weights: token group T = tokens 8q + 4T + i; A slots (2i, 2i+1) both hold token i's weight
-  float esum = 0.f;
+  // weights of tokens 8q + k. The hi half of p is p rounded toward zero to
+  // fp16 (its 11 leading bits: what the conversion below does with p itself),
+  // the lo half p minus those bits. A lane of a lo row subtracts them (its
+  // mask keeps them), a lane of a hi row subtracts 0 and converts p.
+  float esum = 0.f, x[8], xl[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const float e = fast_exp2(t[k] - mref);
     esum += e;
     const float p = e * nv[k];
-    // hi = p truncated to 11 significant bits (exact in fp16), lo = the rest
-    const float hp = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) & 0xffffe000u);
+    const uint32_t pb = __builtin_bit_cast(uint32_t, p);
     if (kSplitN) {
-      w.pa[k >> 2].u[k & 3] = dup16(c.lo_lane ? p - hp : hp);
+      x[k] = p - __builtin_bit_cast(float, pb & c.lo_mask);
     } else {
-      w.pa[k >> 2].u[k & 3] = dup16(hp);
-      w.pa_lo[k >> 2].u[k & 3] = dup16(p - hp);
+      x[k] = p;
+      xl[k] = p - __builtin_bit_cast(float, pb & 0xffffe000u);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w.pa.u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]));
+    if (!kSplitN) w.pa_lo.u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xl[2 * i], xl[2 * i + 1]));
   }
   st.l += esum;
 }
 
-// PV: B = centroids of dim 8n + D for the 4 tokens 4T..4T+3 of V tile q
+// PV: B = hi(alpha c) of dim 8n + D for the tokens 8q .. 8q+7 (V tile q)
 template <int G>
 __device__ __forceinline__ void block_pv(const uint32_t (&vw)[6], const BlockWeights& w, const Consts<G>& c,
                                          WaveState& st) {
   constexpr bool kSplitN = (G <= 8);
 #define IQ_PV(D)                                                                     \
   {                                                                                  \
-    const half8 v0 = code_operand<24 * D>(vw, c.lut, c.lane_off);                    \
-    const half8 v1 = code_operand<24 * D + 12>(vw, c.lut, c.lane_off);               \
-    st.acc[D] = mfma16(w.pa[0].h, v0, st.acc[D]);                                    \
-    st.acc[D] = mfma16(w.pa[1].h, v1, st.acc[D]);                                    \
-    if (!kSplitN) {                                                                  \
-      st.acc[D] = mfma16(w.pa_lo[0].h, v0, st.acc[D]);                               \
-      st.acc[D] = mfma16(w.pa_lo[1].h, v1, st.acc[D]);                               \
-    }                                                                                \
+    const half8 v = code_operand_hi<24 * D>(vw, c.lut, c.lane_off);                  \
+    st.acc[D] = mfma16(w.pa.h, v, st.acc[D]);                                        \
+    if (!kSplitN) st.acc[D] = mfma16(w.pa_lo.h, v, st.acc[D]);                       \
   }
   IQ_PV(0) IQ_PV(1) IQ_PV(2) IQ_PV(3) IQ_PV(4) IQ_PV(5) IQ_PV(6) IQ_PV(7)
 #undef IQ_PV
