@@ -20,9 +20,11 @@ counter summary when it matches the decode sources; valu_roof = the same
 launch pair's VALU instructions (same summary) against the chip's VALU issue
 rate; comparisons = decode
 alone, append + decode as two calls, the FP16-KV and unfused paths, the
-rotation variants and 4-bit K; cpu_baseline = the CPU oracle's decode on a
-bounded sample of the same workload. The quantize-append rate is measured on
-the set-up's bulk encode.
+rotation variants and 4-bit K; cpu_baseline = the plain C oracle's decode (and
+encode) on a bounded sample of the same workload, on the host's cores;
+append_roofline = the long-context bulk encode (131072 tokens x 8 KV heads)
+against the VALU issue roof and the HBM roof, with the one-token append's
+latency.
 """
 from __future__ import annotations
 
@@ -57,24 +59,47 @@ def parse():
     p.add_argument("--no-compare", action="store_true", help="skip the FP16-KV and unfused comparison timings")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="finish with 3 device-to-device copies of this many MiB (reference for HBM counters)")
+    p.add_argument("--profile-append", action="store_true",
+                   help="only the bulk encode of the append roofline (and the calibration copies), for counter runs")
     return p.parse_args()
 
 
-def decode_source_digest() -> str:
-    """sha256 over the sources of the decode kernels (the traffic figures belong to one version)."""
+def calibration_copies(torch, mib: int):
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+DECODE_SOURCES = ("iq_decode.hip", "iq_decode_common.h", "iq_decode_packed.h", "iq_decode_packed_body.inc",
+                  "iq_decode_new_token.h", "iq_device.h", "iq_launch.h")
+ENCODE_SOURCES = ("iq_encode.hip", "iq_device.h", "iq_launch.h")
+
+
+def source_digest(names=DECODE_SOURCES) -> str:
+    """sha256 over the given kernel sources (counter figures belong to one version of them)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_wht_amd", "csrc")
-    for name in ("iq_decode.hip", "iq_decode_common.h", "iq_decode_packed.h", "iq_decode_packed_body.inc",
-                 "iq_decode_new_token.h", "iq_device.h", "iq_launch.h"):
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_counters(workload: str) -> dict:
-    """The per-launch counter figures of the committed summary (HBM bytes, VALU and
-    MFMA instructions), if it was taken on the current decode sources; else {}."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
+def decode_source_digest() -> str:
+    return source_digest(DECODE_SOURCES)
+
+
+def encode_source_digest() -> str:
+    return source_digest(ENCODE_SOURCES)
+
+
+def read_counters(path: str, digest: str) -> dict:
+    """The per-launch counter figures of a committed summary (HBM bytes, VALU and MFMA
+    instructions), if it was taken on the sources with this digest; else {}."""
     if not os.path.exists(path):
         return {}
     fields = {}
@@ -83,7 +108,7 @@ def measured_counters(workload: str) -> dict:
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
                 fields[k.strip("`")] = v.strip().strip("`")
-    if fields.get("decode_source_sha256") != decode_source_digest():
+    if fields.get("source_sha256", fields.get("decode_source_sha256")) != digest:
         return {}
     out = {}
     for k in ("hbm_bytes_per_launch", "valu_insts_per_launch", "mfma_insts_per_launch"):
@@ -94,9 +119,23 @@ def measured_counters(workload: str) -> dict:
     return out
 
 
+def measured_counters(workload: str) -> dict:
+    """Counter figures of the decode step's launch pair (profiles/decode_<workload>_traffic.md)."""
+    return read_counters(os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md"), decode_source_digest())
+
+
 def measured_traffic(workload: str):
     """HBM bytes per decode launch from the committed counter summary, or None."""
     return measured_counters(workload).get("hbm_bytes_per_launch")
+
+
+APPEND_WORKLOAD = "long_t131072"
+
+
+def append_counters() -> dict:
+    """Counter figures of the bulk encode (profiles/append_<workload>_traffic.md)."""
+    return read_counters(os.path.join(ROOT, "profiles", f"append_{APPEND_WORKLOAD}_traffic.md"),
+                         encode_source_digest())
 
 
 def time_per_call(torch, fn, n_calls, stream):
@@ -220,6 +259,53 @@ def k4_decode(iq, qs, seq_start, seq_len, ws, outs, stream, synth_kv, T, hkv, n_
             "bytes_per_launch": hkv * T * (64 + 4 + 48 + 4)}
 
 
+def append_bulk(iq, stream, reps=6):
+    """The long-context workload's bulk encode (prefill-style compression): 131072 fp16 tokens of
+    K and V, 8 KV heads, into three layers' caches in turn (inputs and caches exceed the last-level
+    cache). One iq_rotate_quantize_append call is one launch of the bulk kernel (grid z: K and V).
+    Returns (us per call, tokens, KV heads)."""
+    import torch
+    import iqinputs
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260819)
+    w = iqinputs.WORKLOADS[APPEND_WORKLOAD]
+    T, hkv = w.seq_len, w.num_kv_heads
+    k = torch.randn((T, hkv, 128), generator=gen, device=dev).half()
+    v = torch.randn((T, hkv, 128), generator=gen, device=dev).half()
+    rot = torch.from_numpy(iqinputs.rotation_params(12, 0, hkv)).to(dev)
+    cs = [iq.PackedKVCache.allocate(hkv, T, rot, device=dev) for _ in range(3)]
+    us = time_per_call(torch, lambda i: iq.iq_rotate_quantize_append(cs[i % 3], k, v, first_slot=0, stream=stream),
+                       reps, stream)
+    del k, v, cs
+    torch.cuda.empty_cache()
+    return us, T, hkv
+
+
+def append_roofline(us: float, T: int, hkv: int, one_token_us: float | None) -> dict:
+    """The bulk encode against the VALU issue roof (its bound: the counters read its loop at the
+    issue rate) and the HBM roof. Algorithmic bytes per vector (token, KV head, K or V): 256 B of
+    fp16 in, 48 B of codes and a 4 B norm out."""
+    nbytes = T * hkv * 2 * (256 + ROW_BYTES)
+    gbps = nbytes / us / 1e3
+    c = append_counters()
+    valu = c.get("valu_insts_per_launch")
+    traffic = c.get("hbm_bytes_per_launch")
+    hbm = {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+           "traffic": None if traffic is None else round(traffic), "algorithmic_bytes": nbytes}
+    r = {"kernel": "append_kernel<_Float16, false>",
+         "launch": f"{T} tokens x {hkv} KV heads, K and V (fp16 in)",
+         "launch_us": round(us, 2), "token_layers_per_s": round(T / (us * 1e-6)),
+         "one_token_append_us": None if one_token_us is None else round(one_token_us, 3)}
+    if valu is not None:
+        gi = valu / (us * 1e-6) / 1e9
+        r.update({"bound": "alu", "achieved": round(gi, 2), "peak": VALU_PEAK_GINST, "unit": "Ginst/s",
+                  "frac": round(gi / VALU_PEAK_GINST, 4), "valu_insts_per_launch": round(valu), "hbm": hbm})
+    else:
+        r.update({"bound": "hbm", **{k: hbm[k] for k in ("achieved", "peak", "unit", "frac", "traffic")}})
+    return r
+
+
 def other_workloads(iq, stream):
     """The other measured configurations, timed like the main one (HIP events around back-to-back
     calls). Their caches hold random codes and norms (the decode's work does not depend on the
@@ -282,16 +368,10 @@ def other_workloads(iq, stream):
                    "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     del c, wsb
 
-    # long context: bulk encode of 131072 tokens (prefill-style), then decode over three layers' caches
+    # long context: decode over three layers' caches of 131072 tokens
     w = iqinputs.WORKLOADS["long_t131072"]
     T, hkv, hq = w.seq_len, w.num_kv_heads, w.num_q_heads
-    k = torch.randn((T, hkv, 128), generator=gen, device=dev).half()
-    v = torch.randn((T, hkv, 128), generator=gen, device=dev).half()
-    rot = torch.from_numpy(iqinputs.rotation_params(12, 0, hkv)).to(dev)
-    cs = [iq.PackedKVCache.allocate(hkv, T, rot, device=dev) for _ in range(3)]
-    us_enc = time_per_call(torch, lambda i: iq.iq_rotate_quantize_append(cs[i % 3], k, v, first_slot=0,
-                                                                         stream=stream), 6, stream)
-    del k, v
+    cs = [timing_cache(hkv, T) for _ in range(3)]
     ql = torch.randn((1, hq, 128), generator=gen, device=dev)
     stl = torch.zeros(1, dtype=torch.int32, device=dev)
     lnl = torch.full((1,), T, dtype=torch.int32, device=dev)
@@ -299,11 +379,10 @@ def other_workloads(iq, stream):
     outl = torch.empty_like(ql)
     us_dec = time_per_call(torch, lambda i: iq.iq_decode_attention(cs[i % 3], ql, stl, lnl, T, out=outl,
                                                                    workspace=wsl, stream=stream), 12, stream)
-    enc_bytes = T * hkv * 2 * (256 + ROW_BYTES)
     dec_bytes = hkv * T * 2 * ROW_BYTES
-    res[w.name] = {"bulk_encode_us": round(us_enc, 1), "bulk_encode_token_layers_per_s": round(T / (us_enc * 1e-6)),
-                   "bulk_encode_GBps": round(enc_bytes / us_enc / 1e3, 1), "decode_us": round(us_dec, 2),
-                   "decode_GBps": round(dec_bytes / us_dec / 1e3, 1)}
+    res[w.name] = {"decode_us": round(us_dec, 2), "decode_GBps": round(dec_bytes / us_dec / 1e3, 1),
+                   "frac_hbm_peak": round(dec_bytes / us_dec / 1e3 / HBM_PEAK_GBS, 4),
+                   "note": "the bulk encode of this workload is append_roofline"}
     del cs
 
     # streaming peak on this GPU: device-to-device copy of 1 GiB (read + write bytes)
@@ -379,6 +458,12 @@ def main():
     w = iqinputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_append:
+        us, T_a, hkv_a = append_bulk(iq, torch.cuda.current_stream())
+        if args.copy_calibration_mib > 0:
+            calibration_copies(torch, args.copy_calibration_mib)
+        print(json.dumps({"profile_append_us": round(us, 2), "tokens": T_a, "num_kv_heads": hkv_a}), flush=True)
+        return
     T, L, hq, hkv = w.seq_len, w.n_layers, w.num_q_heads, w.num_kv_heads
     fdt = torch.float16 if w.dtype == "f16" else torch.float32
     stream = torch.cuda.current_stream()
@@ -492,14 +577,15 @@ def main():
                                                      T, hkv, float(dec_us.mean()), new_k, new_v)
     others = None if args.no_compare else other_workloads(iq, stream)
 
+    # quantize-append: the one-token append of the step's shape (latency) over the step's caches, and
+    # the long-context bulk encode against its roofs
+    one_tok_us = time_per_call(torch, lambda i: iq.iq_rotate_quantize_append(
+        caches[i % L], new_k[i % L], new_v[i % L], first_slot=T - 1, stream=stream), 2 * L, stream)
+    app_us, app_T, app_hkv = append_bulk(iq, stream)
+    app_roof = append_roofline(app_us, app_T, app_hkv, one_tok_us)
+
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copies(torch, args.copy_calibration_mib)
 
     res = {
         "metric": "packed-KV decode attention GB/s & % HBM peak; quantize-append tokens/s",
@@ -512,7 +598,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the contractions run on fp16 MFMA with fp32 accumulation; scores and queries in hi/lo fp16
+        # pairs (fp32-level products), V centroids as fp16 hi halves (within 2e-5); softmax in fp32
+        "dtype": "f16 hi/lo MFMA, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "context": T, "layers": L, "num_q_heads": hq, "num_kv_heads": hkv,
                    "head_dim": 128, "batch": 1, "kv_input": w.dtype,
@@ -522,8 +610,12 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_launch_us": {"mean": round(float(dec_us.mean()), 3), "median": round(float(np.median(dec_us)), 3),
                              "min": round(float(dec_us.min()), 3)},
-        "quantize_append_token_layers_per_s": round(append_tok_layers_per_s, 1),
-        "quantize_append_bulk_ms": round(enc_ms, 4),
+        "quantize_append_token_layers_per_s": app_roof["token_layers_per_s"],
+        "quantize_append": {"bulk_131072x8_token_layers_per_s": app_roof["token_layers_per_s"],
+                            "setup_bulk_32767x4_token_layers_per_s": round(append_tok_layers_per_s, 1),
+                            "setup_bulk_32767x4_ms": round(enc_ms, 4),
+                            "one_token_append_us": app_roof["one_token_append_us"]},
+        "append_roofline": app_roof,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},

@@ -1,18 +1,22 @@
-"""Per-launch HBM traffic of the decode from two rocprofv3 counter runs of bench.py.
+"""Per-launch HBM traffic (and instructions) of a measured kernel from rocprofv3 counter runs of bench.py.
 
-Reads the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run (both of
-`bench.py --eager --no-compare --copy-calibration-mib N`), takes the decode
-step's two kernels (the split kernel instantiated for the workload's group
-size with the new token's work-groups, and the merge), scales each counter by what it
-reads for the run's own device-to-device copies of N MiB (their true traffic
-is N MiB read and N MiB written), and writes the summary that bench.py reports
-as roofline.traffic when the decode sources still match. With --insts, a third
-run's instruction counters (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_INSTS_LDS,
-SQ_INSTS_SALU, SQ_WAVES: wave-level instructions summed over the chip) go into
-the same summary; bench.py reports the VALU count against the VALU issue roof.
+Reads the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of bench.py
+(with --copy-calibration-mib N), takes the kernels of one measured launch,
+scales each counter by what it reads for the run's own device-to-device copies
+of N MiB (their true traffic is N MiB read and N MiB written), and writes the
+summary that bench.py reports when the kernel sources still match:
+  --kind decode  the decode step's two kernels (the split kernel for the
+                 workload's group size with the new token's work-groups, and
+                 the merge); bench.py's roofline.traffic and valu_roof;
+  --kind append  the bulk encode of the long-context workload
+                 (bench.py --profile-append); bench.py's append_roofline.
+With --insts, a third run's instruction counters (SQ_INSTS_VALU, SQ_INSTS_MFMA,
+SQ_INSTS_LDS, SQ_INSTS_SALU, SQ_WAVES: wave-level instructions summed over the
+chip) go into the same summary; bench.py reports the VALU count against the
+VALU issue roof.
 
-    python bench_traffic.py --fetch DIR --write DIR --copy-mib N --workload W \\
-        [--insts DIR] --command "..." --out profiles/decode_W_traffic.md
+    python bench_traffic.py --kind decode|append --fetch DIR --write DIR --copy-mib N --workload W \\
+        [--insts DIR] --command "..." --out profiles/<kind>_W_traffic.md
 """
 from __future__ import annotations
 
@@ -41,9 +45,12 @@ def per_kernel(run_dir: str, counter: str):
 
 
 def pick(vals, needle):
-    hits = [v for k, vs in vals.items() if needle in k for v in vs]
+    """Counter values of the dispatches of one kernel: `needle` is (demangled, mangled) names or a
+    single name (the profiler writes either form, depending on its version and options)."""
+    names = needle if isinstance(needle, tuple) else (needle,)
+    hits = [v for k, vs in vals.items() if any(n in k for n in names) for v in vs]
     if not hits:
-        raise SystemExit(f"no dispatch of a kernel named like {needle!r}")
+        raise SystemExit(f"no dispatch of a kernel named like {names!r}")
     return hits
 
 
@@ -53,12 +60,13 @@ def main():
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--workload", required=True)
+    ap.add_argument("--kind", choices=("decode", "append"), default="decode")
     ap.add_argument("--insts", default=None, help="run dir of the instruction-counter pass")
     ap.add_argument("--command", required=True, help="the two profiling commands, for the record")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
 
-    from bench import decode_source_digest, ROW_BYTES
+    from bench import decode_source_digest, encode_source_digest, ROW_BYTES
     import iqinputs
 
     fetch, write = per_kernel(a.fetch, "FETCH_SIZE"), per_kernel(a.write, "WRITE_SIZE")
@@ -70,23 +78,32 @@ def main():
     w_scale = copy_kib / statistics.mean(w_copy)
     w = iqinputs.WORKLOADS[a.workload]
     group = w.num_q_heads // w.num_kv_heads
+    if a.kind == "decode":
+        kernels = (("split", (f"decode_split_kernel<{group}, 3, true>", f"decode_split_kernelILi{group}ELi3ELb1E")),
+                   ("merge", ("decode_merge_kernel<true, 32>", "decode_merge_kernelILb1ELi32E")))
+        alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
+        alg_text = "packed K and V rows, 104 B per token and KV head"
+        digest = decode_source_digest()
+    else:
+        kernels = (("append", ("append_kernel<_Float16, false>", "append_kernelIDF16_Lb0E")),)
+        alg = w.num_kv_heads * w.seq_len * 2 * (256 + ROW_BYTES)
+        alg_text = "per token, KV head and K or V: 256 B of fp16 in, 48 B of codes and a 4 B norm out"
+        digest = encode_source_digest()
     rows = []
     total = 0.0
-    for label, needle in (("split", f"decode_split_kernel<{group}, 3, true>"), ("merge", "decode_merge_kernel<true>")):
+    for label, needle in kernels:
         f = statistics.mean(pick(fetch, needle)) * f_scale * 1024
         wv = statistics.mean(pick(write, needle)) * w_scale * 1024
         rows.append((label, f, wv))
         total += f + wv
-    alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
     inst_names = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES")
     insts = {}
     if a.insts:
         runs = {c: per_kernel(a.insts, c) for c in inst_names}
-        for label, needle in (("split", f"decode_split_kernel<{group}, 3, true>"),
-                              ("merge", "decode_merge_kernel<true>")):
+        for label, needle in kernels:
             insts[label] = {c: statistics.mean(pick(runs[c], needle)) for c in inst_names}
     lines = [
-        f"# HBM traffic{' and instructions' if insts else ''} per decode launch: {a.workload}",
+        f"# HBM traffic{' and instructions' if insts else ''} per {a.kind} launch: {a.workload}",
         "",
         f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch){' and the instruction counters' if insts else ''}, "
         f"one rocprofv3 run each:",
@@ -106,7 +123,7 @@ def main():
         lines.append(f"| {label} | {f:,.0f} | {wv:,.0f} |")
     lines += [
         "",
-        f"Algorithmic bytes per launch (packed K and V rows, 104 B per token and KV head): {alg:,}.",
+        f"Algorithmic bytes per launch ({alg_text}): {alg:,}.",
         f"Measured / algorithmic: {total / alg:.3f}.",
         "",
         f"- hbm_bytes_per_launch: {total:.0f}",
@@ -126,7 +143,7 @@ def main():
             f"- mfma_insts_per_launch: {sum(v['SQ_INSTS_MFMA'] for v in insts.values()):.0f}",
         ]
     lines += [
-        f"- decode_source_sha256: {decode_source_digest()}",
+        f"- source_sha256: {digest}",
         "",
     ]
     with open(a.out, "w") as f:

@@ -67,12 +67,18 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
 //   M = max m_k, l = sum 2^(m_k - M) l_k, o' = sum 2^(m_k - M) o'_k,
 // then out = Hn B^T (o' / l), the single inverse rotation (kRotate; the fp16
 // decode's records are already in the model's basis). Lane t first reads
-// dims 4 (t % 32) .. +3 of records t / 32, t / 32 + 32, ... (coalesced), keeps
-// a running merge of them, and parks the result in LDS; wave 0 then combines
-// the 32 rows and rotates, two dims per lane. An empty sequence gives 0, an
-// invalid one NaN.
-template <bool kRotate>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a) {
+// dims 4 (t % 32) .. +3 of records t / 32, t / 32 + kRows, ... (coalesced),
+// keeps a running merge of them, and parks the result in LDS; wave 0 then
+// combines the kRows rows and rotates, two dims per lane. An empty sequence
+// gives 0, an invalid one NaN.
+//
+// kRows rows of 32 lanes (kRows <= 32): 8 when the records fit one round of
+// loads (a batch with few splits per sequence: 256 threads, so that many
+// work-groups start fast), 32 otherwise.
+template <bool kRotate, int kRows>
+__global__ __launch_bounds__(kRows * kMergeLanes) void decode_merge_kernel(MergeArgs a) {
+  constexpr int kMergeRows = kRows;
+  static_assert(kRows <= 32 && kRows * kMergeLanes >= 4 * kBlocks, "one row per lane of wave 0; 128 builders");
   __shared__ float rm[kMergeRows], rl[kMergeRows];
   __shared__ __align__(16) float ro[kMergeRows][kDim];
   __shared__ __align__(16) float mats[kBlocks * 16];   // the head's block matrices (kRotate)
@@ -165,11 +171,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs a
   // registers, with no further barrier.
   if (tid < 64) {
     const int t = tid;
-    const int r = t & (kMergeRows - 1);
-    const float m_r = rm[r];
+    const int r = t & 31;
+    const float m_r = r < kMergeRows ? rm[r & (kMergeRows - 1)] : -INFINITY;
     const float M = half_wave_reduce<true>(m_r);
-    const float w = M == -INFINITY ? 0.f : fast_exp2(m_r - M);
-    const float L = half_wave_reduce<false>(w * rl[r]);
+    const float w = M == -INFINITY ? 0.f : fast_exp2(m_r - M);   // rows past kMergeRows: 0
+    const float L = half_wave_reduce<false>(w * (r < kMergeRows ? rl[r & (kMergeRows - 1)] : 0.f));
     float x0 = 0.f, x1 = 0.f;
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
@@ -288,10 +294,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
-  if (a.rot != nullptr)
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(a.num_q_heads, a.n_seqs), dim3(kMergeThreads), 0, st, a);
+  const dim3 grid(a.num_q_heads, a.n_seqs);
+  const bool small = a.rec_splits <= 8 * kMergeChunk;   // one round of loads with 8 rows
+  if (a.rot != nullptr) {
+    if (small) hipLaunchKernelGGL((decode_merge_kernel<true, 8>), grid, dim3(8 * kMergeLanes), 0, st, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<true, 32>), grid, dim3(32 * kMergeLanes), 0, st, a);
+  } else {
+    if (small) hipLaunchKernelGGL((decode_merge_kernel<false, 8>), grid, dim3(8 * kMergeLanes), 0, st, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<false, 32>), grid, dim3(32 * kMergeLanes), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -33,9 +33,7 @@ constexpr int kMinBlocksPerSplit = 4;
 // 205 us per layer).
 constexpr int kMaxBlocksPerSplit = 64;
 constexpr int kMaxSplits = 2048;
-constexpr int kMergeThreads = 1024;
 constexpr int kMergeLanes = kDim / 4;                    // lanes per record, 4 dims each
-constexpr int kMergeRows = kMergeThreads / kMergeLanes;  // records read side by side
 // records per lane per round of loads (a fifth, so that 129 records take one
 // round, measured no faster: a merge work-group is bound by how fast its CU
 // pulls the ~68 KB of records, not by the rounds)
@@ -49,6 +47,10 @@ constexpr int kMergeChunk = 4;
 // keep their precision.
 constexpr float kWeightMaxLog2 = 15.0f;
 constexpr float kWeightRefLog2 = 7.0f;
+// Start value of the packed decode's reference: finite, so that 2^(s - m)
+// overflows for the first token that is not masked, which raises m; a wave
+// that saw no token keeps it, and its weight in the merge of the waves is 0.
+constexpr float kRefStart = -0x1p126f;
 
 // Max (or sum) of x over lanes i and i ^ 16, then i ^ 32, of a full wave: the
 // gfx950 row swaps hand each lane itself and its partner, in some order, in

@@ -311,45 +311,85 @@ __device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& 
   constexpr bool kSplitN = (G <= 8);
   const float nk[8] = {cur.nk0.x, cur.nk0.y, cur.nk0.z, cur.nk0.w, cur.nk1.x, cur.nk1.y, cur.nk1.z, cur.nk1.w};
   float nv[8] = {cur.nv0.x, cur.nv0.y, cur.nv0.z, cur.nv0.w, cur.nv1.x, cur.nv1.y, cur.nv1.z, cur.nv1.w};
-  float t[8];
+  // ts = the score before the scale fscale (log2 units after it)
+  float ts[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    t[i] = d0[i];
-    t[4 + i] = d1[i];
+    ts[i] = d0[i];
+    ts[4 + i] = d1[i];
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    if (kSplitN) t[k] += dpp_row_ror8(t[k]);
-    t[k] *= nk[k] * c.fscale;             // the score, log2 units
+    if (kSplitN) ts[k] += dpp_row_ror8(ts[k]);
+    ts[k] *= nk[k];
   }
-  if constexpr (!kFull) {
+  bool valid[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int rel = slot0 + 8 * q + k;
+    valid[k] = kFull || (rel >= c.rel_lo && rel < c.rel_hi);
+    if (!kFull) nv[k] = valid[k] ? nv[k] : 0.f;   // a slot outside the range may hold anything
+  }
+  // ---- online softmax with a lazily raised reference m ----
+  // The weights against the current m go straight into the P operand: e =
+  // 2^(s - m), p = e nV, split into fp16 halves. The hi half of p is p rounded
+  // toward zero to fp16 (its 11 leading bits: what the conversion does with p
+  // itself), the lo half p minus those bits; a lane of a lo row subtracts
+  // them (its mask keeps them), a lane of a hi row subtracts 0 and converts p.
+  // m must be raised (rarely) when some weight would pass 2^15 (fp16's range)
+  // or some e would pass 2^96 (the sum's range); m starts at kRefStart, so the
+  // first token of the wave raises it. Then the weights are formed again.
+  float esum, emax, pmax;
+  auto weights = [&]() {
+    esum = 0.f;
+    emax = 0.f;
+    pmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[2], xl[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k = 2 * i + j;
+        const float arg = __builtin_fmaf(ts[k], c.fscale, -st.m);
+        const float e = fast_exp2(kFull || valid[k] ? arg : -INFINITY);   // 2^-inf = 0
+        const float p = e * nv[k];
+        esum += e;
+        emax = max_hw(emax, e);
+        pmax = max_hw(pmax, p);
+        const uint32_t pb = __builtin_bit_cast(uint32_t, p);
+        if (kSplitN) {
+          x[j] = p - __builtin_bit_cast(float, pb & c.lo_mask);
+        } else {
+          x[j] = p;
+          xl[j] = p - __builtin_bit_cast(float, pb & 0xffffe000u);
+        }
+      }
+      w.pa.u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
+      if (!kSplitN) w.pa_lo.u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xl[0], xl[1]));
+    }
+  };
+  weights();
+  if (__any(pmax > 0x1p15f || emax > 0x1p96f)) {
+    // The new reference follows the largest log2 of a weight, i.e. of
+    // s + log2 nV, token by token, so that the fp16 halves of the weights
+    // keep their precision whatever the scale of the V norms. lg(x) =
+    // bits(x) / 2^23 - 127 is a lower bound of log2 x within 0.09 (the bit
+    // pattern read as a number); a norm below 2^-80 counts as 2^-80 here,
+    // which keeps e below 2^96. (Norms are >= 0.) The largest weight becomes
+    // 2^kWeightRefLog2; m is raised only when a weight would pass
+    // 2^kWeightMaxLog2, and the same for every lane of one head.
+    float u8[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int rel = slot0 + 8 * q + k;
-      const bool valid = rel >= c.rel_lo && rel < c.rel_hi;
-      t[k] = valid ? t[k] : -INFINITY;    // 2^-inf = 0 below
-      nv[k] = valid ? nv[k] : 0.f;        // a slot outside the range may hold anything
+      const float sk = kFull || valid[k] ? ts[k] * c.fscale : -INFINITY;
+      const uint32_t nb = max(__builtin_bit_cast(uint32_t, nv[k]), kNormFloorBits);
+      u8[k] = __builtin_fmaf(static_cast<float>(nb), 0x1p-23f, sk);   // s + lg(nV) + 127
     }
-  }
-  // ---- online softmax with a lazily raised reference ----
-  // The reference follows the largest log2 of a weight p nV = 2^(s - m) nV,
-  // i.e. of s + log2 nV, token by token, so that the fp16 halves of the
-  // weights keep their precision whatever the scale of the V norms. lg(x) =
-  // bits(x) / 2^23 - 127 is a lower bound of log2 x within 0.09 (the bit
-  // pattern read as a number); a norm below 2^-80 counts as 2^-80 here, which
-  // keeps 2^(s - m), and so the weights' sum, below 2^96. (Norms are >= 0.)
-  float u8[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t nb = max(__builtin_bit_cast(uint32_t, nv[k]), kNormFloorBits);
-    u8[k] = __builtin_fmaf(static_cast<float>(nb), 0x1p-23f, t[k]);   // s + lg(nV) + 127
-  }
-  float u = max_hw(max3_hw(u8[0], u8[1], u8[2]), max3_hw(max3_hw(u8[3], u8[4], u8[5]), u8[6], u8[7]));
-  u = rows_reduce<true>(u);
-  const bool bump = u > st.m + (kWeightMaxLog2 + 127.0f);   // same for every lane of one head
-  if (__any(bump)) {
+    float u = max_hw(max3_hw(u8[0], u8[1], u8[2]), max3_hw(max3_hw(u8[3], u8[4], u8[5]), u8[6], u8[7]));
+    u = rows_reduce<true>(u);
+    const bool bump = u > st.m + (kWeightMaxLog2 + 127.0f);
     const float m_new = bump ? u - (kWeightRefLog2 + 127.0f) : st.m;
-    const float alpha = bump ? fast_exp2(st.m - m_new) : 1.f;   // m = -inf gives 0
+    const float alpha = bump ? fast_exp2(st.m - m_new) : 1.f;   // from the start value: 0
     st.l *= alpha;
     st.m = m_new;
     // accumulator rows 4q + i belong to head (4q + i) mod 8 (or 4q + i when G = 16)
@@ -360,47 +400,34 @@ __device__ __forceinline__ void block_softmax(const floatx4& d0, const floatx4& 
 #pragma unroll
       for (int d = 0; d < 8; ++d) st.acc[d][i] *= ar;
     }
-  }
-  const float mref = (st.m == -INFINITY) ? 0.f : st.m;
-  // weights of tokens 8q + k. The hi half of p is p rounded toward zero to
-  // fp16 (its 11 leading bits: what the conversion below does with p itself),
-  // the lo half p minus those bits. A lane of a lo row subtracts them (its
-  // mask keeps them), a lane of a hi row subtracts 0 and converts p.
-  float esum = 0.f, x[8], xl[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float e = fast_exp2(t[k] - mref);
-    esum += e;
-    const float p = e * nv[k];
-    const uint32_t pb = __builtin_bit_cast(uint32_t, p);
-    if (kSplitN) {
-      x[k] = p - __builtin_bit_cast(float, pb & c.lo_mask);
-    } else {
-      x[k] = p;
-      xl[k] = p - __builtin_bit_cast(float, pb & 0xffffe000u);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w.pa.u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]));
-    if (!kSplitN) w.pa_lo.u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xl[2 * i], xl[2 * i + 1]));
+    weights();
   }
   st.l += esum;
 }
 
-// PV: B = hi(alpha c) of dim 8n + D for the tokens 8q .. 8q+7 (V tile q)
+// PV operands: B = hi(alpha c) of dim 8n + D for the tokens 8q .. 8q+7 (V
+// tile q). (Requesting them before the softmax, so that their table reads
+// overlap it, needs the query operands back in LDS for the registers: measured
+// slower, MoE step 15.6 -> 15.8 us, 131K decode 39.3 -> 41.2 us.)
+struct BlockVOps {
+  H8 v[8];
+};
+
 template <int G>
-__device__ __forceinline__ void block_pv(const uint32_t (&vw)[6], const BlockWeights& w, const Consts<G>& c,
-                                         WaveState& st) {
+__device__ __forceinline__ void block_v_ops(const uint32_t (&vw)[6], const Consts<G>& c, BlockVOps& o) {
+#define IQ_VOP(D) o.v[D].h = code_operand_hi<24 * D>(vw, c.lut, c.lane_off);
+  IQ_VOP(0) IQ_VOP(1) IQ_VOP(2) IQ_VOP(3) IQ_VOP(4) IQ_VOP(5) IQ_VOP(6) IQ_VOP(7)
+#undef IQ_VOP
+}
+
+template <int G>
+__device__ __forceinline__ void block_pv(const BlockVOps& o, const BlockWeights& w, WaveState& st) {
   constexpr bool kSplitN = (G <= 8);
-#define IQ_PV(D)                                                                     \
-  {                                                                                  \
-    const half8 v = code_operand_hi<24 * D>(vw, c.lut, c.lane_off);                  \
-    st.acc[D] = mfma16(w.pa.h, v, st.acc[D]);                                        \
-    if (!kSplitN) st.acc[D] = mfma16(w.pa_lo.h, v, st.acc[D]);                       \
+#pragma unroll
+  for (int D = 0; D < 8; ++D) {
+    st.acc[D] = mfma16(w.pa.h, o.v[D].h, st.acc[D]);
+    if (!kSplitN) st.acc[D] = mfma16(w.pa_lo.h, o.v[D].h, st.acc[D]);
   }
-  IQ_PV(0) IQ_PV(1) IQ_PV(2) IQ_PV(3) IQ_PV(4) IQ_PV(5) IQ_PV(6) IQ_PV(7)
-#undef IQ_PV
 }
 
 template <int G, int KB>
@@ -408,12 +435,14 @@ __device__ __forceinline__ void process_block(const BlockData<KB>& cur, int slot
                                               WaveState& st) {
   floatx4 d0, d1;
   BlockWeights w;
+  BlockVOps vo;
   block_scores<G, KB>(cur, c, d0, d1);
   if (slot0 >= c.rel_lo && slot0 + kBlk <= c.rel_hi)   // wave-uniform
     block_softmax<G, KB, true>(d0, d1, cur, slot0, q, c, st, w);
   else
     block_softmax<G, KB, false>(d0, d1, cur, slot0, q, c, st, w);
-  block_pv<G>(cur.vw, w, c, st);
+  block_v_ops<G>(cur.vw, c, vo);
+  block_pv<G>(vo, w, st);
 }
 
 // LDS of one packed split work-group.
