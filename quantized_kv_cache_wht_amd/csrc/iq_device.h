@@ -101,6 +101,63 @@ __device__ __forceinline__ void wht128_quad(float (&x)[kPerLane], int part) {
   }
 }
 
+// x[i] <- x_partner[i] * s + x[i] for i = i0 .. i0+7, the partner being lane
+// part ^ M (M = 1 or 2) of the quad: one v_fmac_f32 per value with its first
+// operand moved across lanes by DPP. (The compiler folds a lane move only into
+// an add, never into a multiply-add, hence the asm.) A DPP read of a register
+// that the instruction before wrote needs two wait states: the s_nop gives
+// them, and within the block no instruction reads another's result.
+template <int M>
+__device__ __forceinline__ void dpp_fmac8(float (&x)[kPerLane], int i0, float s) {
+  static_assert(M == 1 || M == 2, "quad partners");
+#define IQ_DPP_FMAC(K) "v_fmac_f32_dpp %" #K ", %" #K ", %8 " IQ_QP " row_mask:0xf bank_mask:0xf\n\t"
+#define IQ_DPP_BLOCK                                                                                  \
+  asm volatile("s_nop 1\n\t" IQ_DPP_FMAC(0) IQ_DPP_FMAC(1) IQ_DPP_FMAC(2) IQ_DPP_FMAC(3) IQ_DPP_FMAC(4) \
+                   IQ_DPP_FMAC(5) IQ_DPP_FMAC(6) IQ_DPP_FMAC(7)                                       \
+               : "+v"(x[i0]), "+v"(x[i0 + 1]), "+v"(x[i0 + 2]), "+v"(x[i0 + 3]), "+v"(x[i0 + 4]),     \
+                 "+v"(x[i0 + 5]), "+v"(x[i0 + 6]), "+v"(x[i0 + 7])                                     \
+               : "v"(s))
+  if constexpr (M == 1) {
+#define IQ_QP "quad_perm:[1,0,3,2]"
+    IQ_DPP_BLOCK;
+#undef IQ_QP
+  } else {
+#define IQ_QP "quad_perm:[2,3,0,1]"
+    IQ_DPP_BLOCK;
+#undef IQ_QP
+  }
+#undef IQ_DPP_BLOCK
+#undef IQ_DPP_FMAC
+}
+
+// The same transform up to a sign per lane part: returns eps(part) H x with
+// eps(p) = (-1)^popcount(p) (+1 for parts 0 and 3, -1 for parts 1 and 2).
+// Each cross-lane stage is then one multiply-add per value whose lane-moved
+// operand is the partner's (partner * sigma + self, sigma = -1 on the lane
+// with the stage's bit set): the upper lane gets self - partner, the exact
+// negation of the butterfly's partner - self. The signs carried through the
+// second stage come out as eps(p); a caller folds them into the next linear
+// map (negated block matrices), which is exact, so the results are
+// bit-identical to wht128_quad's.
+__device__ __forceinline__ void wht128_quad_signed(float (&x)[kPerLane], int part) {
+#pragma unroll
+  for (int h = 1; h < kPerLane; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+  const float s1 = (part & 1) ? -1.0f : 1.0f, s2 = (part & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < kPerLane; i += 8) dpp_fmac8<1>(x, i, s1);
+#pragma unroll
+  for (int i = 0; i < kPerLane; i += 8) dpp_fmac8<2>(x, i, s2);
+}
+
 // ------------------------------------------------------------- SO(4) ----
 // The block matrices are built without multiply-add contraction, so that
 // every kernel that builds them (each in its own inlining context) gets the
@@ -253,7 +310,9 @@ __device__ __forceinline__ void load_block_params(const float* rot_head, int kin
 // slot 4 b + p, so that the four lanes of a vector, reading their b-th blocks
 // together, hit different LDS banks (block-major order puts them 512 bytes
 // apart, all in one bank); otherwise block-major.
-template <bool kQuadOrder = false>
+// kSigned (quad order, WHT + SO(4) kind only): the matrices of lane parts 1
+// and 2 (blocks 8..23) are negated, to take back wht128_quad_signed's signs.
+template <bool kQuadOrder = false, bool kSigned = false>
 __device__ __forceinline__ void build_head_matrices(int kind, const float (&bp)[8], float* sm) {
   const int t = threadIdx.x;
   if (t < 4 * kBlocks) {
@@ -261,18 +320,21 @@ __device__ __forceinline__ void build_head_matrices(int kind, const float (&bp)[
     const int slot = kQuadOrder ? (b & 7) * 4 + (b >> 3) : b;
     float col[4];
     block_column(kind, bp, c, col);
+    const int p = b >> 3;
+    const bool neg = kSigned && kind == kRotWhtSo4 && (p == 1 || p == 2);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm[slot * 16 + r * 4 + c] = col[r];
+    for (int r = 0; r < 4; ++r) sm[slot * 16 + r * 4 + c] = neg ? -col[r] : col[r];
   }
 }
 
 // Fill LDS with the 32 block matrices of one head (row-major each, in the
 // quad-form order that so4_apply_lane reads). Must be called by all threads of
 // the block (at least 128): threads 0..127 build one column each.
+template <bool kSigned = false>
 __device__ __forceinline__ void load_head_matrices(const float* __restrict__ rot_head, int kind, float* sm) {
   float bp[8];
   load_block_params(rot_head, kind, (threadIdx.x >> 2) & (kBlocks - 1), bp);
-  build_head_matrices<true>(kind, bp, sm);
+  build_head_matrices<true, kSigned>(kind, bp, sm);
 }
 
 // y_b = M_b y_b for this lane's 8 blocks (transpose = use M_b^T); the

@@ -256,7 +256,8 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
       }
     }
   }
-  load_head_matrices(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, sm);
+  // matrices with the signs of wht128_quad_signed folded in
+  load_head_matrices<true>(rot_of_head(a.rot, a.rot_kind, h), a.rot_kind, sm);
   __syncthreads();
 
   for (; win < n_windows; win += gridDim.x) {
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     } else if (win != static_cast<int>(blockIdx.x)) {
       load_vec<T>(src_of(win), ok, x);
     }
-    if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
+    if (a.rot_kind == kRotWhtSo4) wht128_quad_signed(x, part);
     so4_apply_lane<false>(x, sm, part);
     if (kK4 && !is_v) {
       uint32_t w4[4];
