@@ -649,22 +649,16 @@ __device__ __forceinline__ uint32_t centroid16_f16(uint32_t v, const Codebook& c
   return neg ? (mag ^ 0x8000u) : mag;
 }
 
-// Pack 32 codes (3 bits each) into 3 dwords, code i at bits [3i, 3i+3).
+// Pack 32 codes (3 bits each) into 3 dwords, code i at bits [3i, 3i+3):
+// each code is one shift-or into its dword (codes 10 and 21 straddle two).
 __device__ __forceinline__ void pack32(const uint32_t (&c)[kPerLane], uint32_t (&w)[3]) {
-  uint64_t lo = 0, hi = 0;   // 96-bit accumulator
+  w[0] = w[1] = w[2] = 0u;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
-    const int bit = 3 * i;
-    if (bit < 64) {
-      lo |= static_cast<uint64_t>(c[i]) << bit;
-      if (bit > 61) hi |= static_cast<uint64_t>(c[i]) >> (64 - bit);
-    } else {
-      hi |= static_cast<uint64_t>(c[i]) << (bit - 64);
-    }
+    const int bit = 3 * i, word = bit >> 5, off = bit & 31;   // compile-time after unrolling
+    w[word] |= c[i] << off;
+    if (off > 29) w[word + 1] |= c[i] >> (32 - off);
   }
-  w[0] = static_cast<uint32_t>(lo);
-  w[1] = static_cast<uint32_t>(lo >> 32);
-  w[2] = static_cast<uint32_t>(hi);
 }
 
 // Code i (0..31) of a 96-bit group held in 3 dwords.
