@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeArgs
   __shared__ PackedSmem<G, KB> sm;
   __shared__ StageMem<G, KB> stg;
   static_assert(sizeof(PackedSmem<G, KB>) >= sizeof(NewTokenSmem<G>), "new-token LDS must fit");
+  touch_codebook_words<KB>(a.cb);
   if constexpr (kNew) {
     if (blockIdx.z == 0) {
       new_token_block<G, KB>(a, nt, *reinterpret_cast<NewTokenSmem<G>*>(&sm));
@@ -102,10 +103,12 @@ __global__ __launch_bounds__(kRows * kMergeLanes) void decode_merge_kernel(Merge
   for (int i = 0; i < kMergeChunk; ++i) {
     const int p = row + i * kMergeRows;
     const float* r = recs + static_cast<size_t>(p < a.rec_splits ? p : 0) * kRec;
-    mv[i] = r[0];
-    lv[i] = r[1];
+    const float2 ml = *reinterpret_cast<const float2*>(r);
+    mv[i] = ml.x;
+    lv[i] = ml.y;
     ov[i] = reinterpret_cast<const float4*>(r + 4)[d4];
   }
+  float* const dst = a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim;
   bool ok = true;
   int live0 = 0, live1 = 0;
 #pragma unroll
@@ -131,8 +134,9 @@ __global__ __launch_bounds__(kRows * kMergeLanes) void decode_merge_kernel(Merge
       for (int i = 0; i < kMergeChunk; ++i) {
         const int p = p0 + i * kMergeRows;
         const float* r = recs + static_cast<size_t>(p < a.rec_splits ? p : 0) * kRec;
-        mv[i] = r[0];
-        lv[i] = r[1];
+        const float2 ml = *reinterpret_cast<const float2*>(r);
+        mv[i] = ml.x;
+        lv[i] = ml.y;
         ov[i] = reinterpret_cast<const float4*>(r + 4)[d4];
       }
     }
@@ -165,34 +169,45 @@ __global__ __launch_bounds__(kRows * kMergeLanes) void decode_merge_kernel(Merge
   }
   reinterpret_cast<float4*>(ro[row])[d4] = o;
   __syncthreads();
-  // The rest runs on wave 0 alone, two dims per lane (t and t + 64): the row
-  // partials' weights (lane r holds row r's; lanes 32..63 repeat them), their
-  // weighted sum read column-wise from LDS, then the inverse rotation in
-  // registers, with no further barrier.
+  // The rows' weights w_r = 2^(m_r - M) and 1 / L (L = sum_r w_r l_r), by
+  // the first kRows lanes, into LDS; then wave 0 alone: two dims per lane (t
+  // and t + 64), their weighted sum over the rows (weights read as
+  // broadcasts, four independent sums), then the inverse rotation in
+  // registers.
+  __shared__ __align__(16) float rw[kMergeRows];
+  __shared__ float rinv;
   if (tid < 64) {
-    const int t = tid;
-    const int r = t & 31;
+    const int r = tid & 31;
     const float m_r = r < kMergeRows ? rm[r & (kMergeRows - 1)] : -INFINITY;
     const float M = half_wave_reduce<true>(m_r);
     const float w = M == -INFINITY ? 0.f : fast_exp2(m_r - M);   // rows past kMergeRows: 0
     const float L = half_wave_reduce<false>(w * (r < kMergeRows ? rl[r & (kMergeRows - 1)] : 0.f));
-    float x0 = 0.f, x1 = 0.f;
+    if (tid < kMergeRows) rw[tid] = w;
+    if (tid == 0) rinv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int t = tid;
+    float x0[4] = {0.f, 0.f, 0.f, 0.f}, x1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kMergeRows; ++k) {
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-      x0 = __builtin_fmaf(wk, ro[k][t], x0);
-      x1 = __builtin_fmaf(wk, ro[k][t + 64], x1);
+    for (int k0 = 0; k0 < kMergeRows; k0 += 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&rw[k0]);
+      const float wk[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x0[u] = __builtin_fmaf(wk[u], ro[k0 + u][t], x0[u]);
+        x1[u] = __builtin_fmaf(wk[u], ro[k0 + u][t + 64], x1[u]);
+      }
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    x0 *= inv;
-    x1 *= inv;
+    const float inv = rinv;
+    float y0 = ((x0[0] + x0[1]) + (x0[2] + x0[3])) * inv;
+    float y1 = ((x1[0] + x1[1]) + (x1[2] + x1[3])) * inv;
     if (kRotate) {
-      so4_apply_pair<true>(x0, x1, mats, t);
-      if (a.rot_kind == kRotWhtSo4) wht128_pair(x0, x1, t);
+      so4_apply_pair<true>(y0, y1, mats, t);
+      if (a.rot_kind == kRotWhtSo4) wht128_pair(y0, y1, t);
     }
-    float* dst = a.out + (static_cast<size_t>(s) * a.num_q_heads + hq) * kDim;
-    dst[t] = ok ? x0 : NAN;
-    dst[t + 64] = ok ? x1 : NAN;
+    dst[t] = ok ? y0 : NAN;
+    dst[t + 64] = ok ? y1 : NAN;
   }
 }
 

@@ -406,6 +406,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_deferred_split_kernel(F
   if (z < pre.n_splits) {
     f16_split<G>(pre, sm.f, z);
   } else {
+    touch_codebook_words<KB>(suf.cb);
     packed_split<G, KB>(suf, sm.k.p, sm.k.stg, z - pre.n_splits);
   }
 }

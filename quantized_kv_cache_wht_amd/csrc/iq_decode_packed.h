@@ -99,6 +99,27 @@ __device__ __forceinline__ half8 code_operand_hi(const uint32_t (&w)[N], const c
   return r.h;
 }
 
+// The codebook's fp16 words (kernel arguments) into scalar registers at
+// this point: a use in asm makes the compiler load them here, with the
+// kernel's first argument loads. A scalar wait covers every scalar load in
+// flight, so these must not be loaded after the sequence bounds, or the code
+// table's fill would wait for the bounds.
+template <int KB>
+__device__ __forceinline__ void touch_codebook_words(const Codebook& cb) {
+  static_assert(__builtin_offsetof(Codebook, l16) == __builtin_offsetof(Codebook, h16) + 8 &&
+                    __builtin_offsetof(Codebook, l16k) == __builtin_offsetof(Codebook, h16k) + 16,
+                "each lo table follows its hi table");
+  uint32_t cw[4];
+  __builtin_memcpy(cw, cb.h16, sizeof(cw));   // h16[4], l16[4]
+  asm volatile("" ::"s"(cw[0]), "s"(cw[1]), "s"(cw[2]), "s"(cw[3]));
+  if constexpr (KB == 4) {
+    uint32_t kw[8];
+    __builtin_memcpy(kw, cb.h16k, sizeof(kw));   // h16k[8], l16k[8]
+    asm volatile("" ::"s"(kw[0]), "s"(kw[1]), "s"(kw[2]), "s"(kw[3]), "s"(kw[4]), "s"(kw[5]), "s"(kw[6]),
+                 "s"(kw[7]));
+  }
+}
+
 // Packed codes and norms of one 32-slot block for this lane (KB = K bits).
 template <int KB>
 struct BlockData {
