@@ -61,6 +61,8 @@ def parse():
                    help="finish with 3 device-to-device copies of this many MiB (reference for HBM counters)")
     p.add_argument("--profile-append", action="store_true",
                    help="only the bulk encode of the append roofline (and the calibration copies), for counter runs")
+    p.add_argument("--profile-decode", choices=("long_t131072",), default=None,
+                   help="only this workload's decode launches (and the calibration copies), for counter runs")
     return p.parse_args()
 
 
@@ -306,6 +308,44 @@ def append_roofline(us: float, T: int, hkv: int, one_token_us: float | None) -> 
     return r
 
 
+def long_decode(iq, stream, gen, timing_cache, calls=12):
+    """The 131072-token decode (32 query heads, 8 KV heads) over three layers' caches in turn, back
+    to back; returns (us per call, packed bytes per call)."""
+    import torch
+    import iqinputs
+    dev = torch.device("cuda")
+    w = iqinputs.WORKLOADS["long_t131072"]
+    T, hkv, hq = w.seq_len, w.num_kv_heads, w.num_q_heads
+    cs = [timing_cache(hkv, T) for _ in range(3)]
+    ql = torch.randn((1, hq, 128), generator=gen, device=dev)
+    stl = torch.zeros(1, dtype=torch.int32, device=dev)
+    lnl = torch.full((1,), T, dtype=torch.int32, device=dev)
+    wsl = iq.decode_workspace(1, hq, hkv, T, device=dev)
+    outl = torch.empty_like(ql)
+    us = time_per_call(torch, lambda i: iq.iq_decode_attention(cs[i % 3], ql, stl, lnl, T, out=outl,
+                                                               workspace=wsl, stream=stream), calls, stream)
+    del cs
+    return us, hkv * T * 2 * ROW_BYTES
+
+
+def random_code_cache(iq, gen):
+    """A cache factory for timing: random codes and norms (the decode's work does not depend on the
+    values; parity at these shapes is tested separately)."""
+    import torch
+    import iqinputs
+    dev = torch.device("cuda")
+
+    def timing_cache(hkv, cap):
+        rot = torch.from_numpy(iqinputs.rotation_params(11, 0, hkv)).to(dev)
+        c = iq.PackedKVCache.allocate(hkv, cap, rot, device=dev)
+        c.k_codes.random_(0, 256, generator=gen)
+        c.v_codes.random_(0, 256, generator=gen)
+        c.k_norms.uniform_(5.0, 15.0, generator=gen)
+        c.v_norms.uniform_(5.0, 15.0, generator=gen)
+        return c
+    return timing_cache
+
+
 def other_workloads(iq, stream):
     """The other measured configurations, timed like the main one (HIP events around back-to-back
     calls). Their caches hold random codes and norms (the decode's work does not depend on the
@@ -317,15 +357,7 @@ def other_workloads(iq, stream):
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(20260818)
-
-    def timing_cache(hkv, cap):
-        rot = torch.from_numpy(iqinputs.rotation_params(11, 0, hkv)).to(dev)
-        c = iq.PackedKVCache.allocate(hkv, cap, rot, device=dev)
-        c.k_codes.random_(0, 256, generator=gen)
-        c.v_codes.random_(0, 256, generator=gen)
-        c.k_norms.uniform_(5.0, 15.0, generator=gen)
-        c.v_norms.uniform_(5.0, 15.0, generator=gen)
-        return c
+    timing_cache = random_code_cache(iq, gen)
 
     res = {}
     # 8B dense shape: Hq 32, Hkv 8, 8191 cached tokens, 32 layers, one decode step per layer
@@ -369,21 +401,10 @@ def other_workloads(iq, stream):
     del c, wsb
 
     # long context: decode over three layers' caches of 131072 tokens
-    w = iqinputs.WORKLOADS["long_t131072"]
-    T, hkv, hq = w.seq_len, w.num_kv_heads, w.num_q_heads
-    cs = [timing_cache(hkv, T) for _ in range(3)]
-    ql = torch.randn((1, hq, 128), generator=gen, device=dev)
-    stl = torch.zeros(1, dtype=torch.int32, device=dev)
-    lnl = torch.full((1,), T, dtype=torch.int32, device=dev)
-    wsl = iq.decode_workspace(1, hq, hkv, T, device=dev)
-    outl = torch.empty_like(ql)
-    us_dec = time_per_call(torch, lambda i: iq.iq_decode_attention(cs[i % 3], ql, stl, lnl, T, out=outl,
-                                                                   workspace=wsl, stream=stream), 12, stream)
-    dec_bytes = hkv * T * 2 * ROW_BYTES
-    res[w.name] = {"decode_us": round(us_dec, 2), "decode_GBps": round(dec_bytes / us_dec / 1e3, 1),
-                   "frac_hbm_peak": round(dec_bytes / us_dec / 1e3 / HBM_PEAK_GBS, 4),
-                   "note": "the bulk encode of this workload is append_roofline"}
-    del cs
+    us_dec, dec_bytes = long_decode(iq, stream, gen, timing_cache)
+    res["long_t131072"] = {"decode_us": round(us_dec, 2), "decode_GBps": round(dec_bytes / us_dec / 1e3, 1),
+                           "frac_hbm_peak": round(dec_bytes / us_dec / 1e3 / HBM_PEAK_GBS, 4),
+                           "note": "the bulk encode of this workload is append_roofline"}
 
     # streaming peak on this GPU: device-to-device copy of 1 GiB (read + write bytes)
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -458,6 +479,15 @@ def main():
     w = iqinputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_decode:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20260818)
+        us, nbytes = long_decode(iq, torch.cuda.current_stream(), gen, random_code_cache(iq, gen), calls=6)
+        if args.copy_calibration_mib > 0:
+            calibration_copies(torch, args.copy_calibration_mib)
+        print(json.dumps({"profile_decode_us": round(us, 2), "workload": args.profile_decode, "bytes": nbytes}),
+              flush=True)
+        return
     if args.profile_append:
         us, T_a, hkv_a = append_bulk(iq, torch.cuda.current_stream())
         if args.copy_calibration_mib > 0:

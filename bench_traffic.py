@@ -9,14 +9,18 @@ summary that bench.py reports when the kernel sources still match:
                  workload's group size with the new token's work-groups, and
                  the merge); bench.py's roofline.traffic and valu_roof;
   --kind append  the bulk encode of the long-context workload
-                 (bench.py --profile-append); bench.py's append_roofline.
+                 (bench.py --profile-append); bench.py's append_roofline;
+  --kind decode_long  the 131072-token decode's split kernel and merge
+                 (bench.py --profile-decode long_t131072).
 With --insts, a third run's instruction counters (SQ_INSTS_VALU, SQ_INSTS_MFMA,
 SQ_INSTS_LDS, SQ_INSTS_SALU, SQ_WAVES: wave-level instructions summed over the
 chip) go into the same summary; bench.py reports the VALU count against the
-VALU issue roof.
+VALU issue roof. With --sq, more runs' shader counters (any SQ_* counters,
+summed over the chip per dispatch) are tabulated per kernel as well, with the
+instructions per 32-slot block of the decode kinds.
 
-    python bench_traffic.py --kind decode|append --fetch DIR --write DIR --copy-mib N --workload W \\
-        [--insts DIR] --command "..." --out profiles/<kind>_W_traffic.md
+    python bench_traffic.py --kind decode|append|decode_long --fetch DIR --write DIR --copy-mib N \\
+        --workload W [--insts DIR] [--sq DIR ...] --command "..." --out profiles/<kind>_W_traffic.md
 """
 from __future__ import annotations
 
@@ -44,6 +48,19 @@ def per_kernel(run_dir: str, counter: str):
     return vals
 
 
+def all_counters(run_dirs):
+    """{kernel name: {counter: [values of its dispatches]}} over several run dirs."""
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in run_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                out[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
 def pick(vals, needle):
     """Counter values of the dispatches of one kernel: `needle` is (demangled, mangled) names or a
     single name (the profiler writes either form, depending on its version and options)."""
@@ -60,8 +77,9 @@ def main():
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--kind", choices=("decode", "append"), default="decode")
+    ap.add_argument("--kind", choices=("decode", "append", "decode_long"), default="decode")
     ap.add_argument("--insts", default=None, help="run dir of the instruction-counter pass")
+    ap.add_argument("--sq", nargs="*", default=[], help="run dirs of further shader-counter passes")
     ap.add_argument("--command", required=True, help="the two profiling commands, for the record")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
@@ -80,6 +98,12 @@ def main():
     group = w.num_q_heads // w.num_kv_heads
     if a.kind == "decode":
         kernels = (("split", (f"decode_split_kernel<{group}, 3, true>", f"decode_split_kernelILi{group}ELi3ELb1E")),
+                   ("merge", ("decode_merge_kernel<true, 32>", "decode_merge_kernelILb1ELi32E")))
+        alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
+        alg_text = "packed K and V rows, 104 B per token and KV head"
+        digest = decode_source_digest()
+    elif a.kind == "decode_long":
+        kernels = (("split", (f"decode_split_kernel<{group}, 3, false>", f"decode_split_kernelILi{group}ELi3ELb0E")),
                    ("merge", ("decode_merge_kernel<true, 32>", "decode_merge_kernelILb1ELi32E")))
         alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
         alg_text = "packed K and V rows, 104 B per token and KV head"
@@ -142,6 +166,29 @@ def main():
             f"- valu_insts_per_launch: {sum(v['SQ_INSTS_VALU'] for v in insts.values()):.0f}",
             f"- mfma_insts_per_launch: {sum(v['SQ_INSTS_MFMA'] for v in insts.values()):.0f}",
         ]
+    if a.sq:
+        cs = all_counters(a.sq)
+        blocks = w.num_kv_heads * w.seq_len // 32 if a.kind != "append" else None
+        for label, needle in kernels:
+            names = needle if isinstance(needle, tuple) else (needle,)
+            merged = collections.defaultdict(list)
+            for k, d in cs.items():
+                if any(n in k for n in names):
+                    for c, v in d.items():
+                        merged[c].extend(v)
+            if not merged:
+                continue
+            lines += ["", f"Shader counters per dispatch, {label} kernel (mean over dispatches; per-block "
+                          f"columns divide by the launch's {blocks:,} blocks of 32 slots)" if blocks else
+                      f"Shader counters per dispatch, {label} kernel (mean over dispatches)", "",
+                      "| counter | per dispatch |" + (" per block |" if blocks else ""),
+                      "|---|---|" + ("---|" if blocks else "")]
+            for c in sorted(merged):
+                v = statistics.mean(merged[c])
+                lines.append(f"| {c} | {v:,.0f} |" + (f" {v / blocks:,.1f} |" if blocks else ""))
+            if "SQ_LDS_BANK_CONFLICT" in merged and "SQ_LDS_IDX_ACTIVE" in merged:
+                bc, act = statistics.mean(merged["SQ_LDS_BANK_CONFLICT"]), statistics.mean(merged["SQ_LDS_IDX_ACTIVE"])
+                lines.append(f"\nLDS cycles lost to bank conflicts: {bc / act:.2f} of its active cycles.")
     lines += [
         f"- source_sha256: {digest}",
         "",

@@ -25,8 +25,9 @@ def test_counter_summary_is_whole_or_ignored():
         assert set(c) == {"hbm_bytes_per_launch", "valu_insts_per_launch", "mfma_insts_per_launch"}
         # at least the packed K and V rows (104 B per token and KV head) are read
         assert c["hbm_bytes_per_launch"] >= 4 * 32768 * 104
-        # 32 MFMAs per 32-slot block and wave: the 1024 blocks of 4 KV heads x 32768 tokens
-        assert c["mfma_insts_per_launch"] >= 32 * 4 * 1024
+        # 24 MFMAs per 32-slot block (16 for the scores of G = 8 query heads, 8 for PV: all 32
+        # tokens in one MFMA per 16-dim tile): the 1024 blocks of each of 4 KV heads x 32768 tokens
+        assert c["mfma_insts_per_launch"] >= 24 * 4 * 1024
         assert bench.measured_traffic("moe30b_gqa_t32768") == c["hbm_bytes_per_launch"]
     else:
         assert bench.measured_traffic("moe30b_gqa_t32768") is None
