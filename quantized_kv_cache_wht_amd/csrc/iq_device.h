@@ -139,9 +139,11 @@ __device__ __forceinline__ void dpp_fmac8(float (&x)[kPerLane], int i0, float s)
 // second stage come out as eps(p); a caller folds them into the next linear
 // map (negated block matrices), which is exact, so the results are
 // bit-identical to wht128_quad's.
+// kFirstH = 2: the caller has done the first stage (h = 1) itself.
+template <int kFirstH = 1>
 __device__ __forceinline__ void wht128_quad_signed(float (&x)[kPerLane], int part) {
 #pragma unroll
-  for (int h = 1; h < kPerLane; h <<= 1) {
+  for (int h = kFirstH; h < kPerLane; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
       if ((i & h) == 0) {

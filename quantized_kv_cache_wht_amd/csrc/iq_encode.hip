@@ -90,6 +90,28 @@ __device__ __forceinline__ void raw_to_x(const RawVec<T>& r, float (&x)[kPerLane
   }
 }
 
+// The WHT's first butterfly stage (dims 2k and 2k + 1 of the lane, the two
+// fp16 halves of input word k) straight from the fp16 input, in place of
+// the conversion: v_fma_mix_f32 converts each half exactly and rounds the sum
+// once, the same bits as converting first and adding after.
+__device__ __forceinline__ void wht_first_stage_f16(const RawVec<_Float16>& r, float (&x)[kPerLane]) {
+  const float one = 1.0f;
+#pragma unroll
+  for (int i = 0; i < RawVec<_Float16>::kWords; ++i) {
+    const uint32_t u[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float sum, dif;
+      asm("v_fma_mix_f32 %0, %2, %3, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]\n\t"
+          "v_fma_mix_f32 %1, %2, %3, -%2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+          : "=&v"(sum), "=v"(dif)
+          : "v"(u[k]), "s"(one));
+      x[8 * i + 2 * k] = sum;
+      x[8 * i + 2 * k + 1] = dif;
+    }
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_vec(T* __restrict__ dst, const float (&x)[kPerLane]);
 
@@ -263,13 +285,24 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   for (; win < n_windows; win += gridDim.x) {
     const int tok = token_of(win);
     const bool ok = tok >= 0 && tok < a.n_tokens;
+    // fp16 input with the WHT: its first stage reads the raw halves (no conversion)
+    constexpr bool kMixFirst = kPrefetch && sizeof(T) == 2;
+    const bool wht = a.rot_kind == kRotWhtSo4;
     if (kPrefetch) {
-      raw_to_x<T>(raw, x);
+      if constexpr (kMixFirst) {
+        if (wht) wht_first_stage_f16(raw, x);
+        else raw_to_x<T>(raw, x);
+      } else {
+        raw_to_x<T>(raw, x);
+      }
       if (win + static_cast<int>(gridDim.x) < n_windows) load_raw<T>(src_of(win + gridDim.x), raw);
     } else if (win != static_cast<int>(blockIdx.x)) {
       load_vec<T>(src_of(win), ok, x);
     }
-    if (a.rot_kind == kRotWhtSo4) wht128_quad_signed(x, part);
+    if (wht) {
+      if constexpr (kMixFirst) wht128_quad_signed<2>(x, part);
+      else wht128_quad_signed<1>(x, part);
+    }
     so4_apply_lane<false>(x, sm, part);
     if (kK4 && !is_v) {
       uint32_t w4[4];
