@@ -74,11 +74,16 @@ __device__ __forceinline__ double dpp_f64(double x) {
 
 // ---------------------------------------------------------------- WHT ----
 // Unnormalised Sylvester Hadamard transform of the 128-vector held by a quad
-// of lanes (x = this lane's 32 dims). The 1/sqrt(128) is folded into the SO(4)
-// matrices by the callers.
+// of lanes (x = this lane's 32 dims), without its two innermost stages. The
+// transform is the product of seven commuting butterfly stages, one per bit
+// of the dim index; the stages of bits 0 and 1 act within each 4-dim block,
+// as the 4x4 Hadamard matrix H4, and are folded into the block matrices (M H4
+// in place of M, see fold_h4_*), as is the 1/sqrt(128). Every kernel that
+// rotates uses folded matrices and skips these two stages, forward and back
+// (the inverse applies (M H4)^T = H4 M^T, H4 being symmetric).
 __device__ __forceinline__ void wht128_quad(float (&x)[kPerLane], int part) {
 #pragma unroll
-  for (int h = 1; h < kPerLane; h <<= 1) {
+  for (int h = 4; h < kPerLane; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
       if ((i & h) == 0) {
@@ -139,11 +144,12 @@ __device__ __forceinline__ void dpp_fmac8(float (&x)[kPerLane], int i0, float s)
 // second stage come out as eps(p); a caller folds them into the next linear
 // map (negated block matrices), which is exact, so the results are
 // bit-identical to wht128_quad's.
-// kFirstH = 2: the caller has done the first stage (h = 1) itself.
-template <int kFirstH = 1>
+// (Without the two innermost stages, as wht128_quad.) kFirstDone: the caller
+// has done the first remaining stage (bit 2, h = 4) itself.
+template <bool kFirstDone = false>
 __device__ __forceinline__ void wht128_quad_signed(float (&x)[kPerLane], int part) {
 #pragma unroll
-  for (int h = kFirstH; h < kPerLane; h <<= 1) {
+  for (int h = kFirstDone ? 8 : 4; h < kPerLane; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
       if ((i & h) == 0) {
@@ -261,6 +267,36 @@ __device__ __forceinline__ void givens_column(const float* p4, int c, float col[
   col[3] = k == 1 ? y : 0.f;
 }
 
+// M H4 for the WHT + SO(4) kind: row r of the block matrix times the 4x4
+// Sylvester Hadamard matrix, as two butterfly stages over its four entries in
+// a fixed order (u = (m0 + m1, m0 - m1, m2 + m3, m2 - m3), then (u0 + u2, u1 +
+// u3, u0 - u2, u1 - u3)). fold_h4_row does it on a row in registers,
+// fold_h4_columns on a block whose column c is held by lane c of a quad; both
+// perform the same operations on the same operands, so every kernel gets the
+// same bits.
+__device__ __forceinline__ void fold_h4_row(float* m) {
+  const float u0 = m[0] + m[1], u1 = m[0] - m[1], u2 = m[2] + m[3], u3 = m[2] - m[3];
+  m[0] = u0 + u2;
+  m[1] = u1 + u3;
+  m[2] = u0 - u2;
+  m[3] = u1 - u3;
+}
+
+__device__ __forceinline__ void fold_h4_columns(float (&col)[4], int c) {
+  // (the lane with the stage's bit set takes partner - self, as the row form's
+  // second operand minus its first)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = dpp_f32<kQuadXor1>(col[r]);
+    col[r] = (c & 1) ? p - col[r] : col[r] + p;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = dpp_f32<kQuadXor2>(col[r]);
+    col[r] = (c & 2) ? p - col[r] : col[r] + p;
+  }
+}
+
 // Column c of the block matrix of the given kind (every kernel builds the
 // matrices through this, so all of them use the same values).
 __device__ __forceinline__ void block_column(int kind, const float* p, int c, float col[4]) {
@@ -291,6 +327,10 @@ __device__ __forceinline__ void block_matrix(int kind, const float* p, float m[1
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r * 4 + c] = col[c][r];
+  if (kind == kRotWhtSo4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fold_h4_row(m + 4 * r);
+  }
 }
 
 // The stored parameters of block b of a head: 8 floats for the WHT + SO(4)
@@ -322,6 +362,7 @@ __device__ __forceinline__ void build_head_matrices(int kind, const float (&bp)[
     const int slot = kQuadOrder ? (b & 7) * 4 + (b >> 3) : b;
     float col[4];
     block_column(kind, bp, c, col);
+    if (kind == kRotWhtSo4) fold_h4_columns(col, c);   // the quad of threads 4b .. 4b + 3 holds the block
     const int p = b >> 3;
     const bool neg = kSigned && kind == kRotWhtSo4 && (p == 1 || p == 2);
 #pragma unroll
@@ -406,7 +447,8 @@ __device__ __forceinline__ float lane_xor_far(float x) {
 //     the block matrices in mats (row-major 4x4 per block); the four dims of
 //     a block are the lanes of one quad, fetched by quad broadcasts.
 //   wht128_pair: the unnormalised Sylvester Hadamard transform: bit 6 of the
-//     dim in the lane, bits 5 and 4 by row swaps, bits 3..0 within a row.
+//     dim in the lane, bits 5 and 4 by row swaps, bits 3 and 2 within a row
+//     (bits 1 and 0 folded into the block matrices, as for wht128_quad).
 template <bool kTranspose>
 __device__ __forceinline__ void so4_apply_pair(float& x0, float& x1, const float* mats, int t) {
   const int i = t & 3;
@@ -441,8 +483,7 @@ __device__ __forceinline__ void wht128_pair(float& x0, float& x1, int t) {
   IQ_PAIR_STAGE(16, lane_xor_far<16>)
   IQ_PAIR_STAGE(8, row_xor<8>)
   IQ_PAIR_STAGE(4, row_xor<4>)
-  IQ_PAIR_STAGE(2, row_xor<2>)
-  IQ_PAIR_STAGE(1, row_xor<1>)
+  // (dim bits 1 and 0: folded into the block matrices, as for wht128_quad)
 #undef IQ_PAIR_STAGE
 }
 
@@ -453,10 +494,12 @@ __device__ __forceinline__ void wht_row_stage(float (&x)[8], int p) {
   for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], s, row_xor<M>(x[i]));
 }
 
-// Unnormalised Sylvester Hadamard transform in the 16-lane form.
+// Unnormalised Sylvester Hadamard transform in the 16-lane form, without
+// the stages of dim bits 0 and 1 (folded into the block matrices, as for
+// wht128_quad).
 __device__ __forceinline__ void wht128_row(float (&x)[8], int p) {
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+  for (int h = 4; h < 8; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if ((i & h) == 0) {

@@ -90,24 +90,41 @@ __device__ __forceinline__ void raw_to_x(const RawVec<T>& r, float (&x)[kPerLane
   }
 }
 
-// The WHT's first butterfly stage (dims 2k and 2k + 1 of the lane, the two
-// fp16 halves of input word k) straight from the fp16 input, in place of
-// the conversion: v_fma_mix_f32 converts each half exactly and rounds the sum
-// once, the same bits as converting first and adding after.
+// The WHT's first stage (dim bit 2: dims i and i + 4 of the lane, which are
+// the same fp16 half of input words i / 2 and i / 2 + 2) straight from the
+// fp16 input, in place of the conversion: v_fma_mix_f32 converts each half
+// exactly and rounds the sum once, the same bits as converting first and
+// adding after.
+template <int kHalf>
+__device__ __forceinline__ void mix_butterfly(uint32_t a, uint32_t b, float one, float& sum, float& dif) {
+  if constexpr (kHalf == 0) {
+    asm("v_fma_mix_f32 %0, %2, %4, %3 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %1, %2, %4, -%3 op_sel:[0,0,0] op_sel_hi:[1,0,1]"
+        : "=&v"(sum), "=v"(dif)
+        : "v"(a), "v"(b), "s"(one));
+  } else {
+    asm("v_fma_mix_f32 %0, %2, %4, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %1, %2, %4, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(sum), "=v"(dif)
+        : "v"(a), "v"(b), "s"(one));
+  }
+}
+
 __device__ __forceinline__ void wht_first_stage_f16(const RawVec<_Float16>& r, float (&x)[kPerLane]) {
   const float one = 1.0f;
+  uint32_t u[16];
 #pragma unroll
   for (int i = 0; i < RawVec<_Float16>::kWords; ++i) {
-    const uint32_t u[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+    u[4 * i] = r.w[i].x;
+    u[4 * i + 1] = r.w[i].y;
+    u[4 * i + 2] = r.w[i].z;
+    u[4 * i + 3] = r.w[i].w;
+  }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float sum, dif;
-      asm("v_fma_mix_f32 %0, %2, %3, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]\n\t"
-          "v_fma_mix_f32 %1, %2, %3, -%2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
-          : "=&v"(sum), "=v"(dif)
-          : "v"(u[k]), "s"(one));
-      x[8 * i + 2 * k] = sum;
-      x[8 * i + 2 * k + 1] = dif;
+  for (int k = 0; k < 16; ++k) {
+    if ((k & 2) == 0) {   // words k and k + 2: dims 2k, 2k + 1 and 2k + 4, 2k + 5
+      mix_butterfly<0>(u[k], u[k + 2], one, x[2 * k], x[2 * k + 4]);
+      mix_butterfly<1>(u[k], u[k + 2], one, x[2 * k + 1], x[2 * k + 5]);
     }
   }
 }
@@ -182,14 +199,18 @@ __device__ __forceinline__ void tile_quad_bits(const uint32_t (*rows)[12], int r
   out[0] = out[1] = out[2] = 0u;
   const int bit = 12 * jq;                  // dims 4jq.. start at bit 12 jq of a row
   const int word = bit >> 5, off = bit & 31;
+  // the next word's bits are used only when the 12 bits cross into it (off >
+  // 20, and then word + 1 <= 11); otherwise any word of the row will do, and
+  // an unconditional read keeps the lanes together
+  const int word_hi = min(word + 1, 11);
 #pragma unroll
   for (int r = 0; r < kTile; ++r) {
     const uint32_t lo = rows[r0 + r][word];
-    const uint32_t hi = (word + 1 < 12) ? rows[r0 + r][word + 1] : 0u;
-    const uint32_t c12 = __builtin_amdgcn_alignbit(hi, lo, off) & 0xfffu;   // 4 codes
+    const uint32_t hi = rows[r0 + r][word_hi];
+    const uint32_t c12 = __builtin_amdgcn_alignbit(hi, lo, off);   // 4 codes in bits 0..11
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t c = (c12 >> (3 * d)) & 7u;
+      const uint32_t c = __builtin_amdgcn_ubfe(c12, 3 * d, 3);
       const int pos = 24 * d + 3 * r;       // compile-time after unrolling
       out[pos >> 5] |= c << (pos & 31);
       if ((pos & 31) > 29) out[(pos >> 5) + 1] |= c >> (32 - (pos & 31));
@@ -236,15 +257,14 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   // three memory round trips of a short append overlap.
   int win = blockIdx.x;
   auto token_of = [&](int w) { return scatter ? w * kVecPerBlock + vec : w0 + w * kVecPerBlock + vec - a.first_slot; };
-  auto tile_mask = [&](int w) {   // slots of tile tt that this call writes
+  // slots of tile tt that this call writes (contiguous slots only, where the
+  // host has checked 0 <= first_slot and first_slot + n_tokens <= capacity):
+  // positions [lo, hi) of the tile's 8
+  auto tile_mask = [&](int w) {
     const int s0 = w0 + w * kVecPerBlock + tt * kTile;
-    uint32_t m = 0u;
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      const int sl = s0 + r;
-      m |= (sl >= a.first_slot && sl - a.first_slot < a.n_tokens && sl < a.capacity) ? (1u << r) : 0u;
-    }
-    return m;
+    const int lo = max(a.first_slot - s0, 0);
+    const int hi = min(a.first_slot + a.n_tokens - s0, kTile);
+    return hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
   };
   auto tile_dst = [&](int w) {
     return reinterpret_cast<uint32_t*>(
@@ -300,8 +320,8 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
       load_vec<T>(src_of(win), ok, x);
     }
     if (wht) {
-      if constexpr (kMixFirst) wht128_quad_signed<2>(x, part);
-      else wht128_quad_signed<1>(x, part);
+      if constexpr (kMixFirst) wht128_quad_signed<true>(x, part);
+      else wht128_quad_signed<false>(x, part);
     }
     so4_apply_lane<false>(x, sm, part);
     if (kK4 && !is_v) {
