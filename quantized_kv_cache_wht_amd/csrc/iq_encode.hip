@@ -151,19 +151,127 @@ __device__ __forceinline__ void store_vec<_Float16>(_Float16* __restrict__ dst, 
   }
 }
 
+// Codes of 32 values straight into their 3 packed dwords (code i at bits
+// [3i, 3i+3)), for a finite norm: the count of code_of in two comparisons per
+// value, and one add with carry per code bit.
+//  - With a = |y| and neg = !(y > 0), u = 2 bits(a) + neg compares with
+//    T = 2 bits(t) as bits(a) + neg does with bits(t); bits(y) + bits(y) drops
+//    the sign, so u is one add with neg as the carry.
+//  - m = #{k >= 4 : u > T_k} by bisection (T4 <= T5 <= T6): c1 = u > T5, then
+//    c0 = u > (c1 ? T6 : T4), m = 2 c1 + c0.
+//  - The code, 4 + m (y > 0) or 3 - m, has bits (1, c1, c0) or (0, !c1, !c0):
+//    (!neg, c1 ^ neg, c0 ^ neg). Each dword is built from its top bit down as
+//    w = w + w + bit, the bit being a lane mask used as the carry; neg is
+//    pushed in place of !neg and the caller flips those bits afterwards.
+// One asm block handles dims 2g+1 and 2g, top dim first, so its masks are
+// made and used inside it: a lane mask that a VALU instruction writes is read
+// by another VALU instruction only after two wait states, which the s_nops
+// and the order of the block give; SALU reads of such masks wait in hardware.
+// The adds' carry-out goes to VCC, which the block clobbers. kSplit: how many
+// of the pair's 6 bits (the top ones) go to the higher dword wh before the
+// rest go to wl.
+#define IQ_PUSH(W, M) "v_addc_co_u32_e64 %[" #W "], vcc, %[" #W "], %[" #W "], %[" #M "]\n\t"
+#define IQ_CODES_HEAD                                         \
+  "v_cmp_ngt_f32_e64 %[n1], %[y1], 0\n\t"                     \
+  "v_cmp_ngt_f32_e64 %[n0], %[y0], 0\n\t"                     \
+  "s_nop 0\n\t"                                               \
+  "v_addc_co_u32_e64 %[u1], vcc, %[y1], %[y1], %[n1]\n\t"     \
+  "v_addc_co_u32_e64 %[u0], vcc, %[y0], %[y0], %[n0]\n\t"     \
+  "v_cmp_gt_u32_e64 %[p1], %[u1], %[t5]\n\t"                  \
+  "v_cmp_gt_u32_e64 %[p0], %[u0], %[t5]\n\t"                  \
+  "s_nop 0\n\t"                                               \
+  "v_cndmask_b32_e64 %[x], %[t4], %[t6], %[p1]\n\t"           \
+  "v_cmp_gt_u32_e64 %[q1], %[u1], %[x]\n\t"                   \
+  "v_cndmask_b32_e64 %[x], %[t4], %[t6], %[p0]\n\t"           \
+  "v_cmp_gt_u32_e64 %[q0], %[u0], %[x]\n\t"                   \
+  "s_xor_b64 %[p1], %[p1], %[n1]\n\t"                         \
+  "s_xor_b64 %[q1], %[q1], %[n1]\n\t"                         \
+  "s_xor_b64 %[p0], %[p0], %[n0]\n\t"                         \
+  "s_xor_b64 %[q0], %[q0], %[n0]\n\t"
+#define IQ_CODES_OPERANDS                                                                                     \
+  [u1] "=&v"(u[1]), [u0] "=&v"(u[0]), [x] "=&v"(xs), [n1] "=&s"(n[1]), [n0] "=&s"(n[0]), [p1] "=&s"(p[1]), \
+      [p0] "=&s"(p[0]), [q1] "=&s"(q[1]), [q0] "=&s"(q[0])
+#define IQ_CODES_INPUTS \
+  [y1] "v"(y[2 * g + 1]), [y0] "v"(y[2 * g]), [t4] "v"(T4), [t5] "v"(T5), [t6] "v"(T6)
+template <int g>
+__device__ __forceinline__ void codes_pair(const float (&y)[kPerLane], uint32_t T4, uint32_t T5, uint32_t T6,
+                                           uint32_t (&w)[3]) {
+  constexpr int top = 6 * g + 5, wh = top >> 5, wl = (6 * g) >> 5;
+  constexpr int kSplit = wh == wl ? 6 : top - 32 * wh + 1;
+  static_assert(kSplit == 6 || kSplit == 4 || kSplit == 2, "pair layout");
+  uint32_t u[2], xs;
+  uint64_t n[2], p[2], q[2];
+  if constexpr (kSplit == 6) {
+    asm(IQ_CODES_HEAD IQ_PUSH(wh, n1) IQ_PUSH(wh, p1) IQ_PUSH(wh, q1) IQ_PUSH(wh, n0) IQ_PUSH(wh, p0)
+            IQ_PUSH(wh, q0)
+        : [wh] "+v"(w[wh]), IQ_CODES_OPERANDS
+        : IQ_CODES_INPUTS
+        : "vcc");
+  } else if constexpr (kSplit == 4) {
+    asm(IQ_CODES_HEAD IQ_PUSH(wh, n1) IQ_PUSH(wh, p1) IQ_PUSH(wh, q1) IQ_PUSH(wh, n0) IQ_PUSH(wl, p0)
+            IQ_PUSH(wl, q0)
+        : [wh] "+v"(w[wh]), [wl] "+v"(w[wl]), IQ_CODES_OPERANDS
+        : IQ_CODES_INPUTS
+        : "vcc");
+  } else {
+    asm(IQ_CODES_HEAD IQ_PUSH(wh, n1) IQ_PUSH(wh, p1) IQ_PUSH(wl, q1) IQ_PUSH(wl, n0) IQ_PUSH(wl, p0)
+            IQ_PUSH(wl, q0)
+        : [wh] "+v"(w[wh]), [wl] "+v"(w[wl]), IQ_CODES_OPERANDS
+        : IQ_CODES_INPUTS
+        : "vcc");
+  }
+}
+#undef IQ_CODES_INPUTS
+#undef IQ_CODES_OPERANDS
+#undef IQ_CODES_HEAD
+#undef IQ_PUSH
+
+// Pairs g, g - 1, .. 0 in that order (the dwords fill from their top bit down).
+template <int g>
+__device__ __forceinline__ void codes_pairs_down(const float (&y)[kPerLane], uint32_t T4, uint32_t T5, uint32_t T6,
+                                                 uint32_t (&w)[3]) {
+  codes_pair<g>(y, T4, T5, T6, w);
+  if constexpr (g > 0) codes_pairs_down<g - 1>(y, T4, T5, T6, w);
+}
+
+__device__ __forceinline__ void codes_pack32(const float (&y)[kPerLane], float t4, float t5, float t6,
+                                             uint32_t (&w)[3]) {
+  const uint32_t T4 = __float_as_uint(t4) << 1, T5 = __float_as_uint(t5) << 1, T6 = __float_as_uint(t6) << 1;
+  w[0] = w[1] = w[2] = 0u;
+  codes_pairs_down<15>(y, T4, T5, T6, w);
+  // bit 3i + 2 holds neg of value i: flip it to !neg
+  w[0] ^= 0x24924924u;
+  w[1] ^= 0x49249249u;
+  w[2] ^= 0x92492492u;
+}
+
 // Norm, codes and the lane's 3 packed dwords of a rotated vector.
 __device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], const Codebook& cb,
                                                     uint32_t (&w)[3]) {
   const float n = quad_norm(y);
-  const float t4 = __fmul_rn(cb.t[4], n), t5 = __fmul_rn(cb.t[5], n), t6 = __fmul_rn(cb.t[6], n);
-  uint32_t c[kPerLane];
+  float t4 = __fmul_rn(cb.t[4], n), t5 = __fmul_rn(cb.t[5], n), t6 = __fmul_rn(cb.t[6], n);
+  float v[kPerLane];
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) c[i] = code_of(y[i], t4, t5, t6);
+  for (int i = 0; i < kPerLane; ++i) v[i] = y[i];
   if (norm_nonfinite(n)) {
+    // code_nonfinite's codes through the same packing: 3 where n = +inf and
+    // y > -inf, else 0. A value of 0 against thresholds of 2 (the bits of the
+    // least subnormal, doubled) gives code 3; -inf, NaN, or any value against
+    // thresholds of 0, gives code 0.
+    // (One value at a time: v_cmp_class with classes 7 = signalling NaN,
+    // quiet NaN, -inf; the s_nop gives the mask's two wait states.)
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) c[i] = code_nonfinite(y[i], n, 3u);
+    for (int i = 0; i < kPerLane; ++i) {
+      uint64_t m;
+      asm("v_cmp_class_f32_e64 %[m], %[y], 7\n\t"
+          "s_nop 1\n\t"
+          "v_cndmask_b32_e64 %[v], 0, %[y], %[m]"
+          : [v] "=v"(v[i]), [m] "=&s"(m)
+          : [y] "v"(y[i]));
+    }
+    t4 = t5 = t6 = n == __builtin_huge_valf() ? __uint_as_float(1u) : 0.0f;
   }
-  pack32(c, w);
+  codes_pack32(v, t4, t5, t6, w);
   return n;
 }
 
