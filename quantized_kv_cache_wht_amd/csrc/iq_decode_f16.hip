@@ -375,7 +375,7 @@ __device__ __forceinline__ void f16_split(const F16DecodeArgs& a, F16Smem<G>& sm
       float m[32];
       so4_matrices_row(a.rot_kind, rp, m);
       if (a.rot_kind == kRotWhtSo4) wht128_row(x, pl);
-      so4_apply_row<false>(x, m);
+      blocks_apply_row<false>(a.rot_kind, x, m);
       float4* dst = reinterpret_cast<float4*>(rec0 + pg * head_stride + 4 + 8 * pl);
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);

@@ -79,7 +79,7 @@ __device__ __forceinline__ void new_token_block(const DecodeArgs& a, const NewTo
     float m[32];
     so4_matrices_row(a.rot_kind, rp, m);
     if (a.rot_kind == kRotWhtSo4) wht128_row(x, p);
-    so4_apply_row<false>(x, m);
+    blocks_apply_row<false>(a.rot_kind, x, m);
     n = row_norm(x);
     uint32_t c[8];
     if (wave == 0 && KB == 4) {
@@ -122,7 +122,7 @@ __device__ __forceinline__ void new_token_block(const DecodeArgs& a, const NewTo
         const float4 q0 = qp[0], q1 = qp[1];
         float y[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         if (a.rot_kind == kRotWhtSo4) wht128_row(y, p);
-        so4_apply_row<false>(y, m);
+        blocks_apply_row<false>(a.rot_kind, y, m);
 #pragma unroll
         for (int i = 0; i < 8; ++i) sm.qr[g][8 * p + i] = y[i];
       }

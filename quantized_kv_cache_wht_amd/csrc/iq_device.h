@@ -402,6 +402,39 @@ __device__ __forceinline__ void so4_apply_lane(float (&x)[kPerLane], const float
   }
 }
 
+// The PLANAR kind's blocks hold two 2x2 Givens blocks (dims 0-1 and 2-3) and
+// zeros elsewhere; its products take the four nonzero entries of each row
+// pair: 2 multiply-adds per value instead of 4. The skipped terms are exact
+// zeros, so the values are so4_apply_*'s (up to the sign of a zero result).
+// e[0..7] = m00 m01 m10 m11 m22 m23 m32 m33 of one block.
+template <bool kTranspose>
+__device__ __forceinline__ void givens_apply4(float* x, const float (&e)[8]) {
+  const float v0 = x[0], v1 = x[1], v2 = x[2], v3 = x[3];
+  x[0] = __builtin_fmaf(kTranspose ? e[2] : e[1], v1, e[0] * v0);
+  x[1] = __builtin_fmaf(e[3], v1, (kTranspose ? e[1] : e[2]) * v0);
+  x[2] = __builtin_fmaf(kTranspose ? e[6] : e[5], v3, e[4] * v2);
+  x[3] = __builtin_fmaf(e[7], v3, (kTranspose ? e[5] : e[6]) * v2);
+}
+
+template <bool kTranspose>
+__device__ __forceinline__ void givens_apply_lane(float (&x)[kPerLane], const float* sm, int part) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const float* mp = sm + (b * 4 + part) * 16;
+    const float2 r0 = *reinterpret_cast<const float2*>(mp), r1 = *reinterpret_cast<const float2*>(mp + 4);
+    const float2 r2 = *reinterpret_cast<const float2*>(mp + 10), r3 = *reinterpret_cast<const float2*>(mp + 14);
+    const float e[8] = {r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+    givens_apply4<kTranspose>(x + 4 * b, e);
+  }
+}
+
+// The lane's block products for any kind (kind is the same for every lane).
+template <bool kTranspose>
+__device__ __forceinline__ void blocks_apply_lane(int kind, float (&x)[kPerLane], const float* sm, int part) {
+  if (kind == kRotPlanar) givens_apply_lane<kTranspose>(x, sm, part);
+  else so4_apply_lane<kTranspose>(x, sm, part);
+}
+
 // ------------------------------------------------- 16-lane form ----
 // A 128-vector spread over one DPP row (16 consecutive lanes), 8 dims per
 // lane: lane p holds dims 8p .. 8p+7, i.e. SO(4) blocks 2p and 2p+1. Four
@@ -563,6 +596,21 @@ __device__ __forceinline__ void so4_apply_row(float (&x)[8], const float (&m)[32
       const float a3 = kTranspose ? mb[3 * 4 + r] : mb[r * 4 + 3];
       x[4 * b + r] = __builtin_fmaf(a3, v3, __builtin_fmaf(a2, v2, __builtin_fmaf(a1, v1, a0 * v0)));
     }
+  }
+}
+
+// so4_apply_row for any kind (the PLANAR kind through its 2x2 blocks).
+template <bool kTranspose>
+__device__ __forceinline__ void blocks_apply_row(int kind, float (&x)[8], const float (&m)[32]) {
+  if (kind == kRotPlanar) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float* mb = m + 16 * b;
+      const float e[8] = {mb[0], mb[1], mb[4], mb[5], mb[10], mb[11], mb[14], mb[15]};
+      givens_apply4<kTranspose>(x + 4 * b, e);
+    }
+  } else {
+    so4_apply_row<kTranspose>(x, m);
   }
 }
 

@@ -245,6 +245,22 @@ __device__ __forceinline__ void codes_pack32(const float (&y)[kPerLane], float t
   w[2] ^= 0x92492492u;
 }
 
+// v = 0 where y > -inf, else y (-inf or NaN): the values that give a
+// non-finite norm's codes through the packing above. One value at a time:
+// v_cmp_class with classes 7 (signalling NaN, quiet NaN, -inf); the s_nop
+// gives the mask's two wait states.
+__device__ __forceinline__ void zero_above_neg_inf(const float (&y)[kPerLane], float (&v)[kPerLane]) {
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    uint64_t m;
+    asm("v_cmp_class_f32_e64 %[m], %[y], 7\n\t"
+        "s_nop 1\n\t"
+        "v_cndmask_b32_e64 %[v], 0, %[y], %[m]"
+        : [v] "=v"(v[i]), [m] "=&s"(m)
+        : [y] "v"(y[i]));
+  }
+}
+
 // Norm, codes and the lane's 3 packed dwords of a rotated vector.
 __device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], const Codebook& cb,
                                                     uint32_t (&w)[3]) {
@@ -258,39 +274,94 @@ __device__ __forceinline__ float quantize_pack_lane(const float (&y)[kPerLane], 
     // y > -inf, else 0. A value of 0 against thresholds of 2 (the bits of the
     // least subnormal, doubled) gives code 3; -inf, NaN, or any value against
     // thresholds of 0, gives code 0.
-    // (One value at a time: v_cmp_class with classes 7 = signalling NaN,
-    // quiet NaN, -inf; the s_nop gives the mask's two wait states.)
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      uint64_t m;
-      asm("v_cmp_class_f32_e64 %[m], %[y], 7\n\t"
-          "s_nop 1\n\t"
-          "v_cndmask_b32_e64 %[v], 0, %[y], %[m]"
-          : [v] "=v"(v[i]), [m] "=&s"(m)
-          : [y] "v"(y[i]));
-    }
+    zero_above_neg_inf(y, v);
     t4 = t5 = t6 = n == __builtin_huge_valf() ? __uint_as_float(1u) : 0.0f;
   }
   codes_pack32(v, t4, t5, t6, w);
   return n;
 }
 
+// The 16-level codes of 4-bit K rows the same way (code i at bits [4i, 4i+4)
+// of dword i / 8): with the positive thresholds T_0 .. T_6 (doubled bits of
+// fl(thr_{8+k} n)), m = #{k : u > T_k} by three bisection steps, c2 = u > T3,
+// c1 = u > (c2 ? T5 : T1), c0 = u > T_{4 c2 + 2 c1}; the code 8 + m or 7 - m
+// has bits (!neg, c2 ^ neg, c1 ^ neg, c0 ^ neg). Dims 2g+1 and 2g per block,
+// dword g / 4 filled from its top; the last comparison's threshold is picked
+// by c2 between (T4, T0) and (T6, T2), then by c1.
+#define IQ_PUSH16(M) "v_addc_co_u32_e64 %[w], vcc, %[w], %[w], %[" #M "]\n\t"
+template <int g>
+__device__ __forceinline__ void codes16_pair(const float (&y)[kPerLane], const uint32_t (&T)[7], uint32_t& w) {
+  uint32_t u1, u0, x1, x0, ya1, yb1, ya0, yb0;
+  uint64_t n1, n0, a1, a0, b1, b0, c1, c0;
+  asm("v_cmp_ngt_f32_e64 %[n1], %[y1], 0\n\t"
+      "v_cmp_ngt_f32_e64 %[n0], %[y0], 0\n\t"
+      "s_nop 0\n\t"
+      "v_addc_co_u32_e64 %[u1], vcc, %[y1], %[y1], %[n1]\n\t"
+      "v_addc_co_u32_e64 %[u0], vcc, %[y0], %[y0], %[n0]\n\t"
+      "v_cmp_gt_u32_e64 %[a1], %[u1], %[t3]\n\t"
+      "v_cmp_gt_u32_e64 %[a0], %[u0], %[t3]\n\t"
+      "s_nop 0\n\t"
+      "v_cndmask_b32_e64 %[x1], %[t1], %[t5], %[a1]\n\t"
+      "v_cndmask_b32_e64 %[x0], %[t1], %[t5], %[a0]\n\t"
+      "v_cndmask_b32_e64 %[ya1], %[t0], %[t4], %[a1]\n\t"
+      "v_cndmask_b32_e64 %[yb1], %[t2], %[t6], %[a1]\n\t"
+      "v_cndmask_b32_e64 %[ya0], %[t0], %[t4], %[a0]\n\t"
+      "v_cndmask_b32_e64 %[yb0], %[t2], %[t6], %[a0]\n\t"
+      "v_cmp_gt_u32_e64 %[b1], %[u1], %[x1]\n\t"
+      "v_cmp_gt_u32_e64 %[b0], %[u0], %[x0]\n\t"
+      "s_nop 0\n\t"
+      "v_cndmask_b32_e64 %[x1], %[ya1], %[yb1], %[b1]\n\t"
+      "v_cndmask_b32_e64 %[x0], %[ya0], %[yb0], %[b0]\n\t"
+      "v_cmp_gt_u32_e64 %[c1], %[u1], %[x1]\n\t"
+      "v_cmp_gt_u32_e64 %[c0], %[u0], %[x0]\n\t"
+      "s_xor_b64 %[a1], %[a1], %[n1]\n\t"
+      "s_xor_b64 %[b1], %[b1], %[n1]\n\t"
+      "s_xor_b64 %[c1], %[c1], %[n1]\n\t"
+      "s_xor_b64 %[a0], %[a0], %[n0]\n\t"
+      "s_xor_b64 %[b0], %[b0], %[n0]\n\t"
+      "s_xor_b64 %[c0], %[c0], %[n0]\n\t"
+      IQ_PUSH16(n1) IQ_PUSH16(a1) IQ_PUSH16(b1) IQ_PUSH16(c1) IQ_PUSH16(n0) IQ_PUSH16(a0) IQ_PUSH16(b0)
+      IQ_PUSH16(c0)
+      : [w] "+v"(w), [u1] "=&v"(u1), [u0] "=&v"(u0), [x1] "=&v"(x1), [x0] "=&v"(x0), [ya1] "=&v"(ya1),
+        [yb1] "=&v"(yb1), [ya0] "=&v"(ya0), [yb0] "=&v"(yb0), [n1] "=&s"(n1), [n0] "=&s"(n0), [a1] "=&s"(a1),
+        [a0] "=&s"(a0), [b1] "=&s"(b1), [b0] "=&s"(b0), [c1] "=&s"(c1), [c0] "=&s"(c0)
+      : [y1] "v"(y[2 * g + 1]), [y0] "v"(y[2 * g]), [t0] "v"(T[0]), [t1] "v"(T[1]), [t2] "v"(T[2]),
+        [t3] "v"(T[3]), [t4] "v"(T[4]), [t5] "v"(T[5]), [t6] "v"(T[6])
+      : "vcc");
+}
+#undef IQ_PUSH16
+
+template <int g>
+__device__ __forceinline__ void codes16_pairs_down(const float (&y)[kPerLane], const uint32_t (&T)[7],
+                                                   uint32_t (&w)[4]) {
+  codes16_pair<g>(y, T, w[g >> 2]);
+  if constexpr (g > 0) codes16_pairs_down<g - 1>(y, T, w);
+}
+
 // Norm, 16-level codes and the lane's 4 packed dwords (code i at bits 4i) of a
-// rotated vector: the 4-bit K rows.
+// rotated vector: the 4-bit K rows. A non-finite norm goes through the same
+// packing as in quantize_pack_lane (code 7 or 0).
 __device__ __forceinline__ float quantize_pack_lane16(const float (&y)[kPerLane], const Codebook& cb,
                                                       uint32_t (&w)[4]) {
   const float n = quad_norm(y);
   float tp[7];
 #pragma unroll
   for (int k = 0; k < 7; ++k) tp[k] = __fmul_rn(cb.t4[8 + k], n);
-  const bool nf = norm_nonfinite(n);
+  float v[kPerLane];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t v = 0u;
+  for (int i = 0; i < kPerLane; ++i) v[i] = y[i];
+  if (norm_nonfinite(n)) {
+    zero_above_neg_inf(y, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v |= (nf ? code_nonfinite(y[8 * d + i], n, 7u) : code16_of(y[8 * d + i], tp)) << (4 * i);
-    w[d] = v;
+    for (int k = 0; k < 7; ++k) tp[k] = n == __builtin_huge_valf() ? __uint_as_float(1u) : 0.0f;
   }
+  uint32_t T[7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) T[k] = __float_as_uint(tp[k]) << 1;
+  w[0] = w[1] = w[2] = w[3] = 0u;
+  codes16_pairs_down<15>(v, T, w);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) w[d] ^= 0x88888888u;   // bit 3 of each code held neg: flip it to !neg
   return n;
 }
 
@@ -342,7 +413,10 @@ __device__ __forceinline__ void tile_keep_bits(uint32_t mask, uint32_t (&keep)[3
   }
 }
 
-template <typename T, bool kK4>   // kK4: the cache's K rows are 4-bit
+// kK4: the cache's K rows are 4-bit; kGivens: the PLANAR kind (2x2 blocks,
+// no WHT), an instance of its own so that the other kinds' loop keeps its
+// register budget.
+template <typename T, bool kK4, bool kGivens>
 __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
   __shared__ __align__(16) float sm[kBlocks * 16];
   __shared__ __align__(16) uint32_t rows[kVecPerBlock][12];
@@ -415,7 +489,7 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
     const bool ok = tok >= 0 && tok < a.n_tokens;
     // fp16 input with the WHT: its first stage reads the raw halves (no conversion)
     constexpr bool kMixFirst = kPrefetch && sizeof(T) == 2;
-    const bool wht = a.rot_kind == kRotWhtSo4;
+    const bool wht = !kGivens && a.rot_kind == kRotWhtSo4;
     if (kPrefetch) {
       if constexpr (kMixFirst) {
         if (wht) wht_first_stage_f16(raw, x);
@@ -431,7 +505,8 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
       if constexpr (kMixFirst) wht128_quad_signed<true>(x, part);
       else wht128_quad_signed<false>(x, part);
     }
-    so4_apply_lane<false>(x, sm, part);
+    if constexpr (kGivens) givens_apply_lane<false>(x, sm, part);
+    else so4_apply_lane<false>(x, sm, part);
     if (kK4 && !is_v) {
       uint32_t w4[4];
       const float n4 = quantize_pack_lane16(x, a.cb, w4);
@@ -568,7 +643,7 @@ __global__ __launch_bounds__(64) void append_row_kernel(AppendArgs a) {
   float m[32];
   so4_matrices_row(a.rot_kind, rp, m);
   if (a.rot_kind == kRotWhtSo4) wht128_row(x, p);
-  so4_apply_row<false>(x, m);
+  blocks_apply_row<false>(a.rot_kind, x, m);
   const float n = row_norm(x);
   if (!is_v && a.k_bits == 4) {
     // 4-bit K: this lane's 8 codes are the row's dword p
@@ -634,11 +709,11 @@ __global__ __launch_bounds__(kEncThreads) void rotate_kernel(RotateArgs a) {
     float x[kPerLane];
     load_vec<float>(a.x + off, ok, x);
     if (kInverse) {
-      so4_apply_lane<true>(x, sm, part);
+      blocks_apply_lane<true>(a.rot_kind, x, sm, part);
       if (wht) wht128_quad(x, part);
     } else {
       if (wht) wht128_quad(x, part);
-      so4_apply_lane<false>(x, sm, part);
+      blocks_apply_lane<false>(a.rot_kind, x, sm, part);
     }
     if (ok) store_vec<float>(a.y + off, x);
   }
@@ -724,7 +799,7 @@ __global__ __launch_bounds__(kEncThreads) void dequant_kernel(DequantArgs a) {
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) x[i] = centroid(code_at(w, i), a.cb);
     }
-    so4_apply_lane<true>(x, sm, part);
+    blocks_apply_lane<true>(a.rot_kind, x, sm, part);
     if (a.rot_kind == kRotWhtSo4) wht128_quad(x, part);
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) x[i] *= n;
@@ -752,18 +827,22 @@ hipError_t launch_append(const AppendArgs& a, bool f16, hipStream_t s) {
     return hipGetLastError();
   }
   dim3 grid(enc_grid_x(a.n_tokens, 2LL * a.num_kv_heads), a.num_kv_heads, 2);
-  const bool k4 = a.k_bits == 4;
+  const bool k4 = a.k_bits == 4, givens = a.rot_kind == kRotPlanar;
+#define IQ_APPEND(T, K4, GV) hipLaunchKernelGGL((append_kernel<T, K4, GV>), grid, dim3(kEncThreads), 0, s, a)
   if (f16) {
-    if (k4)
-      hipLaunchKernelGGL((append_kernel<_Float16, true>), grid, dim3(kEncThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((append_kernel<_Float16, false>), grid, dim3(kEncThreads), 0, s, a);
+    if (givens) {
+      if (k4) IQ_APPEND(_Float16, true, true); else IQ_APPEND(_Float16, false, true);
+    } else {
+      if (k4) IQ_APPEND(_Float16, true, false); else IQ_APPEND(_Float16, false, false);
+    }
   } else {
-    if (k4)
-      hipLaunchKernelGGL((append_kernel<float, true>), grid, dim3(kEncThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((append_kernel<float, false>), grid, dim3(kEncThreads), 0, s, a);
+    if (givens) {
+      if (k4) IQ_APPEND(float, true, true); else IQ_APPEND(float, false, true);
+    } else {
+      if (k4) IQ_APPEND(float, true, false); else IQ_APPEND(float, false, false);
+    }
   }
+#undef IQ_APPEND
   return hipGetLastError();
 }
 
