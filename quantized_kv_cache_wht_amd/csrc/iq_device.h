@@ -575,10 +575,10 @@ __device__ __forceinline__ float row_norm(const float (&y)[8]) {
 }
 
 // Row-major matrices of the lane's two blocks from their stored parameters
-// (p16 as load_row_params leaves it).
+// (p16 as load_row_params leaves it: the second block's at p16 + 8).
 __device__ __forceinline__ void so4_matrices_row(int kind, const float (&p16)[16], float (&m)[32]) {
   block_matrix(kind, p16, m);
-  block_matrix(kind, p16 + rot_params_per_block(kind), m + 16);
+  block_matrix(kind, p16 + 8, m + 16);
 }
 
 // y_b = M_b y_b (or M_b^T y_b) for the lane's two blocks.
@@ -614,18 +614,21 @@ __device__ __forceinline__ void blocks_apply_row(int kind, float (&x)[8], const 
   }
 }
 
-// The stored parameters of the lane's two blocks: 16 floats (four float4
-// loads) for the WHT + SO(4) kind, 8 (two) for the others, whose p16[8..15]
-// repeat p16[0..7] and go unused. All four loads are unconditional: a load
-// under a condition makes the compiler wait for it where the paths join.
+// The stored parameters of the lane's two blocks: the first block's at
+// p16[0..], the second's at p16[8..] (8 floats each for the WHT + SO(4) kind,
+// 4 for the others, whose p16[4..7] and p16[12..15] repeat a float4 and go
+// unused). The second block sits at a constant offset so that no register
+// array is indexed at run time (which would put it in scratch memory). All
+// four loads are unconditional: a load under a condition makes the compiler
+// wait for it where the paths join.
 __device__ __forceinline__ void load_row_params(const float* rot_head, int kind, int p, float (&p16)[16]) {
   const int per = 2 * rot_params_per_block(kind);
   const float4* r = reinterpret_cast<const float4*>(rot_head + per * p);
-  const int hi = kind == kRotWhtSo4 ? 2 : 0;
+  const bool eight = kind == kRotWhtSo4;
+  const float4 t[4] = {r[0], r[eight ? 1 : 0], r[eight ? 2 : 1], r[eight ? 3 : 1]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float4 t = r[i < 2 ? i : hi + i - 2];
-    p16[4 * i] = t.x; p16[4 * i + 1] = t.y; p16[4 * i + 2] = t.z; p16[4 * i + 3] = t.w;
+    p16[4 * i] = t[i].x; p16[4 * i + 1] = t[i].y; p16[4 * i + 2] = t[i].z; p16[4 * i + 3] = t[i].w;
   }
 }
 
