@@ -548,6 +548,54 @@ __device__ __forceinline__ void wht128_row(float (&x)[8], int p) {
   wht_row_stage<8>(x, p);
 }
 
+// ------------------------------------------------- 32-lane form ----
+// A 128-vector over 32 consecutive lanes (half a wave), 4 dims per lane: lane
+// t holds dims 4t .. 4t+3, i.e. SO(4) block t. Dim bits 0 and 1 are in the
+// lane (their WHT stages folded into the block matrices); bits 2 .. 6 are
+// lane bits 0 .. 4, exchanged by DPP within a row and by a row swap across
+// the two rows.
+template <int M>
+__device__ __forceinline__ float half_xor(float x) {
+  if constexpr (M == 16) return lane_xor_far<16>(x);
+  else return row_xor<M>(x);
+}
+
+template <int M>
+__device__ __forceinline__ void wht_half_stage(float (&x)[4], int t) {
+  const float s = (t & M) ? -1.0f : 1.0f;   // the lane with the bit set keeps (partner - self)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(x[i], s, half_xor<M>(x[i]));
+}
+
+// Unnormalised Sylvester Hadamard transform in the 32-lane form, without the
+// stages of dim bits 0 and 1 (folded into the block matrices).
+__device__ __forceinline__ void wht128_half(float (&x)[4], int t) {
+  wht_half_stage<1>(x, t);
+  wht_half_stage<2>(x, t);
+  wht_half_stage<4>(x, t);
+  wht_half_stage<8>(x, t);
+  wht_half_stage<16>(x, t);
+}
+
+// The lane's block product in the 32-lane form (m: its row-major matrix).
+template <bool kTranspose>
+__device__ __forceinline__ void block_apply4(int kind, float (&x)[4], const float (&m)[16]) {
+  if (kind == kRotPlanar) {
+    const float e[8] = {m[0], m[1], m[4], m[5], m[10], m[11], m[14], m[15]};
+    givens_apply4<kTranspose>(x, e);
+  } else {
+    const float v0 = x[0], v1 = x[1], v2 = x[2], v3 = x[3];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a0 = kTranspose ? m[0 * 4 + r] : m[r * 4 + 0];
+      const float a1 = kTranspose ? m[1 * 4 + r] : m[r * 4 + 1];
+      const float a2 = kTranspose ? m[2 * 4 + r] : m[r * 4 + 2];
+      const float a3 = kTranspose ? m[3 * 4 + r] : m[r * 4 + 3];
+      x[r] = __builtin_fmaf(a3, v3, __builtin_fmaf(a2, v2, __builtin_fmaf(a1, v1, a0 * v0)));
+    }
+  }
+}
+
 // fp64 value of lane (p ^ M) of this lane's row.
 template <int M>
 __device__ __forceinline__ double row_xor64(double x) {
