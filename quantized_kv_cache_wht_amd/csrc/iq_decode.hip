@@ -170,12 +170,15 @@ __global__ __launch_bounds__(kRows * kMergeLanes) void decode_merge_kernel(Merge
   reinterpret_cast<float4*>(ro[row])[d4] = o;
   __syncthreads();
   // The rows' weights w_r = 2^(m_r - M) and 1 / L (L = sum_r w_r l_r), by
-  // the first kRows lanes, into LDS; then wave 0 alone: two dims per lane (t
-  // and t + 64), their weighted sum over the rows (weights read as
-  // broadcasts, four independent sums), then the inverse rotation in
-  // registers.
+  // the first kRows lanes, into LDS; then the weighted sum over the rows in
+  // two levels: every thread sums four rows of one dim (kRows / 4 groups x
+  // 128 dims: all the threads), and wave 0 adds the group sums of two dims
+  // per lane (t and t + 64) and applies the inverse rotation in registers.
   __shared__ __align__(16) float rw[kMergeRows];
   __shared__ float rinv;
+  constexpr int kGroups = kMergeRows / 4;
+  static_assert(kGroups * kDim == kMergeRows * kMergeLanes, "one thread per (row group, dim)");
+  __shared__ float part[kGroups][kDim];
   if (tid < 64) {
     const int r = tid & 31;
     const float m_r = r < kMergeRows ? rm[r & (kMergeRows - 1)] : -INFINITY;
@@ -186,22 +189,34 @@ __global__ __launch_bounds__(kRows * kMergeLanes) void decode_merge_kernel(Merge
     if (tid == 0) rinv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
   }
   __syncthreads();
+  {
+    const int d = tid & (kDim - 1), g = tid / kDim;
+    const float4 w4 = *reinterpret_cast<const float4*>(&rw[4 * g]);
+    const float x = __builtin_fmaf(w4.w, ro[4 * g + 3][d],
+                                   __builtin_fmaf(w4.z, ro[4 * g + 2][d],
+                                                  __builtin_fmaf(w4.y, ro[4 * g + 1][d], w4.x * ro[4 * g][d])));
+    part[g][d] = x;
+  }
+  __syncthreads();
   if (tid < 64) {
     const int t = tid;
-    float x0[4] = {0.f, 0.f, 0.f, 0.f}, x1[4] = {0.f, 0.f, 0.f, 0.f};
+    float x0[kGroups], x1[kGroups];
 #pragma unroll
-    for (int k0 = 0; k0 < kMergeRows; k0 += 4) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&rw[k0]);
-      const float wk[4] = {w4.x, w4.y, w4.z, w4.w};
+    for (int g = 0; g < kGroups; ++g) {
+      x0[g] = part[g][t];
+      x1[g] = part[g][t + 64];
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x0[u] = __builtin_fmaf(wk[u], ro[k0 + u][t], x0[u]);
-        x1[u] = __builtin_fmaf(wk[u], ro[k0 + u][t + 64], x1[u]);
+    for (int w = 1; w < kGroups; w *= 2) {   // pairwise sums
+#pragma unroll
+      for (int g = 0; g + w < kGroups; g += 2 * w) {
+        x0[g] += x0[g + w];
+        x1[g] += x1[g + w];
       }
     }
     const float inv = rinv;
-    float y0 = ((x0[0] + x0[1]) + (x0[2] + x0[3])) * inv;
-    float y1 = ((x1[0] + x1[1]) + (x1[2] + x1[3])) * inv;
+    float y0 = x0[0] * inv;
+    float y1 = x1[0] * inv;
     if (kRotate) {
       so4_apply_pair<true>(y0, y1, mats, t);
       if (a.rot_kind == kRotWhtSo4) wht128_pair(y0, y1, t);
