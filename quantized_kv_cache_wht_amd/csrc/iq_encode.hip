@@ -553,11 +553,15 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
       }
       continue;
     }
-    // V, contiguous slots: stage rows in LDS, then write whole tile groups
+    // V, contiguous slots: stage rows in LDS, then write whole tile groups.
+    // A wave's 16 vectors are exactly the two tiles its threads assemble
+    // (tt = 2 wave, 2 wave + 1), so the exchange stays inside the wave: its
+    // LDS operations execute in issue order, and a wave barrier (no
+    // instruction) only keeps the compiler from moving them across.
     rows[vec][3 * part] = w[0];
     rows[vec][3 * part + 1] = w[1];
     rows[vec][3 * part + 2] = w[2];
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     const uint32_t mask = tile_mask(win);
     if (mask != 0u) {
       uint32_t bits[3];
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(kEncThreads) void append_kernel(AppendArgs a) {
       dst[1] = bits[1];
       dst[2] = bits[2];
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();   // (the next window's rows go where these were read)
   }
 }
 
