@@ -295,7 +295,7 @@ def append_roofline(us: float, T: int, hkv: int, one_token_us: float | None) -> 
     traffic = c.get("hbm_bytes_per_launch")
     hbm = {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
            "traffic": None if traffic is None else round(traffic), "algorithmic_bytes": nbytes}
-    r = {"kernel": "append_kernel<_Float16, false>",
+    r = {"kernel": "append_kernel<_Float16, false, false>",
          "launch": f"{T} tokens x {hkv} KV heads, K and V (fp16 in)",
          "launch_us": round(us, 2), "token_layers_per_s": round(T / (us * 1e-6)),
          "one_token_append_us": None if one_token_us is None else round(one_token_us, 3)}

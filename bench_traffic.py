@@ -109,7 +109,7 @@ def main():
         alg_text = "packed K and V rows, 104 B per token and KV head"
         digest = decode_source_digest()
     else:
-        kernels = (("append", ("append_kernel<_Float16, false>", "append_kernelIDF16_Lb0E")),)
+        kernels = (("append", ("append_kernel<_Float16, false, false>", "append_kernelIDF16_Lb0ELb0E")),)
         alg = w.num_kv_heads * w.seq_len * 2 * (256 + ROW_BYTES)
         alg_text = "per token, KV head and K or V: 256 B of fp16 in, 48 B of codes and a 4 B norm out"
         digest = encode_source_digest()
