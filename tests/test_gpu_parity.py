@@ -228,6 +228,27 @@ def test_decode_matches_oracle(hq, hkv, lens):
         assert np.all(out[s] == 0)
 
 
+@pytest.mark.parametrize("hq,hkv,start,n", [
+    (32, 4, 31, 2100),     # last start whose row still begins in block 0
+    (32, 4, 32, 2100),     # first start that does not
+    (32, 4, 100, 1),
+    (8, 8, 5000, 700),     # fewer live blocks than splits times waves
+    (16, 1, 3000, 9000),
+    (4, 1, 60, 65),
+])
+def test_decode_single_sequence_at_any_start(hq, hkv, start, n):
+    """One sequence per launch: a row that does not begin at slot 0 of its cache row, in a cache with
+    more slots before and after it."""
+    total = start + n + 40
+    rot, kr, kn, vr, vn = _oracle_cache(start + n, hkv, total)
+    cache = _upload(rot, kr, kn, vr, vn)
+    starts, lens = np.array([start], np.int32), np.array([n], np.int32)
+    q = iqinputs.queries(hq, 2, 1, hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens), n))
+    ref = R.decode_attention(q, kr, kn, vr, vn, rot, starts, lens, SCALE, C32)
+    _assert_attention_close(out, ref, f"hq={hq} hkv={hkv} start={start} len={n}")
+
+
 def test_decode_invalid_ranges_give_nan_and_no_fault():
     hkv, hq = 2, 4
     rot, kr, kn, vr, vn = _oracle_cache(77, hkv, 300)
@@ -453,9 +474,20 @@ def test_decode_k4_matches_oracle(kind, hq, hkv, lens):
 def test_append_decode_equals_append_then_decode(hq, hkv, lens, k_bits, kind, f16):
     """The fused step writes the same codes and norms as iq_rotate_quantize_append and returns the
     decode over the grown cache (checked against the oracle too)."""
+    _check_append_decode(hq, hkv, lens, k_bits, kind, f16, 5)
+
+
+@pytest.mark.parametrize("hq,hkv,n,first", [(32, 4, 2100, 32), (32, 4, 700, 4133), (8, 8, 90, 31)])
+def test_append_decode_single_sequence_at_any_start(hq, hkv, n, first):
+    """One sequence per launch whose row does not begin at slot 0 of its cache row (and one that
+    begins in the row's first block)."""
+    _check_append_decode(hq, hkv, [n], 3, "wht_so4", True, first)
+
+
+def _check_append_decode(hq, hkv, lens, k_bits, kind, f16, first):
     lens = np.array(lens, np.int32)
     n_seqs = len(lens)
-    starts = (np.concatenate([[0], np.cumsum(lens + 1)[:-1]]) + 5).astype(np.int32)   # room for each new token
+    starts = (np.concatenate([[0], np.cumsum(lens + 1)[:-1]]) + first).astype(np.int32)   # room for each new token
     cap = -(-(int(starts[-1] + lens[-1]) + 1) // 32) * 32
     seed = int(lens.sum()) + hq
     rot = iqinputs.rotation_params_kind(seed, 0, hkv, kind)
