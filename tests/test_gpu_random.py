@@ -1,0 +1,114 @@
+"""Seeded random decode configurations against the oracle (MI355X only).
+
+Each case draws its own mix of what the fixed cases in test_gpu_parity.py
+vary one or two at a time: group size, KV heads, K width, rotation kind, batch
+size, empty sequences, starts that are not multiples of 32, gaps between the
+sequences' rows, lengths that straddle split boundaries, a max_seq_len bound
+larger than the longest sequence (which changes the split plan), and now and
+then a sequence whose length exceeds that bound (its output must be NaN).
+Both the decode alone and the fused decode step are checked, to the same
+tolerances as the fixed cases (max-abs 2e-3, relative L2 1e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import iqinputs
+import quantized_kv_cache_wht_amd as iq
+from oracle import iqref as R
+
+pytestmark = pytest.mark.gpu
+from parity_util import C32, T32, SCALE, _t, _np, _assert_attention_close  # noqa: E402
+
+C16, T16, _ = R.codebook(levels=16)
+CASES = 16
+
+
+def _draw(case):
+    g = np.random.default_rng(7000 + case)
+    hkv = int(g.choice([1, 2, 4, 8]))
+    group = int(g.choice([1, 2, 4, 8, 16]))
+    k_bits = int(g.choice([3, 4]))
+    kind = str(g.choice(iqinputs.ROTATION_KINDS))
+    n_seqs = int(g.integers(1, 6))
+    lens = []
+    for _ in range(n_seqs):
+        r = g.random()
+        lens.append(0 if r < 0.12 else int(g.integers(1, 40)) if r < 0.35 else int(g.integers(40, 3000)))
+    budget = max(1, 6000 // max(1, hkv // 2))   # keeps the oracle's encode within seconds
+    scale_down = max(1.0, sum(lens) / budget)
+    lens = np.array([int(x / scale_down) for x in lens], np.int32)
+    gaps = g.integers(0, 40, n_seqs)
+    starts = (np.concatenate([[0], np.cumsum(lens + gaps)[:-1]]) + gaps[0]).astype(np.int32)
+    max_len = int(lens.max()) + int(g.integers(0, 200))
+    bad = int(g.integers(0, n_seqs)) if (n_seqs > 1 and g.random() < 0.3) else -1
+    return hkv, group, k_bits, kind, lens, starts, max_len, bad
+
+
+def _label(case, hkv, group, k_bits, kind, lens, starts, max_len, bad):
+    return (f"case {case}: hkv={hkv} G={group} k_bits={k_bits} {kind} lens={[int(x) for x in lens]} "
+            f"starts={[int(x) for x in starts]} max_seq_len={max_len} over-bound seq={bad}")
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_decode_random_configuration(case):
+    hkv, group, k_bits, kind, lens, starts, max_len, bad = _draw(case)
+    label = _label(case, hkv, group, k_bits, kind, lens, starts, max_len, bad)
+    print(label, flush=True)
+    hq = hkv * group
+    lens_call = lens.copy()
+    if bad >= 0:
+        lens_call[bad] = max_len + 1    # beyond the launch's bound: NaN, and nothing read out of bounds
+    total = int((starts + lens_call).max()) + 5
+    cap = -(-total // 32) * 32
+    rot = iqinputs.rotation_params_kind(case, 0, hkv, kind)
+    k = np.zeros((cap, hkv, 128), np.float16)
+    v = np.zeros_like(k)
+    k[:total] = iqinputs.kv(case, 1, "k", total, hkv, "student_t6", "f16")
+    v[:total] = iqinputs.kv(case, 1, "v", total, hkv, "student_t6", "f16")
+    kr, kn = R.encode_tokens(k, rot, T16 if k_bits == 4 else T32)
+    vt, vn = R.encode_tokens_v(v, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=k_bits)
+    cache.k_codes.copy_(_t(kr))
+    cache.v_codes.copy_(_t(vt))
+    cache.k_norms.copy_(_t(kn))
+    cache.v_norms.copy_(_t(vn))
+    q = iqinputs.queries(case, 2, len(lens), hq)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(starts), _t(lens_call), max_len))
+    good = [s for s in range(len(lens)) if s != bad]
+    ref = R.decode_attention(q, kr, kn, vt, vn, rot, starts, lens_call, SCALE, C32,
+                             k_centroids32=C16 if k_bits == 4 else None, seqs=good)
+    _assert_attention_close(out[good], ref[good], label)
+    for s in good:
+        if lens[s] == 0:
+            assert np.all(out[s] == 0), label
+    if bad >= 0:
+        assert np.all(np.isnan(out[bad])), label
+
+
+@pytest.mark.parametrize("case", range(CASES // 2))
+def test_append_decode_random_configuration(case):
+    """The fused step at the same random shapes: the cache it leaves equals iq_rotate_quantize_append's,
+    and its output equals iq_decode_attention over the grown cache."""
+    hkv, group, k_bits, kind, lens, starts, max_len, _ = _draw(100 + case)
+    label = _label(100 + case, hkv, group, k_bits, kind, lens, starts, max_len, -1)
+    print(label, flush=True)
+    hq = hkv * group
+    starts = (starts + np.arange(len(lens), dtype=np.int32)).astype(np.int32)   # room for each new token
+    cap = -(-(int((starts + lens).max()) + 1 + 5) // 32) * 32
+    rot = iqinputs.rotation_params_kind(case, 0, hkv, kind)
+    x_k = iqinputs.kv(case, 4, "k", cap, hkv, "student_t6", "f16")
+    x_v = iqinputs.kv(case, 4, "v", cap, hkv, "student_t6", "f16")
+    new_slots = starts + lens
+    q = iqinputs.queries(case, 5, len(lens), hq)
+    caches = []
+    for _ in range(2):
+        c = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=k_bits)
+        iq.iq_rotate_quantize_append(c, _t(x_k), _t(x_v), first_slot=0)
+        caches.append(c)
+    k_new, v_new = x_k[new_slots], x_v[new_slots]
+    iq.iq_rotate_quantize_append(caches[0], _t(k_new), _t(v_new), slots=_t(new_slots.astype(np.int32)))
+    ref = _np(iq.iq_decode_attention(caches[0], _t(q), _t(starts), _t(lens + 1), max_len + 1))
+    got = _np(iq.iq_append_decode_attention(caches[1], _t(k_new), _t(v_new), _t(q), _t(starts), _t(lens), max_len))
+    for name in ("k_codes", "v_codes", "k_norms", "v_norms"):
+        assert torch.equal(getattr(caches[0], name), getattr(caches[1], name)), (name, label)
+    _assert_attention_close(got, ref, label)
