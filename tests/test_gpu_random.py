@@ -7,7 +7,10 @@ sequences' rows, lengths that straddle split boundaries, a max_seq_len bound
 larger than the longest sequence (which changes the split plan), and now and
 then a sequence whose length exceeds that bound (its output must be NaN).
 Both the decode alone and the fused decode step are checked, to the same
-tolerances as the fixed cases (max-abs 2e-3, relative L2 1e-3)."""
+tolerances as the fixed cases (max-abs 2e-3, relative L2 1e-3); and random
+appends (short and bulk kernels, contiguous or listed slots) to the encode's
+bar: codes equal up to cell-boundary ties, norms to 2e-6, every slot not
+written unchanged."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +20,7 @@ import quantized_kv_cache_wht_amd as iq
 from oracle import iqref as R
 
 pytestmark = pytest.mark.gpu
-from parity_util import C32, T32, SCALE, _t, _np, _assert_attention_close  # noqa: E402
+from parity_util import C32, T32, SCALE, _t, _np, _assert_attention_close, _boundary_mismatch_ok  # noqa: E402
 
 C16, T16, _ = R.codebook(levels=16)
 CASES = 16
@@ -112,3 +115,72 @@ def test_append_decode_random_configuration(case):
     for name in ("k_codes", "v_codes", "k_norms", "v_norms"):
         assert torch.equal(getattr(caches[0], name), getattr(caches[1], name)), (name, label)
     _assert_attention_close(got, ref, label)
+
+
+def _encode_ref(x, rot, thr):
+    """Oracle codes [Hkv][n][128], norms [Hkv][n] and the float32 rotated vectors of x [n][Hkv][128]."""
+    out_c, out_n, out_y = [], [], []
+    for h in range(x.shape[1]):
+        y32 = R.rotate(x[:, h].astype(np.float64), rot[h]).astype(np.float32)
+        c, n = R.quantize(y32, thr)
+        out_c.append(c), out_n.append(n), out_y.append(y32)
+    return np.stack(out_c), np.stack(out_n), np.stack(out_y)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_append_random_configuration(case):
+    """Random appends into a cache that already holds other tokens: the short-append (<= 64 tokens)
+    and bulk kernels, contiguous slots from any first slot or a slot list with entries outside the
+    cache, fp16 or fp32 input, every rotation kind and K width. Written slots match the oracle (codes
+    up to cell-boundary ties, norms to 2e-6); every other slot, including the other slots of V tiles
+    the append only partly covers, keeps its previous contents bit for bit."""
+    g = np.random.default_rng(9000 + case)
+    hkv = int(g.choice([1, 2, 4, 8]))
+    kind = str(g.choice(iqinputs.ROTATION_KINDS))
+    k_bits = int(g.choice([3, 4]))
+    dt = str(g.choice(["f16", "f32"]))
+    r = g.random()
+    n_tok = int(g.integers(1, 17)) if r < 0.3 else int(g.integers(17, 101)) if r < 0.6 else int(g.integers(101, 3000))
+    use_slots = bool(g.random() < 0.4)
+    label = f"case {case}: hkv={hkv} {kind} k_bits={k_bits} {dt} n_tok={n_tok} slot_list={use_slots}"
+    print(label, flush=True)
+    rot = iqinputs.rotation_params_kind(50 + case, 0, hkv, kind)
+    if use_slots:
+        cap = -(-(2 * n_tok + 8) // 32) * 32
+        slots = g.permutation(cap)[:n_tok].astype(np.int32)
+        k_out = g.random(n_tok) < 0.1
+        slots[k_out] = np.where(g.random(int(k_out.sum())) < 0.5, -1 - g.integers(0, 5, int(k_out.sum())),
+                                cap + g.integers(0, 5, int(k_out.sum())))
+        written = slots[(slots >= 0) & (slots < cap)]
+        sel = np.nonzero((slots >= 0) & (slots < cap))[0]
+    else:
+        first = int(g.integers(0, 100))
+        cap = -(-(first + n_tok + int(g.integers(0, 40))) // 32) * 32
+        written = np.arange(first, first + n_tok)
+        sel = np.arange(n_tok)
+    x_bg = iqinputs.kv(60 + case, 0, "k", cap, hkv, "student_t6", "f16")
+    k = iqinputs.kv(70 + case, 0, "k", n_tok, hkv, "student_t6", dt)
+    v = iqinputs.kv(70 + case, 0, "v", n_tok, hkv, "student_t6", dt)
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=k_bits)
+    assert cache.capacity == cap
+    iq.iq_rotate_quantize_append(cache, _t(x_bg), _t(x_bg), first_slot=0)   # every slot holds a token first
+    before = {n: getattr(cache, n).clone() for n in ("k_codes", "v_codes", "k_norms", "v_norms")}
+    if use_slots:
+        iq.iq_rotate_quantize_append(cache, _t(k), _t(v), slots=_t(slots))
+    else:
+        iq.iq_rotate_quantize_append(cache, _t(k), _t(v), first_slot=first)
+    thr_k = T16 if k_bits == 4 else T32
+    kc, kn, ky = _encode_ref(k[sel], rot, thr_k)
+    vc, vn, vy = _encode_ref(v[sel], rot, T32)
+    got_k = R.unpack(_np(cache.k_codes))
+    got_v = R.unpack_tiles(_np(cache.v_codes))
+    _boundary_mismatch_ok(got_k[:, written], kc, ky, kn, thr_k)
+    _boundary_mismatch_ok(got_v[:, written], vc, vy, vn)
+    for name, ref in (("k_norms", kn), ("v_norms", vn)):
+        assert np.max(np.abs(_np(getattr(cache, name))[:, written] - ref) / ref) < 2e-6, (name, label)
+    others = np.setdiff1d(np.arange(cap), written)
+    old_k, old_v = R.unpack(_np(before["k_codes"])), R.unpack_tiles(_np(before["v_codes"]))
+    assert np.array_equal(got_k[:, others], old_k[:, others]), label
+    assert np.array_equal(got_v[:, others], old_v[:, others]), label
+    for name in ("k_norms", "v_norms"):
+        assert np.array_equal(_np(getattr(cache, name))[:, others], _np(before[name])[:, others]), (name, label)
