@@ -10,7 +10,8 @@ Both the decode alone and the fused decode step are checked, to the same
 tolerances as the fixed cases (max-abs 2e-3, relative L2 1e-3); and random
 appends (short and bulk kernels, contiguous or listed slots) to the encode's
 bar: codes equal up to cell-boundary ties, norms to 2e-6, every slot not
-written unchanged."""
+written unchanged; and the deferred decode (fp16 prefix, packed suffix) and
+the FP16-KV baseline decode at random shapes in either fp16 layout."""
 import numpy as np
 import pytest
 import torch
@@ -184,3 +185,71 @@ def test_append_random_configuration(case):
     assert np.array_equal(got_v[:, others], old_v[:, others]), label
     for name in ("k_norms", "v_norms"):
         assert np.array_equal(_np(getattr(cache, name))[:, others], _np(before[name])[:, others]), (name, label)
+
+
+def _ragged(g, n_seqs, budget, p_empty=0.2):
+    lens = np.array([0 if g.random() < p_empty else int(g.integers(1, 2500)) for _ in range(n_seqs)], np.int64)
+    if lens.sum() > budget:
+        lens = (lens * budget // lens.sum())
+    lens = lens.astype(np.int32)
+    gaps = g.integers(0, 40, n_seqs)
+    starts = (np.concatenate([[0], np.cumsum(lens + gaps)[:-1]]) + gaps[0]).astype(np.int32)
+    return lens, starts
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_deferred_and_f16_decode_random_configuration(case):
+    """The deferred decode (fp16 prefix, then the packed suffix) and the FP16-KV baseline decode at random
+    shapes, either fp16 layout, against attention from the definition over the same K/V."""
+    g = np.random.default_rng(11000 + case)
+    hkv = int(g.choice([1, 2, 4, 8]))
+    group = int(g.choice([1, 2, 4, 8, 16]))
+    kind = str(g.choice(iqinputs.ROTATION_KINDS))
+    k_bits = int(g.choice([3, 4]))
+    token_major = bool(g.random() < 0.5)
+    n_seqs = int(g.integers(1, 5))
+    budget = max(64, 5000 // max(1, hkv // 2))
+    pre, pst = _ragged(g, n_seqs, budget // 2)
+    suf, sst = _ragged(g, n_seqs, budget // 2)
+    hq = hkv * group
+    label = (f"case {case}: hkv={hkv} G={group} {kind} k_bits={k_bits} token_major={token_major} "
+             f"prefix={[int(x) for x in pre]} at {[int(x) for x in pst]} suffix={[int(x) for x in suf]} "
+             f"at {[int(x) for x in sst]}")
+    print(label, flush=True)
+    cap16 = -(-(int((pst + pre).max()) + 1) // 32) * 32
+    cap = -(-(int((sst + suf).max()) + 1) // 32) * 32
+    rot = iqinputs.rotation_params_kind(80 + case, 0, hkv, kind)
+    k16 = iqinputs.kv(90 + case, 1, "k", cap16, hkv, "student_t6", "f16")
+    v16 = iqinputs.kv(90 + case, 1, "v", cap16, hkv, "student_t6", "f16")
+    k = iqinputs.kv(90 + case, 2, "k", cap, hkv, "student_t6", "f16")
+    v = iqinputs.kv(90 + case, 2, "v", cap, hkv, "student_t6", "f16")
+    c_k, t_k, _ = R.codebook(levels=16 if k_bits == 4 else 8)
+    kr, kn = R.encode_tokens(k, rot, t_k)
+    vt, vn = R.encode_tokens_v(v, rot, T32)
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot), k_bits=k_bits)
+    cache.k_codes.copy_(_t(kr))
+    cache.v_codes.copy_(_t(vt))
+    cache.k_norms.copy_(_t(kn))
+    cache.v_norms.copy_(_t(vn))
+    q = iqinputs.queries(95 + case, 3, n_seqs, hq)
+    lay = (lambda a: _t(a)) if token_major else (lambda a: _t(np.ascontiguousarray(a.transpose(1, 0, 2))))
+    max_pre, max_suf = int(pre.max()) + int(g.integers(0, 50)), int(suf.max()) + int(g.integers(0, 50))
+    out = _np(iq.iq_decode_attention_deferred(cache, _t(sst), _t(suf), max_suf, lay(k16), lay(v16), _t(pst), _t(pre),
+                                              max_pre, _t(q), token_major=token_major))
+    ref = R.decode_attention_deferred(q, k16, v16, pst, pre, kr, kn, vt, vn, rot, sst, suf, SCALE, C32,
+                                      k_centroids32=c_k)
+    _assert_attention_close(out, ref, "deferred " + label)
+    for s in np.nonzero((pre + suf) == 0)[0]:
+        assert np.all(out[s] == 0), label
+    # the FP16-KV baseline over the prefix alone
+    out16 = _np(iq.iq_decode_attention_f16(lay(k16), lay(v16), _t(q), _t(pst), _t(pre), max_pre,
+                                           token_major=token_major))
+    ref16 = np.zeros_like(out16, dtype=np.float64)
+    for s in range(n_seqs):
+        a, n = int(pst[s]), int(pre[s])
+        for h in range(hkv):
+            if n:
+                ref16[s, h * group:(h + 1) * group] = R.attention(q[s, h * group:(h + 1) * group],
+                                                                   k16[a:a + n, h].astype(np.float64),
+                                                                   v16[a:a + n, h].astype(np.float64), SCALE)
+    _assert_attention_close(out16, ref16, "f16 " + label)
