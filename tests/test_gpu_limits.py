@@ -10,6 +10,8 @@
   each weighted by how often it occurs in the sequence: the oracle computes
   that from the definition, exactly, at a size it could not take token by
   token.
+* A head whose K codes pass 2^31 bytes (48M slots): encode, decode and the
+  fused step where every byte offset needs 64-bit arithmetic.
 Tolerances as in test_gpu_parity (max-abs 2e-3, relative L2 1e-3)."""
 import numpy as np
 import pytest
@@ -20,7 +22,7 @@ import quantized_kv_cache_wht_amd as iq
 from oracle import iqref as R
 
 pytestmark = pytest.mark.gpu
-from parity_util import C32, T32, SCALE, DEV, _t, _np, _assert_attention_close  # noqa: E402
+from parity_util import C32, T32, SCALE, DEV, _t, _np, _assert_attention_close, _boundary_mismatch_ok  # noqa: E402
 
 
 def test_decode_and_step_at_the_largest_batch():
@@ -92,3 +94,48 @@ def test_decode_beyond_the_split_cap_periodic():
     w = count[None, :] * np.exp(s - s.max(axis=1, keepdims=True))
     ref = (w @ v_hat) / w.sum(axis=1, keepdims=True)
     _assert_attention_close(out[0], ref, f"{n_tok} tokens, periodic cache")
+
+
+def test_cache_past_two_gib_per_head():
+    """A head whose K rows reach past 2^31 bytes (48M slots x 48 B): the encode, the decode and the
+    fused step in the cache's far end, where every byte offset needs more than 31 bits."""
+    hkv, group = 1, 4
+    hq = hkv * group
+    cap = 48 * 2 ** 20
+    n_tok, first = 3000, cap - 3200                     # rows past byte 2^31 of the head's K codes
+    assert first * 48 > 2 ** 31
+    rot = iqinputs.rotation_params(13, 0, hkv)
+    cache = iq.PackedKVCache.allocate(hkv, cap, _t(rot))
+    assert cache.capacity == cap
+    k = iqinputs.kv(13, 0, "k", n_tok, hkv, "student_t6", "f16")
+    v = iqinputs.kv(13, 0, "v", n_tok, hkv, "student_t6", "f16")
+    iq.iq_rotate_quantize_append(cache, _t(k), _t(v), first_slot=first)
+    # slots written one by one through a slot list, at both ends of the head
+    far = np.array([7, cap - 1, cap - 9, 100], np.int32)
+    kf = iqinputs.kv(14, 0, "k", len(far), hkv, "student_t6", "f16")
+    iq.iq_rotate_quantize_append(cache, _t(kf), _t(kf), slots=_t(far))
+    a0 = first - 32                                     # read back a window (tile-aligned)
+    kr = _np(cache.k_codes[:, a0:])
+    kn = _np(cache.k_norms[:, a0:])
+    vt = _np(cache.v_codes[:, a0 // 8:])
+    vn = _np(cache.v_norms[:, a0:])
+    for x, got_c, got_n, rows in ((k, R.unpack(kr), kn, np.arange(32, 32 + n_tok)),
+                                  (v, R.unpack_tiles(vt), vn, np.arange(32, 32 + n_tok))):
+        y = R.rotate(x[:, 0].astype(np.float64), rot[0]).astype(np.float32)
+        c_ref, n_ref = R.quantize(y, T32)
+        _boundary_mismatch_ok(got_c[0, rows], c_ref, y, n_ref)
+        assert np.max(np.abs(got_n[0, rows] - n_ref) / n_ref) < 2e-6
+    y = R.rotate(kf[:, 0].astype(np.float64), rot[0]).astype(np.float32)
+    c_ref, n_ref = R.quantize(y, T32)
+    ends = [cap - 1 - a0, cap - 9 - a0]
+    _boundary_mismatch_ok(R.unpack(kr)[0, ends], c_ref[[1, 2]], y[[1, 2]], n_ref[[1, 2]])
+    # decode over the far sequence, and the fused step appending right after it
+    q = iqinputs.queries(13, 1, 1, hq)
+    st, ln = np.array([first], np.int32), np.array([n_tok], np.int32)
+    out = _np(iq.iq_decode_attention(cache, _t(q), _t(st), _t(ln), n_tok))
+    ref = R.decode_attention(q, kr, kn, vt, vn, rot, st - a0, ln, SCALE, C32)
+    _assert_attention_close(out, ref, "decode past 2 GiB")
+    k_new = iqinputs.kv(15, 0, "k", 1, hkv, "student_t6", "f16")
+    got = _np(iq.iq_append_decode_attention(cache, _t(k_new), _t(k_new), _t(q), _t(st), _t(ln), n_tok))
+    want = _np(iq.iq_decode_attention(cache, _t(q), _t(st), _t(ln + 1), n_tok + 1))
+    _assert_attention_close(got, want, "fused step past 2 GiB")
