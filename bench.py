@@ -61,7 +61,7 @@ def parse():
                    help="finish with 3 device-to-device copies of this many MiB (reference for HBM counters)")
     p.add_argument("--profile-append", action="store_true",
                    help="only the bulk encode of the append roofline (and the calibration copies), for counter runs")
-    p.add_argument("--profile-decode", choices=("long_t131072",), default=None,
+    p.add_argument("--profile-decode", choices=("long_t131072", "ragged32_gqa"), default=None,
                    help="only this workload's decode launches (and the calibration copies), for counter runs")
     return p.parse_args()
 
@@ -328,6 +328,30 @@ def long_decode(iq, stream, gen, timing_cache, calls=12):
     return us, hkv * T * 2 * ROW_BYTES
 
 
+def ragged_decode(iq, stream, gen, timing_cache, calls=10):
+    """The 32-sequence ragged batch (seeded lengths in [1024, 32768], 32 query heads, 8 KV heads) on
+    one layer's cache, back to back; returns (us per call, packed bytes per call)."""
+    import numpy as np
+    import torch
+    import iqinputs
+    dev = torch.device("cuda")
+    w = iqinputs.WORKLOADS["ragged32_gqa"]
+    lens = np.asarray(iqinputs.seq_lengths(w), np.int32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    total, hkv, hq = int(lens.sum()), w.num_kv_heads, w.num_q_heads
+    cap = -(-total // 32) * 32
+    c = timing_cache(hkv, cap)
+    qb = torch.randn((len(lens), hq, 128), generator=gen, device=dev)
+    stb, lnb = torch.from_numpy(starts).to(dev), torch.from_numpy(lens).to(dev)
+    ml = int(lens.max())
+    wsb = iq.decode_workspace(len(lens), hq, hkv, ml, device=dev)
+    outb = torch.empty_like(qb)
+    us = time_per_call(torch, lambda i: iq.iq_decode_attention(c, qb, stb, lnb, ml, out=outb, workspace=wsb,
+                                                                stream=stream), calls, stream)
+    del c, wsb
+    return us, hkv * total * 2 * ROW_BYTES
+
+
 def random_code_cache(iq, gen):
     """A cache factory for timing: random codes and norms (the decode's work does not depend on the
     values; parity at these shapes is tested separately)."""
@@ -351,7 +375,6 @@ def other_workloads(iq, stream):
     calls). Their caches hold random codes and norms (the decode's work does not depend on the
     values; parity at these shapes is tested separately); the bulk encode runs on seeded N(0,1) fp16
     K/V. Also a device-to-device copy, the streaming peak measured on this GPU."""
-    import numpy as np
     import torch
     import iqinputs
     dev = torch.device("cuda")
@@ -382,23 +405,9 @@ def other_workloads(iq, stream):
     del cs
 
     # batched: 32 sequences with seeded lengths in [1024, 32768], Hkv 8, one layer (over 400 MB)
-    w = iqinputs.WORKLOADS["ragged32_gqa"]
-    lens = np.asarray(iqinputs.seq_lengths(w), np.int32)
-    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
-    total, hkv, hq = int(lens.sum()), w.num_kv_heads, w.num_q_heads
-    cap = -(-total // 32) * 32
-    c = timing_cache(hkv, cap)
-    qb = torch.randn((len(lens), hq, 128), generator=gen, device=dev)
-    stb, lnb = torch.from_numpy(starts).to(dev), torch.from_numpy(lens).to(dev)
-    ml = int(lens.max())
-    wsb = iq.decode_workspace(len(lens), hq, hkv, ml, device=dev)
-    outb = torch.empty_like(qb)
-    us = time_per_call(torch, lambda i: iq.iq_decode_attention(c, qb, stb, lnb, ml, out=outb, workspace=wsb,
-                                                                stream=stream), 10, stream)
-    nbytes = hkv * total * 2 * ROW_BYTES
-    res[w.name] = {"decode_us": round(us, 1), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
-                   "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
-    del c, wsb
+    us, nbytes = ragged_decode(iq, stream, gen, timing_cache)
+    res["ragged32_gqa"] = {"decode_us": round(us, 1), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                           "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
     # long context: decode over three layers' caches of 131072 tokens
     us_dec, dec_bytes = long_decode(iq, stream, gen, timing_cache)
@@ -482,7 +491,8 @@ def main():
     if args.profile_decode:
         gen = torch.Generator(device=dev)
         gen.manual_seed(20260818)
-        us, nbytes = long_decode(iq, torch.cuda.current_stream(), gen, random_code_cache(iq, gen), calls=6)
+        run = long_decode if args.profile_decode == "long_t131072" else ragged_decode
+        us, nbytes = run(iq, torch.cuda.current_stream(), gen, random_code_cache(iq, gen), calls=6)
         if args.copy_calibration_mib > 0:
             calibration_copies(torch, args.copy_calibration_mib)
         print(json.dumps({"profile_decode_us": round(us, 2), "workload": args.profile_decode, "bytes": nbytes}),

@@ -11,7 +11,9 @@ summary that bench.py reports when the kernel sources still match:
   --kind append  the bulk encode of the long-context workload
                  (bench.py --profile-append); bench.py's append_roofline;
   --kind decode_long  the 131072-token decode's split kernel and merge
-                 (bench.py --profile-decode long_t131072).
+                 (bench.py --profile-decode long_t131072);
+  --kind decode_ragged  the 32-sequence ragged batch's split kernel and merge
+                 (bench.py --profile-decode ragged32_gqa).
 With --insts, a third run's instruction counters (SQ_INSTS_VALU, SQ_INSTS_MFMA,
 SQ_INSTS_LDS, SQ_INSTS_SALU, SQ_WAVES: wave-level instructions summed over the
 chip) go into the same summary; bench.py reports the VALU count against the
@@ -77,7 +79,7 @@ def main():
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--kind", choices=("decode", "append", "decode_long"), default="decode")
+    ap.add_argument("--kind", choices=("decode", "append", "decode_long", "decode_ragged"), default="decode")
     ap.add_argument("--insts", default=None, help="run dir of the instruction-counter pass")
     ap.add_argument("--sq", nargs="*", default=[], help="run dirs of further shader-counter passes")
     ap.add_argument("--command", required=True, help="the two profiling commands, for the record")
@@ -102,6 +104,17 @@ def main():
         alg = w.num_kv_heads * w.seq_len * 2 * ROW_BYTES
         alg_text = "packed K and V rows, 104 B per token and KV head"
         digest = decode_source_digest()
+    elif a.kind == "decode_ragged":
+        import numpy as np
+        lens = np.asarray(iqinputs.seq_lengths(w), np.int64)
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        kernels = (("split", (f"decode_split_kernel<{group}, 3, false>", f"decode_split_kernelILi{group}ELi3ELb0E")),
+                   ("merge", ("decode_merge_kernel<true, 8>", "decode_merge_kernelILb1ELi8E")))
+        alg = int(w.num_kv_heads * lens.sum() * 2 * ROW_BYTES)
+        alg_text = "packed K and V rows of the batch's tokens, 104 B per token and KV head"
+        digest = decode_source_digest()
+        # 32-slot blocks the launch streams: each sequence from its 32-aligned start
+        ragged_blocks = int(w.num_kv_heads * sum(-(-(int(s) % 32 + int(n)) // 32) for s, n in zip(starts, lens)))
     elif a.kind == "decode_long":
         kernels = (("split", (f"decode_split_kernel<{group}, 3, false>", f"decode_split_kernelILi{group}ELi3ELb0E")),
                    ("merge", ("decode_merge_kernel<true, 32>", "decode_merge_kernelILb1ELi32E")))
@@ -168,7 +181,8 @@ def main():
         ]
     if a.sq:
         cs = all_counters(a.sq)
-        blocks = w.num_kv_heads * w.seq_len // 32 if a.kind != "append" else None
+        blocks = (ragged_blocks if a.kind == "decode_ragged" else
+                  w.num_kv_heads * w.seq_len // 32 if a.kind != "append" else None)
         for label, needle in kernels:
             names = needle if isinstance(needle, tuple) else (needle,)
             merged = collections.defaultdict(list)
